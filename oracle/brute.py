@@ -1,0 +1,81 @@
+"""Pure-Python loop versions of the block's steps, for tiny shapes only
+(test infrastructure; pins for ``oracle.block``).
+
+No numpy arithmetic here: every sum, product, maximum and exponential is a
+Python float operation on one scalar, so an indexing or transposition slip in
+the vectorised oracle cannot be repeated here by the same library call.
+Follows the same passages as ``oracle.block`` (SAM3 ``layer_norm_rows``,
+``run_attn``; SigLIP ``encoder_block``; Hiera plan "MaskUnitAttention").
+"""
+import math
+
+
+def layer_norm(rows, gamma, beta, eps):
+    out = []
+    for r in rows:
+        d = len(r)
+        mean = sum(r) / d
+        var = sum((v - mean) * (v - mean) for v in r) / d
+        inv = 1.0 / math.sqrt(var + eps)
+        out.append([(r[i] - mean) * inv * gamma[i] + beta[i] for i in range(d)])
+    return out
+
+
+def linear(rows, w, b):
+    """y[i][o] = sum_k rows[i][k] * w[o][k] + b[o] (w is [out, in])."""
+    return [[sum(r[k] * w[o][k] for k in range(len(r))) + b[o]
+             for o in range(len(w))] for r in rows]
+
+
+def gelu_erf(v):
+    return 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0)))
+
+
+def gelu_tanh(v):
+    return 0.5 * v * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3)))
+
+
+def attention_head(q_rows, k_rows, v_rows, scale):
+    """One (window, head): for each query, scores against every key, stable
+    softmax, weighted sum of the values."""
+    out = []
+    for q in q_rows:
+        s = [sum(q[d] * k[d] for d in range(len(q))) * scale for k in k_rows]
+        m = max(s)
+        e = [math.exp(v - m) for v in s]
+        z = sum(e)
+        p = [v / z for v in e]
+        out.append([sum(p[j] * v_rows[j][d] for j in range(len(v_rows)))
+                    for d in range(len(v_rows[0]))])
+    return out
+
+
+def block_forward_mask_unit(x, w, n_windows, heads, eps, gelu="erf"):
+    """Whole block for one frame with mask-unit windows, q_stride 1, fused
+    qkv, no RoPE (the tiny configuration's shape). x is a list of token rows
+    in unrolled order; w holds nested lists. Returns (ctx, y)."""
+    n = len(x)
+    h = layer_norm(x, w["ln1_g"], w["ln1_b"], eps)
+    qkv = linear(h, w["qkv_w"], w["qkv_b"])
+    D = len(qkv[0]) // 3
+    hd = D // heads
+    scale = 1.0 / math.sqrt(hd)
+    ctx = [[0.0] * D for _ in range(n)]
+    for win in range(n_windows):
+        toks = list(range(win, n, n_windows))
+        for t in range(heads):
+            lo = t * hd
+            qr = [qkv[i][lo:lo + hd] for i in toks]
+            kr = [qkv[i][D + lo:D + lo + hd] for i in toks]
+            vr = [qkv[i][2 * D + lo:2 * D + lo + hd] for i in toks]
+            o = attention_head(qr, kr, vr, scale)
+            for a, i in enumerate(toks):
+                ctx[i][lo:lo + hd] = o[a]
+    ab = linear(ctx, w["o_w"], w["o_b"])
+    x1 = [[x[i][c] + ab[i][c] for c in range(D)] for i in range(n)]
+    h2 = layer_norm(x1, w["ln2_g"], w["ln2_b"], eps)
+    g = gelu_erf if gelu == "erf" else gelu_tanh
+    u = [[g(v) for v in row] for row in linear(h2, w["fc1_w"], w["fc1_b"])]
+    mb = linear(u, w["fc2_w"], w["fc2_b"])
+    y = [[x1[i][c] + mb[i][c] for c in range(D)] for i in range(n)]
+    return ctx, y

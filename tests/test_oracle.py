@@ -1,0 +1,344 @@
+"""Pins for the CPU oracle (no GPU). Each test ties one oracle function to
+something other than itself: a value printed on the pages, a closed form, an
+invariant, a library routine, or the pure-Python brute force."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import block as ob
+from oracle import brute
+from oracle import index_maps as im
+from vision_transformer_encoder_vit_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(i=0):
+    return np.random.default_rng(1000 + i)
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+def test_layer_norm_closed_form():
+    # gamma = 1, beta = 0: each row has mean 0 and (biased) variance
+    # var / (var + eps), the closed form of the SAM3 layer_norm_rows step.
+    x = _rng().normal(3.0, 2.0, (7, 112))
+    eps = 1e-6
+    y = ob.layer_norm(x, np.ones(112), np.zeros(112), eps)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(y.var(axis=1), var / (var + eps), rtol=1e-12)
+    # a large eps shrinks the variance as the closed form says
+    y2 = ob.layer_norm(x, np.ones(112), np.zeros(112), 4.0)
+    np.testing.assert_allclose(y2.var(axis=1), var / (var + 4.0), rtol=1e-12)
+
+
+def test_layer_norm_vs_torch_and_brute():
+    r = _rng(1)
+    x, g, b = r.normal(size=(5, 48)), 1 + 0.1 * r.normal(size=48), 0.1 * r.normal(size=48)
+    y = ob.layer_norm(x, g, b, 1e-6)
+    t = torch.nn.functional.layer_norm(torch.from_numpy(x), (48,), torch.from_numpy(g),
+                                       torch.from_numpy(b), eps=1e-6).numpy()
+    np.testing.assert_allclose(y, t, atol=1e-12)
+    np.testing.assert_allclose(y, brute.layer_norm(x.tolist(), g.tolist(), b.tolist(), 1e-6), atol=1e-12)
+
+
+# ------------------------------------------------------------------ Linear
+
+def test_linear_vs_brute_and_orientation():
+    r = _rng(2)
+    x, w, b = r.normal(size=(4, 6)), r.normal(size=(3, 6)), r.normal(size=3)
+    np.testing.assert_allclose(ob.linear(x, w, b), brute.linear(x.tolist(), w.tolist(), b.tolist()), atol=1e-12)
+    # [out, in] orientation: a one-hot input row picks a column of w
+    e = np.zeros((1, 6)); e[0, 4] = 1.0
+    np.testing.assert_allclose(ob.linear(e, w, np.zeros(3))[0], w[:, 4], atol=0)
+
+
+# -------------------------------------------------------------------- GELU
+
+def test_gelu_tanh_page_values():
+    rows = np.loadtxt(os.path.join(GOLDEN, "gelu_tanh_siglip.txt"))
+    for x, want, tol in rows:
+        got = ob.gelu_tanh(np.float64(x))
+        if tol == 0:
+            assert got == want
+        else:
+            assert abs(got - want) < tol, (x, got, want)
+    for x, want, tol in rows:
+        if tol:
+            assert abs(brute.gelu_tanh(x) - want) < tol
+
+
+def test_gelu_erf_closed_form():
+    # GELU(u) = u * Phi(u); Phi from the host's math.erf.
+    for u in (-6.0, -1.0, -0.3, 0.0, 0.5, 1.0, 2.5):
+        phi = 0.5 * (1 + math.erf(u / math.sqrt(2)))
+        assert abs(ob.gelu_erf(np.float64(u)) - u * phi) < 1e-15
+    assert abs(ob.gelu_erf(np.float64(1.0)) - 0.8413447460685429) < 1e-12
+    assert abs(ob.gelu_erf(np.float64(-1.0)) + 0.15865525393145707) < 1e-12
+    u = np.linspace(-4, 4, 33)
+    t = torch.nn.functional.gelu(torch.from_numpy(u)).numpy()
+    np.testing.assert_allclose(ob.gelu_erf(u), t, atol=1e-14)
+    # the two GELU forms are different functions: they must not be swapped
+    assert abs(ob.gelu_erf(np.float64(1.0)) - ob.gelu_tanh(np.float64(1.0))) > 1e-4
+
+
+# ----------------------------------------------------------------- softmax
+
+def test_softmax_rows_sum_to_one_and_shift_invariant():
+    s = _rng(3).normal(0, 30, (9, 40))
+    p = ob.softmax_rows(s)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(ob.softmax_rows(s + 123.0), p, atol=1e-12)
+    # scores as large as the SAM3 trunk's (~155) stay finite
+    big = ob.softmax_rows(np.array([[155.0, 150.0, -20.0]]))
+    assert np.all(np.isfinite(big)) and abs(big.sum() - 1) < 1e-12
+    # beyond float64's exp range the row max must still be subtracted first
+    huge = ob.softmax_rows(np.array([[1000.0, 1000.0 - math.log(3.0)]]))
+    np.testing.assert_allclose(huge, [[0.75, 0.25]], atol=1e-12)
+
+
+# --------------------------------------------------------------- attention
+
+def test_attention_vs_torch_sdpa():
+    r = _rng(4)
+    N, D, H = 24, 32, 4
+    q, k, v = r.normal(size=(N, D)), r.normal(size=(N, D)), r.normal(size=(N, D))
+    ctx = ob.attention(q, k, v, [(np.arange(N), np.arange(N))], H, (D // H) ** -0.5)
+    t = lambda a: torch.from_numpy(a).reshape(N, H, D // H).transpose(0, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v)).transpose(0, 1).reshape(N, D)
+    np.testing.assert_allclose(ctx, ref.numpy(), atol=1e-12)
+
+
+def test_attention_special_cases():
+    r = _rng(5)
+    N, D, H = 6, 8, 2
+    q, v = r.normal(size=(N, D)), r.normal(size=(N, D))
+    k_same = np.tile(r.normal(size=(1, D)), (N, 1))
+    ctx = ob.attention(q, k_same, v, [(np.arange(N), np.arange(N))], H, 0.5)
+    np.testing.assert_allclose(ctx, np.tile(v.mean(axis=0), (N, 1)), atol=1e-12)
+    # a window with a single key returns that key's value row
+    wins = [(np.array([i]), np.array([i])) for i in range(N)]
+    ctx1 = ob.attention(q, r.normal(size=(N, D)), v, wins, H, 0.5)
+    np.testing.assert_allclose(ctx1, v, atol=1e-15)
+
+
+def test_attention_windows_vs_brute():
+    r = _rng(6)
+    N, D, H, nw = 16, 12, 3, 4
+    q, k, v = r.normal(size=(N, D)), r.normal(size=(N, D)), r.normal(size=(N, D))
+    wins = im.mask_unit_windows(N, nw, 1)
+    ctx = ob.attention(q, k, v, wins, H, 0.7)
+    hd = D // H
+    for qi, ki in wins:
+        for t in range(H):
+            c = slice(t * hd, (t + 1) * hd)
+            want = brute.attention_head(q[qi, c].tolist(), k[ki, c].tolist(), v[ki, c].tolist(), 0.7)
+            np.testing.assert_allclose(ctx[qi, c], want, atol=1e-12)
+
+
+# --------------------------------------------------------------------- RoPE
+
+def test_rope_properties():
+    hd, H, W = 64, 6, 5
+    tab = synth.axial_rope_table(H, W, hd, 10000.0).astype(np.float64)
+    r = _rng(7)
+    q = r.normal(size=(H * W, 2 * hd))
+    rows = np.arange(H * W)
+    qr = ob.apply_rope(q, tab, rows, hd)
+    # each rotated pair keeps its length (to the float32 table's cos^2+sin^2)
+    np.testing.assert_allclose(qr[:, 0::2] ** 2 + qr[:, 1::2] ** 2, q[:, 0::2] ** 2 + q[:, 1::2] ** 2, rtol=1e-6)
+    # table row 0 (position (0, 0)) is the identity
+    np.testing.assert_allclose(qr[0], q[0], atol=1e-7)
+    # <R_p a, R_p' b> depends only on p' - p per axis: shift both positions
+    a, b = r.normal(size=(1, hd)), r.normal(size=(1, hd))
+    def dot(p1, p2):
+        return (ob.apply_rope(a, tab, np.array([p1]), hd) @ ob.apply_rope(b, tab, np.array([p2]), hd).T).item()
+    pos = lambda y, x: y * W + x
+    assert abs(dot(pos(0, 0), pos(2, 3)) - dot(pos(1, 1), pos(3, 4))) < 1e-5
+    assert abs(dot(pos(0, 0), pos(2, 3)) - dot(pos(0, 0), pos(3, 2))) > 1e-4  # axes are distinct
+    # the pair rotation direction: (1, 0) at angle theta goes to (cos, sin)
+    e = np.zeros((1, hd)); e[0, 0] = 1.0
+    out = ob.apply_rope(e, tab, np.array([pos(0, 1)]), hd)
+    assert abs(out[0, 0] - math.cos(1.0)) < 1e-6 and abs(out[0, 1] - math.sin(1.0)) < 1e-6
+
+
+def test_rope_rows_for_modes():
+    spec = dict(grid_h=72, grid_w=72, mode="spatial", win_h=24, win_w=24)
+    rows = ob.rope_rows_for(spec)
+    assert rows.max() == 575 and rows[24] == 0 and rows[72] == 24
+    spec["mode"] = "global"
+    assert ob.rope_rows_for(spec)[5183] == 5183
+
+
+# -------------------------------------------------------------- index maps
+
+@pytest.mark.parametrize("H,W,L", [(8, 8, 2), (128, 128, 3), (64, 64, 2), (16, 32, 3), (4, 4, 0)])
+def test_unroll_bijection_and_roundtrip(H, W, L):
+    pos = im.unroll_positions(H, W, L)
+    assert sorted(pos.tolist()) == list(range(H * W))
+    payload = np.arange(H * W, dtype=np.int64).reshape(1, H * W, 1) * 3 + 7
+    assert np.array_equal(im.reroll(im.unroll(payload, H, W, L), H, W, L), payload)
+
+
+def test_mask_unit_is_spatial_block_and_pool_is_2x2_cell():
+    H = W = 128
+    L = 3
+    N = H * W
+    pos = im.unroll_positions(H, W, L)
+    ys, xs = np.divmod(np.arange(N), W)
+    n_w = (H >> L) * (W >> L)
+    # window n mod n_w == the 8x8 spatial block index
+    blk = (ys >> L) * (W >> L) + (xs >> L)
+    assert np.array_equal(pos % n_w, blk)
+    # every pool group is one 2x2 spatial cell
+    inv = np.empty(N, dtype=np.int64)
+    inv[pos] = np.arange(N)
+    g = im.pool_groups(N)
+    cells = (ys[inv[g]] >> 1) * (W >> 1) + (xs[inv[g]] >> 1)
+    assert np.all(cells == cells[:, :1])
+    # the pooled order is the (L-1)-level unroll of the half-size grid
+    pooled_cell = cells[:, 0]
+    want = im.unroll_positions(H // 2, W // 2, L - 1)
+    assert np.array_equal(want[pooled_cell], np.arange(N // 4))
+
+
+def test_hiera_stage_shape_contract():
+    # 512^2 input, stride-4 patch embed, 3 unroll levels, 3 pools: the stage
+    # grids, mask-unit sizes and widths listed on the pages.
+    rows = np.loadtxt(os.path.join(GOLDEN, "hiera_stage_shapes.txt"), dtype=np.int64)
+    side, L = 512 // 4, 3
+    N = side * side
+    n_w = (side >> L) ** 2
+    payload = np.arange(N, dtype=np.int64).reshape(1, N, 1)
+    tok = im.unroll(payload, side, side, L)[0, :, 0]
+    ys, xs = np.divmod(tok, side)
+    for stage, grid, dim, heads, win, mu in rows:
+        assert grid * grid == len(tok)
+        assert len(tok) // n_w == win
+        assert dim % heads == 0 and dim // heads == 56
+        # every window (n mod n_w) stays one spatial block of the stage grid
+        cell = 1 << (L - stage)
+        scale = side // grid
+        by, bx = (ys // scale) // cell, (xs // scale) // cell
+        for w in range(0, n_w, 37):
+            sel = np.arange(w, len(tok), n_w)
+            assert len(set(zip(by[sel].tolist(), bx[sel].tolist()))) == 1
+        if stage < 3:
+            g = im.pool_groups(len(tok))
+            # max-pool of the token ids' coarse position: all four share it
+            assert np.all((ys[g] // (2 * scale)) == (ys[g][:, :1] // (2 * scale)))
+            tok, ys, xs = tok[g[:, 0]], ys[g[:, 0]], xs[g[:, 0]]
+
+
+def test_spatial_windows():
+    wins = im.spatial_windows(72, 72, 24, 24)
+    assert len(wins) == 9 and all(len(w) == 576 for w in wins)
+    assert sorted(np.concatenate(wins).tolist()) == list(range(72 * 72))
+    w4 = wins[4]  # centre window
+    ys, xs = np.divmod(w4, 72)
+    assert ys.min() == 24 and ys.max() == 47 and xs.min() == 24 and xs.max() == 47
+    assert w4[1] - w4[0] == 1 and w4[24] - w4[0] == 72
+
+
+# -------------------------------------------------------------- pool4
+
+def test_pool4_definition():
+    z = _rng(8).normal(size=(16, 3))
+    p = ob.pool4(z)
+    for m in range(4):
+        np.testing.assert_array_equal(p[m], np.max(z[[m, m + 4, m + 8, m + 12]], axis=0))
+
+
+# ------------------------------------------------------- whole block (tiny)
+
+def _as_lists(w):
+    return {k: np.asarray(v, dtype=np.float64).tolist() for k, v in w.items()}
+
+
+def test_block_vs_brute_on_tiny_config():
+    spec = synth.CONFIGS["c1_tiny_f32"]
+    inp = synth.make_inputs(spec, seed=0)
+    seams = ob.block_forward(inp["x"], inp, spec)
+    ctx, y = brute.block_forward_mask_unit(np.asarray(inp["x"][0], np.float64).tolist(),
+                                            _as_lists(inp), spec["n_windows"], spec["heads"], spec["eps"])
+    np.testing.assert_allclose(seams["ctx"][0], ctx, atol=1e-12)
+    np.testing.assert_allclose(seams["y"][0], y, atol=1e-12)
+    # residual structure: y = x1 + mlp_branch, x1 = x + attn_branch
+    np.testing.assert_allclose(seams["x1"], inp["x"] + seams["attn_branch"], atol=1e-12)
+    np.testing.assert_allclose(seams["y"], seams["x1"] + seams["mlp_branch"], atol=1e-12)
+
+
+def test_block_tanh_separate_qkv_vs_brute():
+    # SigLIP structure (separate q/k/v, tanh-GELU, global) on a tiny shape:
+    # separate projections equal the fused one with stacked weights.
+    spec = synth.derive(synth.CONFIGS["c4_siglip_b8"], batch=2, grid_h=2, grid_w=4,
+                        dim_in=16, dim_out=16, heads=2, mlp=32, dtype="f32", scale=None)
+    inp = synth.make_inputs(spec, seed=3)
+    seams = ob.block_forward(inp["x"], inp, spec)
+    fused = dict(inp)
+    fused["qkv_w"] = np.concatenate([inp["q_w"], inp["k_w"], inp["v_w"]])
+    fused["qkv_b"] = np.concatenate([inp["q_b"], inp["k_b"], inp["v_b"]])
+    for b in range(2):
+        ctx, y = brute.block_forward_mask_unit(np.asarray(inp["x"][b], np.float64).tolist(),
+                                                _as_lists(fused), 1, 2, spec["eps"], gelu="tanh")
+        np.testing.assert_allclose(seams["y"][b], y, atol=1e-12)
+        np.testing.assert_allclose(seams["ctx"][b], ctx, atol=1e-12)
+
+
+def test_block_frames_independent():
+    # frames never attend to each other: frame f of a batched run equals the
+    # single-frame run (SigLIP batched-vs-sequential property)
+    spec = synth.derive(synth.CONFIGS["c4_siglip_b8"], batch=3, grid_h=2, grid_w=3,
+                        dim_in=8, dim_out=8, heads=2, mlp=16, dtype="f32")
+    inp = synth.make_inputs(spec, seed=4)
+    all3 = ob.block_forward(inp["x"], inp, spec)["y"]
+    one = ob.block_forward(inp["x"][1:2], inp, synth.derive(spec, batch=1))["y"]
+    np.testing.assert_allclose(all3[1], one[0], atol=0)
+
+
+def test_block_transition_vs_definition():
+    # pooled transition on a tiny grid: q and the residual are 2x2-max-pooled
+    # (after the projection), kv keep every token; compare against a direct
+    # loop over the windows with the brute-force attention.
+    spec = synth.derive(synth.CONFIGS["c3a_hiera_trans"], grid_h=8, grid_w=8,
+                        dim_in=8, dim_out=16, heads=2, mlp=32, n_windows=4, dtype="f32")
+    inp = synth.make_inputs(spec, seed=5)
+    s = ob.block_forward(inp["x"], inp, spec)
+    x = np.asarray(inp["x"][0], np.float64)
+    h = brute.layer_norm(x.tolist(), inp["ln1_g"].tolist(), inp["ln1_b"].tolist(), spec["eps"])
+    res = np.array(brute.linear(h, inp["res_w"].tolist(), inp["res_b"].tolist()))
+    qkv = np.array(brute.linear(h, inp["qkv_w"].tolist(), inp["qkv_b"].tolist()))
+    N, D = 64, 16
+    r = np.maximum.reduce([res[s_ * 16:(s_ + 1) * 16] for s_ in range(4)])
+    q = np.maximum.reduce([qkv[s_ * 16:(s_ + 1) * 16, :D] for s_ in range(4)])
+    np.testing.assert_allclose(s["r"][0], r, atol=1e-12)
+    np.testing.assert_allclose(s["q_pooled"][0], q, atol=1e-12)
+    ctx = np.zeros((16, D))
+    for w in range(4):
+        qi, ki = np.arange(w, 16, 4), np.arange(w, N, 4)
+        for t in range(2):
+            c = slice(t * 8, t * 8 + 8)
+            ctx[qi, c] = brute.attention_head(q[qi, c].tolist(), qkv[ki, D:2 * D][:, c].tolist(),
+                                              qkv[ki, 2 * D:][:, c].tolist(), 8 ** -0.5)
+    np.testing.assert_allclose(s["ctx"][0], ctx, atol=1e-12)
+
+
+def test_block_rope_windowed_locality():
+    # spatial windows: changing a token in one window leaves every other
+    # window's output exactly unchanged
+    spec = synth.derive(synth.CONFIGS["c5w_sam3_win"], grid_h=8, grid_w=8, win_h=4, win_w=4,
+                        dim_in=16, dim_out=16, heads=1, mlp=32, dtype="f32")
+    spec["dim_out"] = 16
+    inp = synth.make_inputs(spec, seed=6)
+    inp["rope"] = synth.axial_rope_table(4, 4, 16, 10000.0)
+    y0 = ob.block_forward(inp["x"], inp, spec)["y"][0]
+    x2 = inp["x"].copy()
+    x2[0, 0] += 1.0  # token (0, 0): window 0
+    y1 = ob.block_forward(x2, inp, spec)["y"][0]
+    changed = np.where(np.any(y0 != y1, axis=1))[0]
+    ys, xs = np.divmod(changed, 8)
+    assert len(changed) == 16 and ys.max() < 4 and xs.max() < 4

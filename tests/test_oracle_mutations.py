@@ -1,0 +1,100 @@
+"""The oracle's pins have teeth: plant a plausible mistake in one oracle
+step (on the CPU, by monkeypatching) and check that a pin in test_oracle
+fails. A pin that still passed with the mistake in place would pin nothing."""
+import numpy as np
+import pytest
+
+import tests.test_oracle as pins
+from oracle import block as ob
+from oracle import index_maps as im
+
+
+def _ln_unbiased(x, g, b, eps):
+    x = np.asarray(x, dtype=np.float64)
+    m = x.mean(axis=-1, keepdims=True)
+    v = x.var(axis=-1, ddof=1, keepdims=True)
+    return (x - m) / np.sqrt(v + eps) * g + b
+
+
+def _ln_eps_outside(x, g, b, eps):
+    x = np.asarray(x, dtype=np.float64)
+    m = x.mean(axis=-1, keepdims=True)
+    v = x.var(axis=-1, keepdims=True)
+    return (x - m) / (np.sqrt(v) + eps) * g + b
+
+
+def _softmax_unshifted(s):
+    e = np.exp(s)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _rope_wrong_sign(t, table, rows, hd):
+    neg = table.copy()
+    neg[..., 1] *= -1
+    return _orig_rope(t, neg, rows, hd)
+
+
+def _rope_half_split(t, table, rows, hd):
+    # pairs (j, j + hd/2) instead of (2j, 2j + 1)
+    out = t.copy()
+    for h0 in range(0, t.shape[1], hd):
+        for j in range(hd // 2):
+            c, s = table[rows, j, 0], table[rows, j, 1]
+            a, b = t[:, h0 + j], t[:, h0 + j + hd // 2]
+            out[:, h0 + j] = a * c - b * s
+            out[:, h0 + j + hd // 2] = b * c + a * s
+    return out
+
+
+def _gelu_erf_as_tanh(u):
+    return ob.gelu_tanh(u)
+
+
+def _mask_unit_contiguous(n, nw, qs):
+    per = n // nw
+    return [(np.arange(w * per // qs, (w + 1) * per // qs), np.arange(w * per, (w + 1) * per)) for w in range(nw)]
+
+
+def _attention_no_scale(q, k, v, windows, heads, scale):
+    return _orig_attention(q, k, v, windows, heads, 1.0)
+
+
+def _pool_adjacent(z):
+    return z.reshape(-1, 4, z.shape[1]).max(axis=1)
+
+
+def _unroll_coarse_first(H, W, L):
+    HL, WL = H >> L, W >> L
+    pos = np.empty(H * W, dtype=np.int64)
+    for y in range(H):
+        for x in range(W):
+            outer = 0
+            for k in reversed(range(L)):
+                outer = outer * 4 + 2 * ((y >> k) & 1) + ((x >> k) & 1)
+            pos[y * W + x] = outer * (HL * WL) + (y >> L) * WL + (x >> L)
+    return pos
+
+
+_orig_rope = ob.apply_rope
+_orig_attention = ob.attention
+
+MUTATIONS = [
+    ("layer_norm unbiased variance", ob, "layer_norm", _ln_unbiased, pins.test_layer_norm_closed_form),
+    ("layer_norm eps outside sqrt", ob, "layer_norm", _ln_eps_outside, pins.test_layer_norm_closed_form),
+    ("softmax without max shift", ob, "softmax_rows", _softmax_unshifted, pins.test_softmax_rows_sum_to_one_and_shift_invariant),
+    ("rope rotation sign", ob, "apply_rope", _rope_wrong_sign, pins.test_rope_properties),
+    ("rope pairs split by halves", ob, "apply_rope", _rope_half_split, pins.test_rope_properties),
+    ("gelu erf replaced by tanh form", ob, "gelu_erf", _gelu_erf_as_tanh, pins.test_gelu_erf_closed_form),
+    ("contiguous mask units", im, "mask_unit_windows", _mask_unit_contiguous, pins.test_block_vs_brute_on_tiny_config),
+    ("attention scale dropped", ob, "attention", _attention_no_scale, pins.test_attention_vs_torch_sdpa),
+    ("pool over adjacent rows", ob, "pool4", _pool_adjacent, pins.test_pool4_definition),
+    ("unroll coarse level first", im, "unroll_positions", _unroll_coarse_first, pins.test_mask_unit_is_spatial_block_and_pool_is_2x2_cell),
+]
+
+
+@pytest.mark.parametrize("label,mod,attr,bad,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, label, mod, attr, bad, pin):
+    monkeypatch.setattr(mod, attr, bad)
+    with pytest.raises((AssertionError, FloatingPointError)):
+        with np.errstate(over="ignore", invalid="ignore"):
+            pin()

@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for the encoder block: shapes, draws and tables.
+
+This module holds no arithmetic of the block itself. It is the one piece that
+both the HIP path's tests/benchmark and the CPU oracle read: it decides the
+shapes of the workloads and draws the random tensors, and both sides consume
+exactly the arrays it returns.
+
+Draws: numpy PCG64 (``default_rng``), one independent stream per tensor,
+keyed by (seed, fixed tensor id), so adding or dropping an optional tensor
+never shifts another tensor's values. Distributions: token inputs N(0, 1);
+weight matrices N(0, 0.02); biases N(0, 0.01); LayerNorm gamma 1 + N(0, 0.1)
+and beta N(0, 0.1). Values are drawn in float64, cast to float32, and for the
+bf16 workloads the matrices and the token input are then rounded to the
+nearest bf16 (ties to even), so both sides see identical bf16-representable
+numbers. Vectors (biases, LN parameters) and RoPE tables stay float32.
+
+Workloads (token grids, widths, heads, windows and GELU forms follow the
+pages: the Hiera plan's stage table, the SigLIP constants, the SAM3 trunk
+constants):
+
+  c1_tiny_f32      1 x 8x8 tokens, D 112, 2 heads, 4 mask units of 16, MLP 448,
+                   float32 end to end
+  c2_hiera_s0      1 x 128x128, D 112, 2 heads, 256 mask units of 64, MLP 448
+  c3a_hiera_trans  1 x 64x64 -> 32x32, D 112 -> 224, 4 heads, 64 mask units
+                   (64 kv / 16 pooled q), residual proj + 2x2 max-pool, MLP 896
+  c3b_hiera_s2     1 x 32x32, D 448, 8 heads, global, MLP 1792
+  c4_siglip_b8     8 x 32x32, D 768, 12 heads (scale 1/8), separate q/k/v,
+                   global per frame, MLP 3072, tanh-GELU
+  c5w_sam3_win     1 x 72x72, D 1024, 16 heads, 24x24 windows, axial RoPE
+                   (in-window table, 576 rows), MLP 4736
+  c5g_sam3_global  as c5w with global attention and a 5184-row RoPE table
+"""
+import numpy as np
+
+_TENSOR_IDS = {
+    "x": 0, "ln1_g": 1, "ln1_b": 2, "res_w": 3, "res_b": 4,
+    "qkv_w": 5, "qkv_b": 6, "q_w": 7, "q_b": 8, "k_w": 9, "k_b": 10,
+    "v_w": 11, "v_b": 12, "o_w": 13, "o_b": 14, "ln2_g": 15, "ln2_b": 16,
+    "fc1_w": 17, "fc1_b": 18, "fc2_w": 19, "fc2_b": 20,
+}
+
+
+def _spec(name, **kw):
+    base = dict(name=name, batch=1, n_windows=1, win_h=0, win_w=0, q_stride=1,
+                gelu="erf", eps=1e-6, scale=None, rope=False, theta=10000.0,
+                qkv="fused", dtype="bf16")
+    base.update(kw)
+    return base
+
+
+CONFIGS = {
+    "c1_tiny_f32": _spec("c1_tiny_f32", grid_h=8, grid_w=8, dim_in=112,
+                         dim_out=112, heads=2, mlp=448, mode="mask_unit",
+                         n_windows=4, dtype="f32"),
+    "c2_hiera_s0": _spec("c2_hiera_s0", grid_h=128, grid_w=128, dim_in=112,
+                         dim_out=112, heads=2, mlp=448, mode="mask_unit",
+                         n_windows=256),
+    "c3a_hiera_trans": _spec("c3a_hiera_trans", grid_h=64, grid_w=64,
+                             dim_in=112, dim_out=224, heads=4, mlp=896,
+                             mode="mask_unit", n_windows=64, q_stride=4),
+    "c3b_hiera_s2": _spec("c3b_hiera_s2", grid_h=32, grid_w=32, dim_in=448,
+                          dim_out=448, heads=8, mlp=1792, mode="global"),
+    "c4_siglip_b8": _spec("c4_siglip_b8", batch=8, grid_h=32, grid_w=32,
+                          dim_in=768, dim_out=768, heads=12, mlp=3072,
+                          mode="global", gelu="tanh", scale=0.125,
+                          qkv="separate"),
+    "c5w_sam3_win": _spec("c5w_sam3_win", grid_h=72, grid_w=72, dim_in=1024,
+                          dim_out=1024, heads=16, mlp=4736, mode="spatial",
+                          win_h=24, win_w=24, rope=True),
+    "c5g_sam3_global": _spec("c5g_sam3_global", grid_h=72, grid_w=72,
+                             dim_in=1024, dim_out=1024, heads=16, mlp=4736,
+                             mode="global", rope=True),
+}
+
+
+def derive(base, **changes):
+    """A copy of a workload spec with some fields changed (for smaller parity
+    cases of the same structure)."""
+    s = dict(base)
+    s.update(changes)
+    return s
+
+
+def bf16_round(a):
+    """Round float32 values to the nearest bfloat16 (ties to even) and return
+    them as float32. Inputs here are finite."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(a):
+    """Upper 16 bits of float32 values that are already bf16-representable."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def axial_rope_table(grid_h, grid_w, head_dim, theta):
+    """(cos, sin) table [grid_h*grid_w, head_dim/2, 2] for 2-D axial RoPE.
+
+    The SAM3 trunk loads this table as a stored per-layer tensor; its layout
+    (32 pairs per 64-wide head, first half of the pairs from the x position,
+    second half from the y position) is stated with ``apply_rope`` on the SAM3
+    page. The frequencies are the plain reading for base theta: pair j of each
+    half turns at theta^(-4j/head_dim), j < head_dim/4. Row y*grid_w + x."""
+    quarter = head_dim // 4
+    freqs = theta ** (-(np.arange(quarter, dtype=np.float64) * 4.0) / head_dim)
+    n = np.arange(grid_h * grid_w)
+    ys, xs = n // grid_w, n % grid_w
+    ang = np.concatenate([np.outer(xs, freqs), np.outer(ys, freqs)], axis=1)
+    tab = np.stack([np.cos(ang), np.sin(ang)], axis=-1)
+    return tab.astype(np.float32)
+
+
+def tensor_shapes(spec):
+    """Name -> shape of every input tensor of one block (PyTorch Linear
+    layout [out, in] for matrices)."""
+    B, N = spec["batch"], spec["grid_h"] * spec["grid_w"]
+    Di, Do, M = spec["dim_in"], spec["dim_out"], spec["mlp"]
+    s = {"x": (B, N, Di), "ln1_g": (Di,), "ln1_b": (Di,)}
+    if spec["q_stride"] == 4:
+        s.update(res_w=(Do, Di), res_b=(Do,))
+    if spec["qkv"] == "separate":
+        for p in "qkv":
+            s[p + "_w"] = (Do, Di)
+            s[p + "_b"] = (Do,)
+    else:
+        s.update(qkv_w=(3 * Do, Di), qkv_b=(3 * Do,))
+    s.update(o_w=(Do, Do), o_b=(Do,), ln2_g=(Do,), ln2_b=(Do,),
+             fc1_w=(M, Do), fc1_b=(M,), fc2_w=(Do, M), fc2_b=(Do,))
+    return s
+
+
+def make_inputs(spec, seed=0, qk_gain=1.0):
+    """Draw every input of one block as float32 numpy arrays (bf16-rounded
+    where the workload is bf16). ``qk_gain`` scales the query and key weight
+    rows after drawing (the sharp-softmax stress variant); 1.0 is the plain
+    workload. Adds the RoPE table under "rope" when the workload uses it."""
+    out = {}
+    bf16 = spec["dtype"] == "bf16"
+    Do = spec["dim_out"]
+    for name, shape in tensor_shapes(spec).items():
+        rng = np.random.default_rng([seed, _TENSOR_IDS[name]])
+        if name == "x":
+            a = rng.standard_normal(shape)
+        elif name.endswith("_w"):
+            a = rng.normal(0.0, 0.02, shape)
+        elif name.endswith("_g"):
+            a = 1.0 + rng.normal(0.0, 0.1, shape)
+        elif name.endswith("_b") and name.startswith("ln"):
+            a = rng.normal(0.0, 0.1, shape)
+        else:
+            a = rng.normal(0.0, 0.01, shape)
+        if qk_gain != 1.0:
+            if name == "qkv_w":
+                a[:2 * Do] *= qk_gain
+            elif name in ("q_w", "k_w"):
+                a *= qk_gain
+        a = a.astype(np.float32)
+        if bf16 and (name == "x" or name.endswith("_w")):
+            a = bf16_round(a)
+        out[name] = a
+    if spec["rope"]:
+        hd = Do // spec["heads"]
+        if spec["mode"] == "spatial":
+            out["rope"] = axial_rope_table(spec["win_h"], spec["win_w"], hd, spec["theta"])
+        else:
+            out["rope"] = axial_rope_table(spec["grid_h"], spec["grid_w"], hd, spec["theta"])
+    return out
+
+
+def out_tokens(spec):
+    """Tokens per frame leaving the block (4x fewer at a pooled transition)."""
+    return spec["grid_h"] * spec["grid_w"] // spec["q_stride"]
