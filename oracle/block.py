@@ -201,3 +201,60 @@ def block_forward(x, w, spec):
                           ("u", u), ("mlp_branch", mlp_branch), ("y", y)):
             seams[name].append(val)
     return {k: np.stack(v) for k, v in seams.items() if v}
+
+
+def block_forward_rows(x, w, spec, rows):
+    """The same block, evaluated only at the output token rows ``rows`` of
+    every frame (for full-size workloads, where all rows would take too long).
+
+    Exactly the steps of ``block_forward``: LN1 and the projections run over
+    every token (keys and values of every window are needed), attention and
+    everything after it only for the chosen query rows. Returns the seams
+    restricted to those rows: qkv/h rows are not returned; ctx, attn_branch,
+    r, x1, h2, u, mlp_branch, y are [B, len(rows), cols]."""
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+    x = f64(x)
+    rows = np.asarray(rows, dtype=np.int64)
+    D, heads = spec["dim_out"], spec["heads"]
+    hd = D // heads
+    scale = spec.get("scale") or hd ** -0.5
+    gelu = gelu_erf if spec["gelu"] == "erf" else gelu_tanh
+    wins = windows_for(spec)
+    owner = {}
+    for wi, (qi, _) in enumerate(wins):
+        for pos, t in enumerate(qi):
+            owner[int(t)] = (wi, pos)
+    out = {k: [] for k in ("r", "ctx", "attn_branch", "x1", "h2", "u", "mlp_branch", "y")}
+    for b in range(x.shape[0]):
+        xb = x[b]
+        h = layer_norm(xb, f64(w["ln1_g"]), f64(w["ln1_b"]), spec["eps"])
+        if spec["q_stride"] == 4:
+            r = pool4(linear(h, w["res_w"], f64(w["res_b"])))[rows]
+        else:
+            r = xb[rows]
+        if spec.get("qkv", "fused") == "separate":
+            qkv = np.concatenate([linear(h, w["q_w"], f64(w["q_b"])),
+                                  linear(h, w["k_w"], f64(w["k_b"])),
+                                  linear(h, w["v_w"], f64(w["v_b"]))], axis=1)
+        else:
+            qkv = linear(h, w["qkv_w"], f64(w["qkv_b"]))
+        if spec.get("rope"):
+            qkv[:, :2 * D] = apply_rope(qkv[:, :2 * D], f64(w["rope"]), rope_rows_for(spec), hd)
+        q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
+        if spec["q_stride"] == 4:
+            q = pool4(q)
+        ctx = np.zeros((len(rows), D))
+        for a, t in enumerate(rows):
+            wi, _ = owner[int(t)]
+            ki = wins[wi][1]
+            ctx[a] = attention(q[[t]], k[ki], v[ki], [(np.array([0]), np.arange(len(ki)))],
+                               heads, scale)[0]
+        ab = linear(ctx, w["o_w"], f64(w["o_b"]))
+        x1 = r + ab
+        h2 = layer_norm(x1, f64(w["ln2_g"]), f64(w["ln2_b"]), spec["eps"])
+        u = gelu(linear(h2, w["fc1_w"], f64(w["fc1_b"])))
+        mb = linear(u, w["fc2_w"], f64(w["fc2_b"]))
+        for name, val in (("r", r), ("ctx", ctx), ("attn_branch", ab), ("x1", x1), ("h2", h2),
+                          ("u", u), ("mlp_branch", mb), ("y", x1 + mb)):
+            out[name].append(val)
+    return {k: np.stack(v) for k, v in out.items()}

@@ -342,3 +342,22 @@ def test_block_rope_windowed_locality():
     changed = np.where(np.any(y0 != y1, axis=1))[0]
     ys, xs = np.divmod(changed, 8)
     assert len(changed) == 16 and ys.max() < 4 and xs.max() < 4
+
+
+def test_block_rows_equals_full_block():
+    # the sampled-row evaluation used at full sizes is the same computation
+    for name, kw in (("c3a_hiera_trans", dict(grid_h=8, grid_w=8, dim_in=8, dim_out=16, heads=2,
+                                               mlp=32, n_windows=4)),
+                     ("c5w_sam3_win", dict(grid_h=8, grid_w=8, win_h=4, win_w=4, dim_in=16,
+                                           dim_out=16, heads=1, mlp=32)),
+                     ("c4_siglip_b8", dict(batch=2, grid_h=3, grid_w=4, dim_in=16, dim_out=16,
+                                           heads=2, mlp=32))):
+        spec = synth.derive(synth.CONFIGS[name], dtype="f32", **kw)
+        inp = synth.make_inputs(spec, seed=9)
+        if spec["rope"]:
+            inp["rope"] = synth.axial_rope_table(4, 4, 16, 10000.0)
+        full = ob.block_forward(inp["x"], inp, spec)
+        rows = np.array([0, 3, 5, 11])
+        part = ob.block_forward_rows(inp["x"], inp, spec, rows)
+        for k, v in part.items():
+            np.testing.assert_allclose(v, full[k][:, rows], atol=1e-12, err_msg=k)

@@ -1,0 +1,482 @@
+// C ABI of the encoder block: argument validation, the host-side plan
+// (workspace layout), and the kernel sequence of one forward. No device
+// memory is allocated here; every buffer comes from the caller.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/vit_block.h"
+#include "launch.h"
+
+#define VIT_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+vit_status fail(vit_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+vit_status ok() { return VIT_OK; }
+
+vit_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return VIT_OK;
+  return fail(VIT_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return an && bn && x < y + bn && y < x + an;
+}
+
+}  // namespace
+
+struct vit_block_plan {
+  vit_block_desc d;
+  int n_in, n_out, head_dim;
+  int64_t m_in, m_out;
+  size_t esize;
+  // workspace layout (byte offsets)
+  size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, ws_bytes;
+};
+
+static vit_status validate_desc(const vit_block_desc* d) {
+  if (!d) return fail(VIT_ERR_INVALID_ARG, "desc is NULL");
+  if (d->act_dtype != VIT_DTYPE_F32 && d->act_dtype != VIT_DTYPE_BF16)
+    return fail(VIT_ERR_INVALID_ARG, "act_dtype %d is not VIT_DTYPE_F32 or VIT_DTYPE_BF16", d->act_dtype);
+  if (d->batch < 1) return fail(VIT_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
+  if (d->grid_h < 1 || d->grid_w < 1) return fail(VIT_ERR_INVALID_ARG, "grid %dx%d is empty", d->grid_h, d->grid_w);
+  const int64_t n_in = (int64_t)d->grid_h * d->grid_w;
+  if (d->dim_in < 8 || d->dim_out < 8 || d->mlp_hidden < 8 || d->dim_in % 8 || d->dim_out % 8 || d->mlp_hidden % 8)
+    return fail(VIT_ERR_INVALID_ARG, "dim_in %d, dim_out %d, mlp_hidden %d must be positive multiples of 8",
+                d->dim_in, d->dim_out, d->mlp_hidden);
+  if (d->heads < 1 || d->dim_out % d->heads)
+    return fail(VIT_ERR_INVALID_ARG, "heads %d must divide dim_out %d", d->heads, d->dim_out);
+  const int hd = d->dim_out / d->heads;
+  if (hd % 8) return fail(VIT_ERR_UNSUPPORTED, "head_dim %d must be a multiple of 8", hd);
+  if (hd > 64) return fail(VIT_ERR_UNSUPPORTED, "head_dim %d > 64 is not supported", hd);
+  if (d->q_stride != 1 && d->q_stride != 4) return fail(VIT_ERR_INVALID_ARG, "q_stride must be 1 or 4 (got %d)", d->q_stride);
+  if (d->q_stride == 1 && d->dim_in != d->dim_out)
+    return fail(VIT_ERR_INVALID_ARG, "dim_in %d != dim_out %d needs the q_stride-4 residual projection", d->dim_in, d->dim_out);
+  if (d->q_stride == 4 && n_in % 4) return fail(VIT_ERR_INVALID_ARG, "q_stride 4 needs a token count divisible by 4");
+  const int64_t n_out = n_in / d->q_stride;
+  switch (d->attn_mode) {
+    case VIT_ATTN_GLOBAL: break;
+    case VIT_ATTN_MASK_UNIT:
+      if (d->n_windows < 1 || n_in % d->n_windows || n_out % d->n_windows)
+        return fail(VIT_ERR_INVALID_ARG, "n_windows %d must divide the %lld input and %lld output tokens", d->n_windows,
+                    (long long)n_in, (long long)n_out);
+      break;
+    case VIT_ATTN_SPATIAL:
+      if (d->win_h < 1 || d->win_w < 1 || d->grid_h % d->win_h || d->grid_w % d->win_w)
+        return fail(VIT_ERR_INVALID_ARG, "window %dx%d must tile the %dx%d grid", d->win_h, d->win_w, d->grid_h, d->grid_w);
+      if (d->q_stride != 1) return fail(VIT_ERR_UNSUPPORTED, "q_stride 4 with SPATIAL windows is not supported");
+      break;
+    default: return fail(VIT_ERR_INVALID_ARG, "attn_mode %d is not a VIT_ATTN_* value", d->attn_mode);
+  }
+  if (d->gelu != VIT_GELU_ERF && d->gelu != VIT_GELU_TANH) return fail(VIT_ERR_INVALID_ARG, "gelu %d is not a VIT_GELU_* value", d->gelu);
+  if (d->qkv_layout != VIT_QKV_FUSED && d->qkv_layout != VIT_QKV_SEPARATE)
+    return fail(VIT_ERR_INVALID_ARG, "qkv_layout %d is not a VIT_QKV_* value", d->qkv_layout);
+  if (d->rope != VIT_ROPE_NONE && d->rope != VIT_ROPE_AXIAL_TABLE) return fail(VIT_ERR_INVALID_ARG, "rope %d is not a VIT_ROPE_* value", d->rope);
+  if (d->rope == VIT_ROPE_AXIAL_TABLE) {
+    if (d->attn_mode == VIT_ATTN_MASK_UNIT) return fail(VIT_ERR_UNSUPPORTED, "RoPE with mask-unit windows is not supported");
+    if (d->q_stride != 1) return fail(VIT_ERR_UNSUPPORTED, "RoPE with q_stride 4 is not supported");
+    if (hd % 4) return fail(VIT_ERR_INVALID_ARG, "RoPE needs head_dim %% 4 == 0 (head_dim %d)", hd);
+    const int64_t want = d->attn_mode == VIT_ATTN_SPATIAL ? (int64_t)d->win_h * d->win_w : n_in;
+    if (d->rope_rows != want)
+      return fail(VIT_ERR_INVALID_ARG, "rope_rows %d, expected %lld (one row per %s token)", d->rope_rows, (long long)want,
+                  d->attn_mode == VIT_ATTN_SPATIAL ? "in-window" : "grid");
+  }
+  if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps)) return fail(VIT_ERR_INVALID_ARG, "ln_eps must be positive and finite");
+  if (!(d->attn_scale >= 0.f) || !std::isfinite(d->attn_scale)) return fail(VIT_ERR_INVALID_ARG, "attn_scale must be >= 0 and finite");
+  const int64_t widest = std::max<int64_t>(std::max<int64_t>(3LL * d->dim_out, d->mlp_hidden), d->dim_in);
+  if ((int64_t)d->batch * n_in * widest >= (1LL << 40) || (int64_t)d->batch * n_in >= (1LL << 31))
+    return fail(VIT_ERR_UNSUPPORTED, "problem too large");
+  return VIT_OK;
+}
+
+VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out) {
+  if (!out) return fail(VIT_ERR_INVALID_ARG, "out handle pointer is NULL");
+  vit_status st = validate_desc(desc);
+  if (st != VIT_OK) return st;
+  vit_block_plan* p = new (std::nothrow) vit_block_plan();
+  if (!p) return fail(VIT_ERR_INVALID_ARG, "out of host memory");
+  p->d = *desc;
+  p->n_in = desc->grid_h * desc->grid_w;
+  p->n_out = p->n_in / desc->q_stride;
+  p->head_dim = desc->dim_out / desc->heads;
+  p->m_in = (int64_t)desc->batch * p->n_in;
+  p->m_out = (int64_t)desc->batch * p->n_out;
+  p->esize = desc->act_dtype == VIT_DTYPE_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](int64_t rows, int64_t cols) {
+    const size_t at = o;
+    o += round256((size_t)rows * cols * p->esize);
+    return at;
+  };
+  const vit_block_desc& d = *desc;
+  p->off_h = take(p->m_in, d.dim_in);
+  p->off_qkv = take(p->m_in, 3LL * d.dim_out);
+  p->off_rp = d.q_stride == 4 ? take(p->m_in, d.dim_out) : 0;
+  p->off_r = d.q_stride == 4 ? take(p->m_out, d.dim_out) : 0;
+  p->off_ctx = take(p->m_out, d.dim_out);
+  p->off_x1 = take(p->m_out, d.dim_out);
+  p->off_h2 = take(p->m_out, d.dim_out);
+  p->off_u = take(p->m_out, d.mlp_hidden);
+  p->ws_bytes = o;
+  *out = p;
+  return ok();
+}
+
+VIT_API vit_status vit_block_workspace_size(vit_block_t plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(VIT_ERR_INVALID_ARG, "plan or bytes pointer is NULL");
+  *bytes = plan->ws_bytes;
+  return ok();
+}
+
+VIT_API vit_status vit_block_destroy(vit_block_t plan) {
+  delete plan;
+  return ok();
+}
+
+VIT_API const char* vit_last_error(void) { return g_err.c_str(); }
+
+static vit_status check_weights(const vit_block_plan* p, const vit_block_weights* w) {
+  if (!w) return fail(VIT_ERR_INVALID_ARG, "weights struct is NULL");
+  const vit_block_desc& d = p->d;
+  struct Need {
+    const void* ptr;
+    const char* name;
+    bool needed;
+  } need[] = {
+      {w->ln1_gamma, "ln1_gamma", true},
+      {w->ln1_beta, "ln1_beta", true},
+      {w->w_res, "w_res", d.q_stride == 4},
+      {w->b_res, "b_res", d.q_stride == 4},
+      {w->w_qkv, "w_qkv", d.qkv_layout == VIT_QKV_FUSED},
+      {w->b_qkv, "b_qkv", d.qkv_layout == VIT_QKV_FUSED},
+      {w->w_q, "w_q", d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->b_q, "b_q", d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->w_k, "w_k", d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->b_k, "b_k", d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->w_v, "w_v", d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->b_v, "b_v", d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->w_o, "w_o", true},
+      {w->b_o, "b_o", true},
+      {w->ln2_gamma, "ln2_gamma", true},
+      {w->ln2_beta, "ln2_beta", true},
+      {w->w_fc1, "w_fc1", true},
+      {w->b_fc1, "b_fc1", true},
+      {w->w_fc2, "w_fc2", true},
+      {w->b_fc2, "b_fc2", true},
+      {w->rope_table, "rope_table", d.rope == VIT_ROPE_AXIAL_TABLE},
+  };
+  for (const Need& n : need) {
+    if (!n.needed) continue;
+    if (!n.ptr) return fail(VIT_ERR_INVALID_ARG, "weight %s is NULL", n.name);
+    if (!aligned16(n.ptr)) return fail(VIT_ERR_INVALID_ARG, "weight %s is not 16-byte aligned", n.name);
+  }
+  return VIT_OK;
+}
+
+static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
+                               const vit_block_seams* seams, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(VIT_ERR_INVALID_ARG, "plan is NULL");
+  const vit_block_plan& P = *plan;
+  const vit_block_desc& d = P.d;
+  vit_status st = check_weights(&P, w);
+  if (st != VIT_OK) return st;
+  if (!x || !y) return fail(VIT_ERR_INVALID_ARG, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(VIT_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  if (ws_bytes < P.ws_bytes) return fail(VIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, P.ws_bytes);
+  if (P.ws_bytes && !ws) return fail(VIT_ERR_WORKSPACE, "workspace is NULL");
+  if (ws && !aligned16(ws)) return fail(VIT_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const size_t x_bytes = (size_t)P.m_in * d.dim_in * P.esize;
+  const size_t y_bytes = (size_t)P.m_out * d.dim_out * P.esize;
+  if (x == y) {
+    if (d.q_stride != 1) return fail(VIT_ERR_INVALID_ARG, "y == x is allowed only with q_stride 1");
+  } else if (overlaps(x, x_bytes, y, y_bytes)) {
+    return fail(VIT_ERR_INVALID_ARG, "x and y overlap");
+  }
+  if (overlaps(ws, P.ws_bytes, y, y_bytes) || overlaps(ws, P.ws_bytes, x, x_bytes))
+    return fail(VIT_ERR_INVALID_ARG, "workspace overlaps x or y");
+  vit_block_seams S;
+  std::memset(&S, 0, sizeof S);
+  if (seams) {
+    S = *seams;
+    void* const all[] = {S.h, S.qkv, S.q_pooled, S.r, S.ctx, S.attn_branch, S.x1, S.h2, S.u, S.mlp_branch};
+    for (void* s : all)
+      if (s && !aligned16(s)) return fail(VIT_ERR_INVALID_ARG, "seam buffers must be 16-byte aligned");
+  }
+
+  const vit::DType dt = d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  void* h = S.h ? S.h : base + P.off_h;
+  void* qkv = S.qkv ? S.qkv : base + P.off_qkv;
+  void* ctx = S.ctx ? S.ctx : base + P.off_ctx;
+  void* x1 = S.x1 ? S.x1 : base + P.off_x1;
+  void* h2 = S.h2 ? S.h2 : base + P.off_h2;
+  void* u = S.u ? S.u : base + P.off_u;
+  const int Di = d.dim_in, Do = d.dim_out, F = d.mlp_hidden, hd = P.head_dim;
+  hipError_t e;
+
+  // 1. LN1
+  e = vit::launch_layernorm(x, h, w->ln1_gamma, w->ln1_beta, P.m_in, Di, d.ln_eps, dt, s);
+  if ((st = device_status(e, "layernorm (LN1)")) != VIT_OK) return st;
+
+  // 2. qkv projection (+ bias, + RoPE)
+  vit::GemmArgs g;
+  g.A = h;
+  g.lda = Di;
+  g.M = (int)P.m_in;
+  g.N = 3 * Do;
+  g.K = Di;
+  g.C = qkv;
+  g.ldc = 3 * Do;
+  if (d.qkv_layout == VIT_QKV_FUSED) {
+    g.W[0] = w->w_qkv;
+    g.bias[0] = w->b_qkv;
+    g.seg_cols = 3 * Do;
+  } else {
+    g.W[0] = w->w_q;
+    g.W[1] = w->w_k;
+    g.W[2] = w->w_v;
+    g.bias[0] = w->b_q;
+    g.bias[1] = w->b_k;
+    g.bias[2] = w->b_v;
+    g.seg_cols = Do;
+  }
+  if (d.rope == VIT_ROPE_AXIAL_TABLE) {
+    g.epi = vit::EPI_BIAS_ROPE;
+    g.rope = w->rope_table;
+    g.rope_cols = 2 * Do;
+    g.head_dim = hd;
+    g.rope_mode = d.attn_mode == VIT_ATTN_SPATIAL ? 1 : 0;
+    g.tokens_per_frame = P.n_in;
+    g.grid_w = d.grid_w;
+    g.win_h = d.attn_mode == VIT_ATTN_SPATIAL ? d.win_h : 1;
+    g.win_w = d.attn_mode == VIT_ATTN_SPATIAL ? d.win_w : 1;
+  } else {
+    g.epi = vit::EPI_BIAS;
+  }
+  e = vit::launch_gemm(g, dt, s);
+  if ((st = device_status(e, "gemm (qkv)")) != VIT_OK) return st;
+
+  // 3. residual: x, or pool4(h W_res^T + b_res) at a transition
+  const void* r = x;
+  if (d.q_stride == 4) {
+    vit::GemmArgs gr;
+    gr.A = h;
+    gr.lda = Di;
+    gr.M = (int)P.m_in;
+    gr.N = Do;
+    gr.K = Di;
+    gr.W[0] = w->w_res;
+    gr.bias[0] = w->b_res;
+    gr.seg_cols = Do;
+    gr.C = base + P.off_rp;
+    gr.ldc = Do;
+    gr.epi = vit::EPI_BIAS;
+    e = vit::launch_gemm(gr, dt, s);
+    if ((st = device_status(e, "gemm (residual projection)")) != VIT_OK) return st;
+    void* rr = S.r ? S.r : base + P.off_r;
+    e = vit::launch_pool4(base + P.off_rp, Do, rr, Do, d.batch, P.n_in, Do, dt, s);
+    if ((st = device_status(e, "pool4 (residual)")) != VIT_OK) return st;
+    r = rr;
+    if (S.q_pooled) {
+      e = vit::launch_pool4(qkv, 3LL * Do, S.q_pooled, Do, d.batch, P.n_in, Do, dt, s);
+      if ((st = device_status(e, "pool4 (q seam)")) != VIT_OK) return st;
+    }
+  } else if (S.r) {
+    e = hipMemcpyAsync(S.r, x, x_bytes, hipMemcpyDeviceToDevice, s);
+    if ((st = device_status(e, "copy (r seam)")) != VIT_OK) return st;
+  }
+
+  // 4. attention
+  vit::AttnArgs a;
+  a.qkv = qkv;
+  a.ld_qkv = 3 * Do;
+  a.ctx = ctx;
+  a.ld_ctx = Do;
+  a.batch = d.batch;
+  a.tokens_in = P.n_in;
+  a.tokens_out = P.n_out;
+  a.dim = Do;
+  a.heads = d.heads;
+  a.head_dim = hd;
+  a.mode = d.attn_mode;
+  a.n_windows = d.n_windows;
+  a.grid_w = d.grid_w;
+  a.win_h = d.win_h;
+  a.win_w = d.win_w;
+  a.q_stride = d.q_stride;
+  a.scale = d.attn_scale > 0.f ? d.attn_scale : 1.0f / std::sqrt((float)hd);
+  e = vit::launch_attention(a, dt, s);
+  if ((st = device_status(e, "attention")) != VIT_OK) return st;
+
+  // 5. x1 = r + ctx W_o^T + b_o
+  vit::GemmArgs go;
+  go.A = ctx;
+  go.lda = Do;
+  go.M = (int)P.m_out;
+  go.N = Do;
+  go.K = Do;
+  go.W[0] = w->w_o;
+  go.bias[0] = w->b_o;
+  go.seg_cols = Do;
+  go.C = x1;
+  go.ldc = Do;
+  go.epi = vit::EPI_BIAS_RES;
+  go.res = r;
+  go.ldres = Do;
+  go.branch = S.attn_branch;
+  go.ldbranch = Do;
+  e = vit::launch_gemm(go, dt, s);
+  if ((st = device_status(e, "gemm (out projection)")) != VIT_OK) return st;
+
+  // 6. LN2
+  e = vit::launch_layernorm(x1, h2, w->ln2_gamma, w->ln2_beta, P.m_out, Do, d.ln_eps, dt, s);
+  if ((st = device_status(e, "layernorm (LN2)")) != VIT_OK) return st;
+
+  // 7. u = GELU(h2 W_1^T + b_1)
+  vit::GemmArgs g1;
+  g1.A = h2;
+  g1.lda = Do;
+  g1.M = (int)P.m_out;
+  g1.N = F;
+  g1.K = Do;
+  g1.W[0] = w->w_fc1;
+  g1.bias[0] = w->b_fc1;
+  g1.seg_cols = F;
+  g1.C = u;
+  g1.ldc = F;
+  g1.epi = d.gelu == VIT_GELU_ERF ? vit::EPI_GELU_ERF : vit::EPI_GELU_TANH;
+  e = vit::launch_gemm(g1, dt, s);
+  if ((st = device_status(e, "gemm (fc1)")) != VIT_OK) return st;
+
+  // 8. y = x1 + u W_2^T + b_2
+  vit::GemmArgs g2;
+  g2.A = u;
+  g2.lda = F;
+  g2.M = (int)P.m_out;
+  g2.N = Do;
+  g2.K = F;
+  g2.W[0] = w->w_fc2;
+  g2.bias[0] = w->b_fc2;
+  g2.seg_cols = Do;
+  g2.C = y;
+  g2.ldc = Do;
+  g2.epi = vit::EPI_BIAS_RES;
+  g2.res = x1;
+  g2.ldres = Do;
+  g2.branch = S.mlp_branch;
+  g2.ldbranch = Do;
+  e = vit::launch_gemm(g2, dt, s);
+  if ((st = device_status(e, "gemm (fc2)")) != VIT_OK) return st;
+  return ok();
+}
+
+VIT_API vit_status vit_block_forward(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(plan, w, x, y, nullptr, workspace, workspace_bytes, stream);
+}
+
+VIT_API vit_status vit_block_forward_seams(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
+                                           const vit_block_seams* seams, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (!seams) return fail(VIT_ERR_INVALID_ARG, "seams struct is NULL");
+  return forward_impl(plan, w, x, y, seams, workspace, workspace_bytes, stream);
+}
+
+// ---- single steps
+
+static vit_status check_dtype(int32_t dtype) {
+  if (dtype != VIT_DTYPE_F32 && dtype != VIT_DTYPE_BF16) return fail(VIT_ERR_INVALID_ARG, "dtype %d is not a VIT_DTYPE_* value", dtype);
+  return VIT_OK;
+}
+
+VIT_API vit_status vit_layernorm(const void* x, void* y, const float* gamma, const float* beta, int64_t rows,
+                                 int32_t dim, float eps, int32_t dtype, void* stream) {
+  vit_status st = check_dtype(dtype);
+  if (st != VIT_OK) return st;
+  if (rows < 0) return fail(VIT_ERR_INVALID_ARG, "rows < 0");
+  if (dim < 8 || dim % 8 || dim > 8192) return fail(VIT_ERR_INVALID_ARG, "dim %d must be a multiple of 8 in [8, 8192]", dim);
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(VIT_ERR_INVALID_ARG, "eps must be positive and finite");
+  if (rows == 0) return ok();
+  if (!x || !y || !gamma || !beta) return fail(VIT_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta))
+    return fail(VIT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t bytes = (size_t)rows * dim * (dtype == VIT_DTYPE_BF16 ? 2 : 4);
+  if (x != y && overlaps(x, bytes, y, bytes)) return fail(VIT_ERR_INVALID_ARG, "x and y overlap");
+  const vit::DType dt = dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32;
+  st = device_status(vit::launch_layernorm(x, y, gamma, beta, rows, dim, eps, dt, (hipStream_t)stream), "layernorm");
+  return st == VIT_OK ? ok() : st;
+}
+
+static vit_status permute_common(const void* x, void* y, int32_t batch, int32_t gh, int32_t gw, int32_t levels,
+                                 int32_t channels, int32_t dtype, void* stream, bool inverse) {
+  vit_status st = check_dtype(dtype);
+  if (st != VIT_OK) return st;
+  if (batch < 0 || gh < 1 || gw < 1) return fail(VIT_ERR_INVALID_ARG, "bad batch or grid");
+  if (levels < 0 || levels > 8) return fail(VIT_ERR_INVALID_ARG, "levels %d outside 0..8", levels);
+  if (gh % (1 << levels) || gw % (1 << levels))
+    return fail(VIT_ERR_INVALID_ARG, "grid %dx%d not divisible by 2^%d", gh, gw, levels);
+  if (channels < 8 || channels % 8) return fail(VIT_ERR_INVALID_ARG, "channels %d must be a positive multiple of 8", channels);
+  if (batch == 0) return ok();
+  if (!x || !y) return fail(VIT_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(VIT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t bytes = (size_t)batch * gh * gw * channels * (dtype == VIT_DTYPE_BF16 ? 2 : 4);
+  if (overlaps(x, bytes, y, bytes)) return fail(VIT_ERR_INVALID_ARG, "x and y overlap");
+  const vit::DType dt = dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32;
+  st = device_status(vit::launch_permute(x, y, batch, gh, gw, levels, channels, inverse, dt, (hipStream_t)stream),
+                     inverse ? "reroll" : "unroll");
+  return st == VIT_OK ? ok() : st;
+}
+
+VIT_API vit_status vit_unroll(const void* x, void* y, int32_t batch, int32_t grid_h, int32_t grid_w, int32_t levels,
+                              int32_t channels, int32_t dtype, void* stream) {
+  return permute_common(x, y, batch, grid_h, grid_w, levels, channels, dtype, stream, false);
+}
+
+VIT_API vit_status vit_reroll(const void* x, void* y, int32_t batch, int32_t grid_h, int32_t grid_w, int32_t levels,
+                              int32_t channels, int32_t dtype, void* stream) {
+  return permute_common(x, y, batch, grid_h, grid_w, levels, channels, dtype, stream, true);
+}
+
+VIT_API vit_status vit_pool4(const void* x, int64_t x_row_stride, void* y, int64_t y_row_stride, int32_t batch,
+                             int32_t tokens, int32_t channels, int32_t dtype, void* stream) {
+  vit_status st = check_dtype(dtype);
+  if (st != VIT_OK) return st;
+  if (batch < 0 || tokens < 0 || tokens % 4) return fail(VIT_ERR_INVALID_ARG, "tokens must be a non-negative multiple of 4");
+  if (channels < 8 || channels % 8) return fail(VIT_ERR_INVALID_ARG, "channels %d must be a positive multiple of 8", channels);
+  if (x_row_stride < channels || y_row_stride < channels || x_row_stride % 8 || y_row_stride % 8)
+    return fail(VIT_ERR_INVALID_ARG, "row strides must be multiples of 8 and >= channels");
+  if (batch == 0 || tokens == 0) return ok();
+  if (!x || !y) return fail(VIT_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(VIT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t es = dtype == VIT_DTYPE_BF16 ? 2 : 4;
+  if (overlaps(x, (size_t)batch * tokens * x_row_stride * es, y, (size_t)batch * (tokens / 4) * y_row_stride * es))
+    return fail(VIT_ERR_INVALID_ARG, "x and y overlap");
+  const vit::DType dt = dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32;
+  st = device_status(vit::launch_pool4(x, x_row_stride, y, y_row_stride, batch, tokens, channels, dt, (hipStream_t)stream),
+                     "pool4");
+  return st == VIT_OK ? ok() : st;
+}

@@ -1,0 +1,65 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vit {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+enum Epilogue {
+  EPI_BIAS = 0,        // C = acc + bias
+  EPI_BIAS_ROPE = 1,   // C = rope(acc + bias) on columns < rope_cols
+  EPI_GELU_ERF = 2,    // C = gelu_erf(acc + bias)
+  EPI_GELU_TANH = 3,   // C = gelu_tanh(acc + bias)
+  EPI_BIAS_RES = 4,    // C = res + (acc + bias); branch = acc + bias if set
+};
+
+// C[M, N] = epilogue(A[M, K] * W[N, K]^T + bias). W and bias may be split
+// into up to three column segments of seg_cols columns each (separate q/k/v
+// weights); with one segment seg_cols = N.
+struct GemmArgs {
+  const void* A = nullptr;
+  int64_t lda = 0;
+  const void* W[3] = {nullptr, nullptr, nullptr};
+  const float* bias[3] = {nullptr, nullptr, nullptr};
+  int seg_cols = 0;
+  void* C = nullptr;
+  int64_t ldc = 0;
+  int M = 0, N = 0, K = 0;
+  int epi = EPI_BIAS;
+  // EPI_BIAS_RES
+  const void* res = nullptr;
+  int64_t ldres = 0;
+  void* branch = nullptr;
+  int64_t ldbranch = 0;
+  // EPI_BIAS_ROPE: table [rows, head_dim/2, 2]; token t of a frame uses row
+  // t (rope_mode 0) or its in-window raster index (rope_mode 1).
+  const float* rope = nullptr;
+  int rope_cols = 0, head_dim = 0, rope_mode = 0;
+  int tokens_per_frame = 1, grid_w = 1, win_h = 1, win_w = 1;
+};
+hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s);
+
+enum AttnMode { ATTN_GLOBAL = 0, ATTN_MASK_UNIT = 1, ATTN_SPATIAL = 2 };
+
+struct AttnArgs {
+  const void* qkv = nullptr;  // [B * tokens_in, 3 * dim], rows [q | k | v]
+  int64_t ld_qkv = 0;
+  void* ctx = nullptr;        // [B * tokens_out, dim]
+  int64_t ld_ctx = 0;
+  int batch = 1, tokens_in = 0, tokens_out = 0, dim = 0, heads = 1, head_dim = 0;
+  int mode = ATTN_GLOBAL, n_windows = 1, grid_w = 1, win_h = 1, win_w = 1;
+  int q_stride = 1;
+  float scale = 1.f;
+};
+hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s);
+
+hipError_t launch_layernorm(const void* x, void* y, const float* g, const float* b,
+                            int64_t rows, int dim, float eps, DType dt, hipStream_t s);
+hipError_t launch_permute(const void* x, void* y, int batch, int grid_h, int grid_w,
+                          int levels, int channels, bool inverse, DType dt, hipStream_t s);
+hipError_t launch_pool4(const void* x, int64_t x_stride, void* y, int64_t y_stride,
+                        int batch, int tokens, int channels, DType dt, hipStream_t s);
+
+}  // namespace vit

@@ -1,0 +1,206 @@
+// Bandwidth-bound row kernels: LayerNorm, Hiera unroll/reroll permutes and
+// the 4x max-pool. Each row is handled by a group of G lanes that move it in
+// 16-byte vectors, so every global access is a coalesced 16-byte load/store.
+#include "common.h"
+#include "launch.h"
+
+#include <type_traits>
+
+namespace vit {
+
+// Row LayerNorm (SAM3 layer_norm_rows): mean, biased variance over the row,
+// (x - mean) / sqrt(var + eps) * gamma + beta. Statistics in float32, two
+// passes over the values held in registers.
+template <typename T, int G, int V>
+__global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x, T* __restrict__ y,
+                                                        const float* __restrict__ gamma,
+                                                        const float* __restrict__ beta,
+                                                        int64_t rows, int dim, float eps) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x % G;
+  const int64_t row = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
+  if (row >= rows) return;  // whole group exits together (G divides 64)
+  const int nvec = dim / VN;
+  const T* xr = x + row * dim;
+  float v[V][VN];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int vi = lane + i * G;
+    if (vi < nvec) {
+      unpack16<T>(ld16(xr + vi * VN), v[i]);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) s += v[i][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) v[i][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int m = G / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+  const float mean = s / (float)dim;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    if (lane + i * G < nvec) {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        const float d = v[i][e] - mean;
+        q += d * d;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = G / 2; m > 0; m >>= 1) q += __shfl_xor(q, m, 64);
+  const float inv = 1.0f / sqrtf(q / (float)dim + eps);
+  T* yr = y + row * dim;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int vi = lane + i * G;
+    if (vi < nvec) {
+      float o[VN];
+#pragma unroll
+      for (int e = 0; e < VN; e += 4) {
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(gamma + vi * VN + e);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(beta + vi * VN + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[e + j] = (v[i][e + j] - mean) * inv * g4[j] + b4[j];
+      }
+      st16(yr + vi * VN, pack16<T>(o));
+    }
+  }
+}
+
+template <typename T, int G, int V>
+static hipError_t ln_launch(const void* x, void* y, const float* g, const float* b, int64_t rows,
+                            int dim, float eps, hipStream_t s) {
+  const int rpb = 256 / G;
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  hipLaunchKernelGGL((layernorm_kernel<T, G, V>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const T*)x, (T*)y, g, b, rows, dim, eps);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t ln_dispatch(const void* x, void* y, const float* g, const float* b, int64_t rows,
+                              int dim, float eps, hipStream_t s) {
+  const int nvec = dim / Vec<T>::N;
+  if (nvec <= 4) return ln_launch<T, 4, 1>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 8) return ln_launch<T, 8, 1>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 16) return ln_launch<T, 16, 1>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 32) return ln_launch<T, 32, 1>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 64) return ln_launch<T, 64, 1>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 128) return ln_launch<T, 64, 2>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 256) return ln_launch<T, 64, 4>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 512) return ln_launch<T, 64, 8>(x, y, g, b, rows, dim, eps, s);
+  if (nvec <= 1024) return ln_launch<T, 64, 16>(x, y, g, b, rows, dim, eps, s);
+  return ln_launch<T, 64, 32>(x, y, g, b, rows, dim, eps, s);  // float rows up to 8192
+}
+
+hipError_t launch_layernorm(const void* x, void* y, const float* g, const float* b, int64_t rows,
+                            int dim, float eps, DType dt, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  return dt == DType::BF16 ? ln_dispatch<bf16>(x, y, g, b, rows, dim, eps, s)
+                           : ln_dispatch<float>(x, y, g, b, rows, dim, eps, s);
+}
+
+// Unrolled position of the spatial token (i, j) on an H x W grid with L
+// levels: each level appends the token's 2x2 offset 2*(i&1) + (j&1) to an
+// outer index and halves the coordinates; the position is the outer index
+// times the size of the coarse grid plus the token's coarse raster index.
+__device__ __forceinline__ int64_t unrolled_pos(int i, int j, int H, int W, int L) {
+  int64_t outer = 0;
+  for (int k = 0; k < L; ++k) {
+    outer = outer * 4 + 2 * (i & 1) + (j & 1);
+    i >>= 1;
+    j >>= 1;
+  }
+  const int64_t HL = H >> L, WL = W >> L;
+  return outer * (HL * WL) + (int64_t)i * WL + j;
+}
+
+// Row permutation between the spatial order and Hiera's unrolled order. A
+// group of G lanes copies one token row; the group is indexed by the spatial
+// token, so unroll scatters rows and reroll gathers them. Bit-exact copy.
+template <int G>
+__global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict__ x, uint8_t* __restrict__ y,
+                                                      int batch, int H, int W, int L,
+                                                      int row_bytes, int inverse) {
+  const int lane = threadIdx.x % G;
+  const int64_t t = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
+  const int64_t ntok = (int64_t)H * W;
+  if (t >= (int64_t)batch * ntok) return;
+  const int64_t b = t / ntok;
+  const int sp = (int)(t - b * ntok);
+  const int64_t un = unrolled_pos(sp / W, sp % W, H, W, L);
+  const int64_t src = b * ntok + (inverse ? un : sp);
+  const int64_t dst = b * ntok + (inverse ? sp : un);
+  const uint8_t* xs = x + src * row_bytes;
+  uint8_t* yd = y + dst * row_bytes;
+  for (int o = lane * 16; o < row_bytes; o += G * 16) st16(yd + o, ld16(xs + o));
+}
+
+hipError_t launch_permute(const void* x, void* y, int batch, int H, int W, int L, int channels,
+                          bool inverse, DType dt, hipStream_t s) {
+  const int row_bytes = channels * (dt == DType::BF16 ? 2 : 4);
+  const int64_t rows = (int64_t)batch * H * W;
+  if (rows == 0) return hipSuccess;
+  const int nvec = row_bytes / 16;
+  auto go = [&](auto gtag) {
+    constexpr int G = decltype(gtag)::value;
+    const int64_t blocks = (rows + (256 / G) - 1) / (256 / G);
+    hipLaunchKernelGGL((permute_kernel<G>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const uint8_t*)x, (uint8_t*)y, batch, H, W, L, row_bytes, (int)inverse);
+    return hipGetLastError();
+  };
+  if (nvec <= 8) return go(std::integral_constant<int, 8>());
+  if (nvec <= 16) return go(std::integral_constant<int, 16>());
+  if (nvec <= 32) return go(std::integral_constant<int, 32>());
+  return go(std::integral_constant<int, 64>());
+}
+
+// 4x max-pool over the q_stride axis of the unrolled order: output token m
+// of a frame is the elementwise max of tokens m + s * tokens/4, s = 0..3
+// (a 2x2 spatial max). max() of values that are all representable in T
+// returns one of them, so the result is bit-exact.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void pool4_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ y,
+                                                    int64_t ys, int batch, int tokens, int channels) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x % G;
+  const int q = tokens / 4;
+  const int64_t t = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
+  if (t >= (int64_t)batch * q) return;
+  const int64_t b = t / q;
+  const int64_t m = t - b * q;
+  const T* x0 = x + (b * tokens + m) * xs;
+  T* yr = y + t * ys;
+  for (int c = lane * VN; c < channels; c += G * VN) {
+    float acc[VN], v[VN];
+    unpack16<T>(ld16(x0 + c), acc);
+#pragma unroll
+    for (int s = 1; s < 4; ++s) {
+      unpack16<T>(ld16(x0 + (int64_t)s * q * xs + c), v);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] = fmaxf(acc[e], v[e]);
+    }
+    st16(yr + c, pack16<T>(acc));
+  }
+}
+
+hipError_t launch_pool4(const void* x, int64_t xs, void* y, int64_t ys, int batch, int tokens,
+                        int channels, DType dt, hipStream_t s) {
+  const int64_t rows = (int64_t)batch * (tokens / 4);
+  if (rows == 0) return hipSuccess;
+  auto go = [&](auto ttag) {
+    using T = decltype(ttag);
+    constexpr int G = 16;
+    const int64_t blocks = (rows + (256 / G) - 1) / (256 / G);
+    hipLaunchKernelGGL((pool4_kernel<T, G>), dim3((unsigned)blocks), dim3(256), 0, s, (const T*)x, xs,
+                       (T*)y, ys, batch, tokens, channels);
+    return hipGetLastError();
+  };
+  return dt == DType::BF16 ? go(bf16()) : go(float());
+}
+
+}  // namespace vit
