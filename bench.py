@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the pre-LN ViT encoder block on one MI355X.
+
+One step = one full block forward (LN1, qkv projection, attention, out
+projection + residual, LN2, fc1 + GELU, fc2 + residual) over one batch of
+seeded synthetic tokens already resident in HBM, through the C ABI. Prints
+one JSON line per workload with tokens/s (K event-free steps), per-stage
+device times from a second pass of K steps whose kernels carry HIP start/stop
+events on the launch stream, the MFMA-path TFLOP/s and the roofline of the
+dominant kernel from those times, and the CPU oracle timed on the host
+cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encoder-block tokens/sec + attention/GEMM TFLOP/s as % of bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+DEFAULT_CONFIG = "c2_hiera_s0"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "vision_transformer_encoder_vit_amd", "csrc")
+STAGE_SOURCE = {"ln1": "rowops.hip", "ln2": "rowops.hip", "qkv": "gemm.hip", "residual": "gemm.hip",
+                "attn": "attention.hip", "proj": "gemm.hip", "fc1": "gemm.hip", "fc2": "gemm.hip"}
+
+
+def describe(spec):
+    n = spec["grid_h"] * spec["grid_w"]
+    mode = {"mask_unit": "%d mask units" % spec["n_windows"],
+            "spatial": "%dx%d windows" % (spec["win_h"], spec["win_w"]),
+            "global": "global attention"}[spec["mode"]]
+    extra = []
+    if spec["q_stride"] == 4:
+        extra.append("q/residual 2x2 max-pool, D %d->%d" % (spec["dim_in"], spec["dim_out"]))
+    if spec["rope"]:
+        extra.append("axial RoPE")
+    if spec["qkv"] == "separate":
+        extra.append("separate q/k/v")
+    return "%s: %d x %dx%d tokens (%d), D %d, %d heads x %d, %s, MLP %d %s-GELU%s" % (
+        spec["name"], spec["batch"], spec["grid_h"], spec["grid_w"], n, spec["dim_out"], spec["heads"],
+        spec["dim_out"] // spec["heads"], mode, spec["mlp"], spec["gelu"],
+        (", " + ", ".join(extra)) if extra else "")
+
+
+def stage_work(spec):
+    """Algorithmic FLOPs and minimum HBM bytes of each stage."""
+    from vision_transformer_encoder_vit_amd import work
+    e = work.DTYPE_BYTES[spec["dtype"]]
+    B = spec["batch"]
+    n_in = spec["grid_h"] * spec["grid_w"]
+    m_in, m_out = B * n_in, B * n_in // spec["q_stride"]
+    Di, Do = spec["dim_in"], spec["dim_out"]
+    g = work.gemms(spec)
+    w = {"ln1": (0.0, work.layernorm_bytes(m_in, Di, spec["dtype"])),
+         "ln2": (0.0, work.layernorm_bytes(m_out, Do, spec["dtype"]))}
+    w["qkv"] = (work.gemm_flops(*g["qkv"]), work.gemm_bytes(*g["qkv"], spec["dtype"]))
+    if "res" in g:
+        # projection of every input row, then a 4x pool (read 4 rows, write 1)
+        w["residual"] = (work.gemm_flops(*g["res"]),
+                         work.gemm_bytes(*g["res"], spec["dtype"]) + e * (m_in + m_out) * Do)
+    else:
+        w["residual"] = (0.0, 0.0)
+    w["attn"] = (work.attention_flops(spec), work.attention_bytes(spec))
+    w["proj"] = (work.gemm_flops(*g["proj"]), work.gemm_bytes(*g["proj"], spec["dtype"], extra_rows_in=m_out))
+    w["fc1"] = (work.gemm_flops(*g["fc1"]), work.gemm_bytes(*g["fc1"], spec["dtype"]))
+    w["fc2"] = (work.gemm_flops(*g["fc2"]), work.gemm_bytes(*g["fc2"], spec["dtype"], extra_rows_in=m_out))
+    return w
+
+
+def src_hash(stage):
+    h = hashlib.sha256()
+    for f in (STAGE_SOURCE[stage], "common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, stage):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current source of the stage's kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    rec = t.get(config, {}).get(stage)
+    if not rec or rec.get("src_sha") != src_hash(stage):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(spec, budget_s=10.0):
+    """The float64 CPU oracle on frame 0 of the workload, repeated until about
+    budget_s of CPU time; returns tokens/s and the BLAS threads it used."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import block as ob
+    from vision_transformer_encoder_vit_amd import synth
+    one = synth.derive(spec, batch=1)
+    inp = synth.make_inputs(one, seed=0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ob.block_forward(inp["x"], inp, one)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    n = one["grid_h"] * one["grid_w"]
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "float64 numpy oracle, one full block forward of frame 0 (%d tokens), %d rep(s), %.2f s each"
+                      % (n, reps, dt)}
+
+
+def run(spec, steps, warmup, with_cpu):
+    import numpy as np
+    import torch
+    from vision_transformer_encoder_vit_amd import binding as vb
+    from vision_transformer_encoder_vit_amd import synth
+
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+    inp = synth.make_inputs(spec, seed=0)
+    dev = {}
+    for k, a in inp.items():
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        dev[k] = (t.to(dt) if (k == "x" or k.endswith("_w")) else t).cuda()
+    plan = vb.Plan(vb.desc_from_spec(spec))
+    w = vb.weights_struct(dev)
+    y = torch.empty((spec["batch"], synth.out_tokens(spec), spec["dim_out"]), dtype=dt, device="cuda")
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    ns = 2 * vb.VIT_NSTAGES
+    ev = (ctypes.c_void_p * (ns * steps))()
+    slot = lambda i: ctypes.cast(ctypes.addressof(ev) + i * ctypes.sizeof(ctypes.c_void_p),
+                                 ctypes.POINTER(ctypes.c_void_p))
+    for i in range(ns * steps):
+        if hip.hipEventCreate(slot(i)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+    for _ in range(warmup):
+        plan.forward(w, dev["x"], y, ws)
+    # timed region: K plain forwards (throughput)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.forward(w, dev["x"], y, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # kernel-timing pass: the same K forwards with every stage's first/last
+    # kernel carrying HIP start/stop events (dispatch-packet timestamps on the
+    # launch stream); per-launch durations are averaged over the K steps
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xp, yp, wsp = (ctypes.c_void_p(t.data_ptr()) for t in (dev["x"], y, ws))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        vb.check(vb.lib.vit_block_forward_timed(plan.handle, ctypes.byref(w), xp, yp, wsp, plan.workspace_bytes,
+                                                stream, slot(i * ns), ns))
+    torch.cuda.synchronize()
+    elapsed_timed = time.perf_counter() - t1
+    ms = ctypes.c_float()
+    stage_us = {}
+    for s, name in enumerate(vb.STAGES):
+        tot = 0.0
+        for i in range(steps):
+            a, b = ev[i * ns + 2 * s], ev[i * ns + 2 * s + 1]
+            if hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            tot += ms.value
+        stage_us[name] = 1e3 * tot / steps
+    for i in range(ns * steps):
+        hip.hipEventDestroy(ev[i])
+    plan.close()
+
+    ms_step = 1e3 * elapsed / steps
+    tokens = spec["batch"] * spec["grid_h"] * spec["grid_w"]
+    wk = stage_work(spec)
+    mfma_stages = [st for st in ("qkv", "residual", "attn", "proj", "fc1", "fc2") if wk[st][0] > 0]
+    flops = sum(wk[s][0] for s in mfma_stages)
+    t_mfma = sum(stage_us[s] for s in mfma_stages) * 1e-6
+    peak_c = PEAK_BF16_TFLOPS if spec["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    dom = max((st for st in stage_us if wk[st][1] > 0), key=lambda st: stage_us[st])
+    f, by = wk[dom]
+    t = stage_us[dom] * 1e-6
+    ridge = peak_c * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if f > 0 and f / by > ridge:
+        roof = {"bound": "mfma", "achieved": f / t / 1e12, "peak": peak_c, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": by / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(spec["name"], dom)
+    line = {
+        "metric": METRIC, "value": tokens / (elapsed / steps), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
+        "config": {"workload": describe(spec), "batch": spec["batch"], "tokens_per_frame":
+                   spec["grid_h"] * spec["grid_w"], "parallelism": "none (1 GPU)"},
+        "attn_gemm_tflops": flops / t_mfma / 1e12,
+        "attn_gemm_pct_of_peak": 100.0 * flops / t_mfma / 1e12 / peak_c,
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "ms_per_step_with_stage_events": 1e3 * elapsed_timed / steps,
+        "roofline": roof,
+    }
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(spec)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, help="workload name, or 'all'")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported (use --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("steps >= 1 and warmup >= 0")
+    from vision_transformer_encoder_vit_amd import synth
+    names = list(synth.CONFIGS) if args.config == "all" else [args.config]
+    for n in names:
+        if n not in synth.CONFIGS:
+            ap.error("unknown workload %s (choose from %s)" % (n, ", ".join(synth.CONFIGS)))
+    for n in names:
+        with_cpu = not args.no_cpu_baseline and n == names[0]
+        print(json.dumps(run(synth.CONFIGS[n], args.steps, args.warmup, with_cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -184,6 +184,33 @@ vit_status vit_block_forward_seams(vit_block_t plan, const vit_block_weights* w,
                                    const vit_block_seams* seams, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Stages of one forward, in launch order (for vit_block_forward_timed). */
+enum {
+  VIT_STAGE_LN1 = 0,      /* LayerNorm of x                              */
+  VIT_STAGE_QKV = 1,      /* qkv projection (+ bias, + RoPE)              */
+  VIT_STAGE_RESIDUAL = 2, /* transition: residual projection + 4x pool    */
+  VIT_STAGE_ATTN = 3,     /* windowed / global attention                  */
+  VIT_STAGE_PROJ = 4,     /* out projection + bias + residual             */
+  VIT_STAGE_LN2 = 5,      /* LayerNorm of x1                              */
+  VIT_STAGE_FC1 = 6,      /* fc1 + bias + GELU                            */
+  VIT_STAGE_FC2 = 7,      /* fc2 + bias + residual                        */
+  VIT_NSTAGES = 8
+};
+
+/* As vit_block_forward, for measurement: `events` holds n_events hipEvent_t
+ * handles created by the caller (hipEventCreate); for stage i (VIT_STAGE_*)
+ * with 2i+1 < n_events, events[2i] takes the begin timestamp of the stage's
+ * first kernel and events[2i+1] the end timestamp of its last kernel (the
+ * kernels are launched with hipExtLaunchKernel's start/stop events, so no
+ * marker packets are added to the stream), and hipEventElapsedTime(events[2i],
+ * events[2i+1]) is the stage's device time. A stage with no kernel (the
+ * residual stage outside transitions) records both events back to back on
+ * `stream`. The result is bit-identical to vit_block_forward. */
+vit_status vit_block_forward_timed(vit_block_t plan, const vit_block_weights* w,
+                                   const void* x, void* y, void* workspace,
+                                   size_t workspace_bytes, void* stream,
+                                   void* const* events, int32_t n_events);
+
 vit_status vit_block_destroy(vit_block_t plan);
 
 const char* vit_last_error(void);

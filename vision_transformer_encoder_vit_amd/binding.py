@@ -17,6 +17,8 @@ VIT_ATTN_GLOBAL, VIT_ATTN_MASK_UNIT, VIT_ATTN_SPATIAL = 0, 1, 2
 VIT_GELU_ERF, VIT_GELU_TANH = 0, 1
 VIT_QKV_FUSED, VIT_QKV_SEPARATE = 0, 1
 VIT_ROPE_NONE, VIT_ROPE_AXIAL_TABLE = 0, 1
+STAGES = ["ln1", "qkv", "residual", "attn", "proj", "ln2", "fc1", "fc2"]
+VIT_NSTAGES = len(STAGES)
 
 _i32, _f32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -68,6 +70,8 @@ def _load():
         "vit_block_forward": [_vp, P(vit_block_weights), _vp, _vp, _vp, ctypes.c_size_t, _vp],
         "vit_block_forward_seams": [_vp, P(vit_block_weights), _vp, _vp, P(vit_block_seams), _vp,
                                     ctypes.c_size_t, _vp],
+        "vit_block_forward_timed": [_vp, P(vit_block_weights), _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                                    P(_vp), _i32],
         "vit_block_destroy": [_vp],
         "vit_layernorm": [_vp, _vp, _vp, _vp, ctypes.c_int64, _i32, _f32, _i32, _vp],
         "vit_unroll": [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
@@ -158,6 +162,13 @@ class Plan:
         check(lib.vit_block_forward(self.handle, ctypes.byref(weights), _ptr(x), _ptr(y),
                                     _ptr(workspace), workspace.numel() * workspace.element_size()
                                     if workspace is not None else 0, _stream(stream)))
+
+    def forward_timed(self, weights, x, y, workspace, events, stream=None):
+        """events: a ctypes array of 2 * VIT_NSTAGES hipEvent_t handles."""
+        check(lib.vit_block_forward_timed(self.handle, ctypes.byref(weights), _ptr(x), _ptr(y),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size()
+                                          if workspace is not None else 0, _stream(stream), events,
+                                          len(events)))
 
     def forward_seams(self, weights, x, y, seams, workspace, stream=None):
         s = vit_block_seams()

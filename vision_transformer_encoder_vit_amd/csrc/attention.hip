@@ -23,6 +23,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 namespace vit {
@@ -274,18 +276,19 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams<T> p) {
 }
 
 template <typename T, int QB, int HPW, bool POOL>
-static hipError_t attn_go(const AttnArgs& a, AttnParams<T> p, hipStream_t s) {
+static hipError_t attn_go(const AttnArgs& a, AttnParams<T> p, hipStream_t s, StageEvents ev) {
   constexpr int rows = (4 / HPW) * 16 * QB;
   p.q_tiles = (p.n_q + rows - 1) / rows;
   p.head_groups = a.heads / HPW;
   const int64_t blocks = (int64_t)a.batch * p.windows * p.q_tiles * p.head_groups;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attention_kernel<T, QB, HPW, POOL>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  hipExtLaunchKernelGGL((attention_kernel<T, QB, HPW, POOL>), dim3((unsigned)blocks), dim3(256), 0, s, ev.start,
+                        ev.stop, 0, p);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
+static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev) {
   AttnParams<T> p;
   p.qkv = (const T*)a.qkv;
   p.ld_qkv = a.ld_qkv;
@@ -317,17 +320,17 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   const bool pool = a.q_stride == 4;
   // small query sets: several heads per workgroup, one wave each
   if (p.n_q <= 16 && a.heads % 4 == 0) {
-    return pool ? attn_go<T, 1, 4, true>(a, p, s) : attn_go<T, 1, 4, false>(a, p, s);
+    return pool ? attn_go<T, 1, 4, true>(a, p, s, ev) : attn_go<T, 1, 4, false>(a, p, s, ev);
   }
   if (p.n_q <= 32 && a.heads % 2 == 0) {
-    return pool ? attn_go<T, 1, 2, true>(a, p, s) : attn_go<T, 1, 2, false>(a, p, s);
+    return pool ? attn_go<T, 1, 2, true>(a, p, s, ev) : attn_go<T, 1, 2, false>(a, p, s, ev);
   }
-  if (p.n_q <= 64) return pool ? attn_go<T, 1, 1, true>(a, p, s) : attn_go<T, 1, 1, false>(a, p, s);
-  return pool ? attn_go<T, 2, 1, true>(a, p, s) : attn_go<T, 2, 1, false>(a, p, s);
+  if (p.n_q <= 64) return pool ? attn_go<T, 1, 1, true>(a, p, s, ev) : attn_go<T, 1, 1, false>(a, p, s, ev);
+  return pool ? attn_go<T, 2, 1, true>(a, p, s, ev) : attn_go<T, 2, 1, false>(a, p, s, ev);
 }
 
-hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s) {
-  return dt == DType::BF16 ? attn_dispatch<bf16>(a, s) : attn_dispatch<float>(a, s);
+hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s, StageEvents ev) {
+  return dt == DType::BF16 ? attn_dispatch<bf16>(a, s, ev) : attn_dispatch<float>(a, s, ev);
 }
 
 }  // namespace vit

@@ -197,7 +197,8 @@ static vit_status check_weights(const vit_block_plan* p, const vit_block_weights
 }
 
 static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
-                               const vit_block_seams* seams, void* ws, size_t ws_bytes, void* stream) {
+                               const vit_block_seams* seams, void* ws, size_t ws_bytes, void* stream,
+                               void* const* events = nullptr, int n_events = 0) {
   if (!plan) return fail(VIT_ERR_INVALID_ARG, "plan is NULL");
   const vit_block_plan& P = *plan;
   const vit_block_desc& d = P.d;
@@ -237,9 +238,21 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   void* u = S.u ? S.u : base + P.off_u;
   const int Di = d.dim_in, Do = d.dim_out, F = d.mlp_hidden, hd = P.head_dim;
   hipError_t e;
+  // measurement events of stage i: events[2i] (first kernel's start) and
+  // events[2i+1] (last kernel's end)
+  auto stage_ev = [&](int stage) {
+    vit::StageEvents ev;
+    if (events && 2 * stage + 1 < n_events) {
+      ev.start = (hipEvent_t)events[2 * stage];
+      ev.stop = (hipEvent_t)events[2 * stage + 1];
+    }
+    return ev;
+  };
+  auto only_start = [](vit::StageEvents ev) { ev.stop = nullptr; return ev; };
+  auto only_stop = [](vit::StageEvents ev) { ev.start = nullptr; return ev; };
 
   // 1. LN1
-  e = vit::launch_layernorm(x, h, w->ln1_gamma, w->ln1_beta, P.m_in, Di, d.ln_eps, dt, s);
+  e = vit::launch_layernorm(x, h, w->ln1_gamma, w->ln1_beta, P.m_in, Di, d.ln_eps, dt, s, stage_ev(VIT_STAGE_LN1));
   if ((st = device_status(e, "layernorm (LN1)")) != VIT_OK) return st;
 
   // 2. qkv projection (+ bias, + RoPE)
@@ -277,7 +290,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   } else {
     g.epi = vit::EPI_BIAS;
   }
-  e = vit::launch_gemm(g, dt, s);
+  e = vit::launch_gemm(g, dt, s, stage_ev(VIT_STAGE_QKV));
   if ((st = device_status(e, "gemm (qkv)")) != VIT_OK) return st;
 
   // 3. residual: x, or pool4(h W_res^T + b_res) at a transition
@@ -295,20 +308,30 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     gr.C = base + P.off_rp;
     gr.ldc = Do;
     gr.epi = vit::EPI_BIAS;
-    e = vit::launch_gemm(gr, dt, s);
+    e = vit::launch_gemm(gr, dt, s, only_start(stage_ev(VIT_STAGE_RESIDUAL)));
     if ((st = device_status(e, "gemm (residual projection)")) != VIT_OK) return st;
     void* rr = S.r ? S.r : base + P.off_r;
-    e = vit::launch_pool4(base + P.off_rp, Do, rr, Do, d.batch, P.n_in, Do, dt, s);
+    e = vit::launch_pool4(base + P.off_rp, Do, rr, Do, d.batch, P.n_in, Do, dt, s,
+                          only_stop(stage_ev(VIT_STAGE_RESIDUAL)));
     if ((st = device_status(e, "pool4 (residual)")) != VIT_OK) return st;
     r = rr;
     if (S.q_pooled) {
       e = vit::launch_pool4(qkv, 3LL * Do, S.q_pooled, Do, d.batch, P.n_in, Do, dt, s);
       if ((st = device_status(e, "pool4 (q seam)")) != VIT_OK) return st;
     }
-  } else if (S.r) {
-    e = hipMemcpyAsync(S.r, x, x_bytes, hipMemcpyDeviceToDevice, s);
-    if ((st = device_status(e, "copy (r seam)")) != VIT_OK) return st;
+  } else {
+    // no kernel in this stage: mark it empty
+    const vit::StageEvents ev = stage_ev(VIT_STAGE_RESIDUAL);
+    if (ev.start) {
+      if ((st = device_status(hipEventRecord(ev.start, s), "hipEventRecord")) != VIT_OK) return st;
+      if ((st = device_status(hipEventRecord(ev.stop, s), "hipEventRecord")) != VIT_OK) return st;
+    }
+    if (S.r) {
+      e = hipMemcpyAsync(S.r, x, x_bytes, hipMemcpyDeviceToDevice, s);
+      if ((st = device_status(e, "copy (r seam)")) != VIT_OK) return st;
+    }
   }
+
 
   // 4. attention
   vit::AttnArgs a;
@@ -329,7 +352,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   a.win_w = d.win_w;
   a.q_stride = d.q_stride;
   a.scale = d.attn_scale > 0.f ? d.attn_scale : 1.0f / std::sqrt((float)hd);
-  e = vit::launch_attention(a, dt, s);
+  e = vit::launch_attention(a, dt, s, stage_ev(VIT_STAGE_ATTN));
   if ((st = device_status(e, "attention")) != VIT_OK) return st;
 
   // 5. x1 = r + ctx W_o^T + b_o
@@ -349,11 +372,12 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   go.ldres = Do;
   go.branch = S.attn_branch;
   go.ldbranch = Do;
-  e = vit::launch_gemm(go, dt, s);
+  e = vit::launch_gemm(go, dt, s, stage_ev(VIT_STAGE_PROJ));
   if ((st = device_status(e, "gemm (out projection)")) != VIT_OK) return st;
 
   // 6. LN2
-  e = vit::launch_layernorm(x1, h2, w->ln2_gamma, w->ln2_beta, P.m_out, Do, d.ln_eps, dt, s);
+  e = vit::launch_layernorm(x1, h2, w->ln2_gamma, w->ln2_beta, P.m_out, Do, d.ln_eps, dt, s,
+                            stage_ev(VIT_STAGE_LN2));
   if ((st = device_status(e, "layernorm (LN2)")) != VIT_OK) return st;
 
   // 7. u = GELU(h2 W_1^T + b_1)
@@ -369,7 +393,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g1.C = u;
   g1.ldc = F;
   g1.epi = d.gelu == VIT_GELU_ERF ? vit::EPI_GELU_ERF : vit::EPI_GELU_TANH;
-  e = vit::launch_gemm(g1, dt, s);
+  e = vit::launch_gemm(g1, dt, s, stage_ev(VIT_STAGE_FC1));
   if ((st = device_status(e, "gemm (fc1)")) != VIT_OK) return st;
 
   // 8. y = x1 + u W_2^T + b_2
@@ -389,7 +413,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g2.ldres = Do;
   g2.branch = S.mlp_branch;
   g2.ldbranch = Do;
-  e = vit::launch_gemm(g2, dt, s);
+  e = vit::launch_gemm(g2, dt, s, stage_ev(VIT_STAGE_FC2));
   if ((st = device_status(e, "gemm (fc2)")) != VIT_OK) return st;
   return ok();
 }
@@ -397,6 +421,15 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
 VIT_API vit_status vit_block_forward(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(plan, w, x, y, nullptr, workspace, workspace_bytes, stream);
+}
+
+VIT_API vit_status vit_block_forward_timed(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
+                                           void* workspace, size_t workspace_bytes, void* stream,
+                                           void* const* events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && !events)) return fail(VIT_ERR_INVALID_ARG, "bad events array");
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(VIT_ERR_INVALID_ARG, "event %d is NULL", i);
+  return forward_impl(plan, w, x, y, nullptr, workspace, workspace_bytes, stream, events, n_events);
 }
 
 VIT_API vit_status vit_block_forward_seams(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,

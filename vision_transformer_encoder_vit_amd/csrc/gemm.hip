@@ -14,6 +14,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <hip/hip_ext.h>
+
 namespace vit {
 
 template <typename T>
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 }
 
 template <typename T, int BM, int BN, int WTM, int WTN>
-static hipError_t gemm_go(const GemmArgs& a, hipStream_t s) {
+static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   GemmParams<T> p;
   p.A = (const T*)a.A;
   p.lda = a.lda;
@@ -214,21 +216,21 @@ static hipError_t gemm_go(const GemmArgs& a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   dim3 grid((unsigned)tiles), block(256);
   switch (a.epi) {
-    case EPI_BIAS: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS>), grid, block, 0, s, p); break;
-    case EPI_BIAS_ROPE: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS_ROPE>), grid, block, 0, s, p); break;
-    case EPI_GELU_ERF: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_GELU_ERF>), grid, block, 0, s, p); break;
-    case EPI_GELU_TANH: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_GELU_TANH>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS_RES>), grid, block, 0, s, p); break;
+    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS_ROPE>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_GELU_ERF>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_GELU_TANH>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS_RES>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (dt == DType::F32) return gemm_go<float, 64, 64, 2, 2>(a, s);
+  if (dt == DType::F32) return gemm_go<float, 64, 64, 2, 2>(a, s, ev);
   const int64_t big_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (big_tiles >= 512) return gemm_go<bf16, 128, 128, 4, 4>(a, s);
-  return gemm_go<bf16, 64, 64, 2, 2>(a, s);
+  if (big_tiles >= 512) return gemm_go<bf16, 128, 128, 4, 4>(a, s, ev);
+  return gemm_go<bf16, 64, 64, 2, 2>(a, s, ev);
 }
 
 }  // namespace vit

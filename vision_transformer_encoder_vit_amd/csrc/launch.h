@@ -7,6 +7,14 @@ namespace vit {
 
 enum class DType { F32 = 0, BF16 = 1 };
 
+// Optional events for measurement: `start` takes the first kernel's begin
+// time and `stop` the last kernel's end time (hipExtLaunchKernel timestamps
+// from the dispatch packets, so no extra packets enter the stream).
+struct StageEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 enum Epilogue {
   EPI_BIAS = 0,        // C = acc + bias
   EPI_BIAS_ROPE = 1,   // C = rope(acc + bias) on columns < rope_cols
@@ -39,7 +47,7 @@ struct GemmArgs {
   int rope_cols = 0, head_dim = 0, rope_mode = 0;
   int tokens_per_frame = 1, grid_w = 1, win_h = 1, win_w = 1;
 };
-hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 
 enum AttnMode { ATTN_GLOBAL = 0, ATTN_MASK_UNIT = 1, ATTN_SPATIAL = 2 };
 
@@ -53,13 +61,15 @@ struct AttnArgs {
   int q_stride = 1;
   float scale = 1.f;
 };
-hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 
 hipError_t launch_layernorm(const void* x, void* y, const float* g, const float* b,
-                            int64_t rows, int dim, float eps, DType dt, hipStream_t s);
+                            int64_t rows, int dim, float eps, DType dt, hipStream_t s,
+                            StageEvents ev = {});
 hipError_t launch_permute(const void* x, void* y, int batch, int grid_h, int grid_w,
                           int levels, int channels, bool inverse, DType dt, hipStream_t s);
 hipError_t launch_pool4(const void* x, int64_t x_stride, void* y, int64_t y_stride,
-                        int batch, int tokens, int channels, DType dt, hipStream_t s);
+                        int batch, int tokens, int channels, DType dt, hipStream_t s,
+                        StageEvents ev = {});
 
 }  // namespace vit

@@ -4,6 +4,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 namespace vit {
@@ -73,35 +75,35 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
 
 template <typename T, int G, int V>
 static hipError_t ln_launch(const void* x, void* y, const float* g, const float* b, int64_t rows,
-                            int dim, float eps, hipStream_t s) {
+                            int dim, float eps, hipStream_t s, StageEvents ev) {
   const int rpb = 256 / G;
   const int64_t blocks = (rows + rpb - 1) / rpb;
-  hipLaunchKernelGGL((layernorm_kernel<T, G, V>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const T*)x, (T*)y, g, b, rows, dim, eps);
+  hipExtLaunchKernelGGL((layernorm_kernel<T, G, V>), dim3((unsigned)blocks), dim3(256), 0, s, ev.start,
+                        ev.stop, 0, (const T*)x, (T*)y, g, b, rows, dim, eps);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t ln_dispatch(const void* x, void* y, const float* g, const float* b, int64_t rows,
-                              int dim, float eps, hipStream_t s) {
+                              int dim, float eps, hipStream_t s, StageEvents ev) {
   const int nvec = dim / Vec<T>::N;
-  if (nvec <= 4) return ln_launch<T, 4, 1>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 8) return ln_launch<T, 8, 1>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 16) return ln_launch<T, 16, 1>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 32) return ln_launch<T, 32, 1>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 64) return ln_launch<T, 64, 1>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 128) return ln_launch<T, 64, 2>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 256) return ln_launch<T, 64, 4>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 512) return ln_launch<T, 64, 8>(x, y, g, b, rows, dim, eps, s);
-  if (nvec <= 1024) return ln_launch<T, 64, 16>(x, y, g, b, rows, dim, eps, s);
-  return ln_launch<T, 64, 32>(x, y, g, b, rows, dim, eps, s);  // float rows up to 8192
+  if (nvec <= 4) return ln_launch<T, 4, 1>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 8) return ln_launch<T, 8, 1>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 16) return ln_launch<T, 16, 1>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 32) return ln_launch<T, 32, 1>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 64) return ln_launch<T, 64, 1>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 128) return ln_launch<T, 64, 2>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 256) return ln_launch<T, 64, 4>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 512) return ln_launch<T, 64, 8>(x, y, g, b, rows, dim, eps, s, ev);
+  if (nvec <= 1024) return ln_launch<T, 64, 16>(x, y, g, b, rows, dim, eps, s, ev);
+  return ln_launch<T, 64, 32>(x, y, g, b, rows, dim, eps, s, ev);  // float rows up to 8192
 }
 
 hipError_t launch_layernorm(const void* x, void* y, const float* g, const float* b, int64_t rows,
-                            int dim, float eps, DType dt, hipStream_t s) {
+                            int dim, float eps, DType dt, hipStream_t s, StageEvents ev) {
   if (rows == 0) return hipSuccess;
-  return dt == DType::BF16 ? ln_dispatch<bf16>(x, y, g, b, rows, dim, eps, s)
-                           : ln_dispatch<float>(x, y, g, b, rows, dim, eps, s);
+  return dt == DType::BF16 ? ln_dispatch<bf16>(x, y, g, b, rows, dim, eps, s, ev)
+                           : ln_dispatch<float>(x, y, g, b, rows, dim, eps, s, ev);
 }
 
 // Unrolled position of the spatial token (i, j) on an H x W grid with L
@@ -189,15 +191,15 @@ __global__ __launch_bounds__(256) void pool4_kernel(const T* __restrict__ x, int
 }
 
 hipError_t launch_pool4(const void* x, int64_t xs, void* y, int64_t ys, int batch, int tokens,
-                        int channels, DType dt, hipStream_t s) {
+                        int channels, DType dt, hipStream_t s, StageEvents ev) {
   const int64_t rows = (int64_t)batch * (tokens / 4);
   if (rows == 0) return hipSuccess;
   auto go = [&](auto ttag) {
     using T = decltype(ttag);
     constexpr int G = 16;
     const int64_t blocks = (rows + (256 / G) - 1) / (256 / G);
-    hipLaunchKernelGGL((pool4_kernel<T, G>), dim3((unsigned)blocks), dim3(256), 0, s, (const T*)x, xs,
-                       (T*)y, ys, batch, tokens, channels);
+    hipExtLaunchKernelGGL((pool4_kernel<T, G>), dim3((unsigned)blocks), dim3(256), 0, s, ev.start, ev.stop, 0,
+                          (const T*)x, xs, (T*)y, ys, batch, tokens, channels);
     return hipGetLastError();
   };
   return dt == DType::BF16 ? go(bf16()) : go(float());
