@@ -183,8 +183,226 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
   }
 }
 
-template <typename T, int BM, int BN, int WTM, int WTN>
-static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
+// ---------------------------------------------------------------------------
+// bf16 path for K % 64 == 0: 32x32x16 MFMA, operands staged global -> LDS
+// directly (global_load_lds, 16 bytes per lane, no register round trip) in a
+// two-stage ring, and an epilogue that goes through LDS so that every global
+// store is a full 16-byte vector of one output row.
+//
+// LDS layout of a stage: [BM token rows | BN weight rows] x 64 bf16 (128 B
+// per row = 8 chunks of 16 B). One load instruction of a wave fills 8 rows
+// (1 KB, contiguous); the chunk a lane loads is XOR-swizzled by its row so
+// that the 32-row fragment reads of an MFMA operand (one 16-byte chunk per
+// lane) spread over all banks.
+// ---------------------------------------------------------------------------
+
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+__device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Workgroup -> output tile. Workgroups are dealt round-robin to the 8 XCDs
+// (each with its own L2): each XCD gets a contiguous range of the logical
+// tile order, walked in groups of GM tile rows, so the tiles that run
+// together on one XCD share A row panels and W column panels in its L2.
+template <int GM>
+__device__ __forceinline__ void xcd_tile(int bid, int nwg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int q = nwg / 8, r = nwg % 8, x = bid % 8, local = bid / 8;
+  const int t = x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+  const int per_group = GM * tiles_n;
+  const int grp = t / per_group, first_m = grp * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int in = t - grp * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(GemmParams<bf16> p) {
+  constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  constexpr int BK = 64, ST = 2;
+  constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;  // 32x32 tiles per wave
+  constexpr int STAGE = (BM + BN) * BK;                          // bf16 elements
+  constexpr int LPW = (BM + BN) / (8 * NW);                      // load instructions per wave per stage
+  static_assert((BM + BN) % (8 * NW) == 0, "rows must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) bf16 sm[ST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
+  int tmi, tni;
+  xcd_tile<8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tmi, tni);
+  const int m0 = tmi * BM, n0 = tni * BN;
+
+  // per-lane source rows (clamped into the matrix: rows past M or N are
+  // loaded but never stored)
+  const bf16* src[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int row = (wave * LPW + j) * 8 + lane / 8;
+    const int chunk = (lane & 7) ^ lds_swz(row);
+    if (row < BM) {
+      const int m = min(m0 + row, p.M - 1);
+      src[j] = p.A + (int64_t)m * p.lda + chunk * 8;
+    } else {
+      const int n = min(n0 + row - BM, p.N - 1);
+      const int seg = n / p.seg_cols;
+      const bf16* base = seg == 0 ? p.W0 : (seg == 1 ? p.W1 : p.W2);
+      src[j] = base + (int64_t)(n - seg * p.seg_cols) * p.K + chunk * 8;
+    }
+  }
+  auto issue = [&](int kt) {
+    bf16* st = sm + (kt % ST) * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_ptr)(st + (wave * LPW + j) * 512), 16, 0, 0);
+  };
+
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int fr = lane & 31, g = lane >> 5;
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+  u32x4 af[2][TN], bfr[2][TM];
+  auto frags = [&](int buf, int stage, int ks) {
+    const bf16* xs = sm + stage * STAGE;
+    const bf16* ws = xs + BM * BK;
+    const int chunk = ks * 2 + g;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int row = wn * TN * 32 + i * 32 + fr;
+      af[buf][i] = ld16(ws + row * 64 + (chunk ^ lds_swz(row)) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int row = wm * TM * 32 + j * 32 + fr;
+      bfr[buf][j] = ld16(xs + row * 64 + (chunk ^ lds_swz(row)) * 8);
+    }
+  };
+
+  const int nk = p.K / BK;
+  issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of tile kt have landed; after the barrier every
+    // wave's have, and every wave is done reading the stage refilled next
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk) issue(kt + 1);
+    const int stage = kt % ST;
+    frags(0, stage, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) frags((ks + 1) & 1, stage, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next fragment reads ahead of these MFMAs
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ks & 1][i]),
+                                                             __builtin_bit_cast(bf16x8, bfr[ks & 1][j]), acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- epilogue: accumulators -> LDS (fp32, row-major) -> 8 columns per
+  // thread with bias / RoPE / GELU / residual -> one 16-byte store per row
+  // chunk. Lane (fr, g) of 32x32 tile (i, j) holds row j*32+fr, columns
+  // i*32 + 8q + 4g + e in register 4q + e.
+  constexpr int CROW = BN + 4;
+  constexpr int PR0 = (ST * STAGE * 2) / (CROW * 4);
+  constexpr int PR = PR0 >= BM ? BM : (PR0 >= BM / 2 ? BM / 2 : BM / 4);
+  static_assert(PR >= BM / 4 && PR % 32 == 0, "LDS too small for the epilogue");
+  float* cs = reinterpret_cast<float*>(sm);
+  constexpr int WROWS = BM / WAVES_M;
+  constexpr int G8 = BN / 8;
+#pragma unroll
+  for (int pass = 0; pass < BM / PR; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int row = wm * WROWS + j * 32 + fr;
+      if (row >= pass * PR && row < (pass + 1) * PR) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = wn * TN * 32 + i * 32 + 8 * q + 4 * g;
+            *reinterpret_cast<f32x4*>(cs + (row - pass * PR) * CROW + col) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < PR * G8; e += NT) {
+      const int r = e / G8, c8 = (e - r * G8) * 8;
+      const int m = m0 + pass * PR + r, n = n0 + c8;
+      if (m >= p.M || n >= p.N) continue;
+      float v[8];
+      *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8);
+      *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4);
+      const int seg = n / p.seg_cols;
+      const float* bb = (seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2)) + (n - seg * p.seg_cols);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bb), b1 = *reinterpret_cast<const f32x4*>(bb + 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[t] += b0[t];
+        v[4 + t] += b1[t];
+      }
+      if (EPI == EPI_BIAS_ROPE) {
+        if (n < p.rope_cols) {
+          const int t = m % p.tokens_per_frame;
+          int rr = t;
+          if (p.rope_mode == 1) {
+            const int yy = t / p.grid_w, xx = t - yy * p.grid_w;
+            rr = (yy % p.win_h) * p.win_w + (xx % p.win_w);
+          }
+          const int d = (n % (p.rope_cols / 2)) % p.head_dim;  // multiple of 8: pairs d/2 .. d/2+3
+          const float* cs4 = p.rope + ((int64_t)rr * (p.head_dim / 2) + d / 2) * 2;
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs4), c1 = *reinterpret_cast<const f32x4*>(cs4 + 4);
+          const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const float a0 = v[2 * pr], a1 = v[2 * pr + 1], co = cc[2 * pr], si = cc[2 * pr + 1];
+            v[2 * pr] = a0 * co - a1 * si;
+            v[2 * pr + 1] = a1 * co + a0 * si;
+          }
+        }
+      } else if (EPI == EPI_GELU_ERF) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = gelu_erf_f(v[t]);
+      } else if (EPI == EPI_GELU_TANH) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = gelu_tanh_f(v[t]);
+      } else if (EPI == EPI_BIAS_RES) {
+        if (p.branch) st16(p.branch + (int64_t)m * p.ldbranch + n, pack16<bf16>(v));
+        float rv[8];
+        unpack16<bf16>(ld16(p.res + (int64_t)m * p.ldres + n), rv);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] += rv[t];
+      }
+      st16(p.C + (int64_t)m * p.ldc + n, pack16<bf16>(v));
+    }
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+static hipError_t gemm32_go(const GemmParams<bf16>& p, int epi, hipStream_t s, StageEvents ev) {
+  const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
+  switch (epi) {
+    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_BIAS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_BIAS_ROPE>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_GELU_ERF>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_GELU_TANH>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_BIAS_RES>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+static GemmParams<T> make_params(const GemmArgs& a) {
   GemmParams<T> p;
   p.A = (const T*)a.A;
   p.lda = a.lda;
@@ -212,6 +430,12 @@ static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   p.grid_w = a.grid_w;
   p.win_h = a.win_h;
   p.win_w = a.win_w;
+  return p;
+}
+
+template <typename T, int BM, int BN, int WTM, int WTN>
+static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
+  const GemmParams<T> p = make_params<T>(a);
   const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
   dim3 grid((unsigned)tiles), block(256);
@@ -228,6 +452,14 @@ static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (dt == DType::F32) return gemm_go<float, 64, 64, 2, 2>(a, s, ev);
+  if (a.K % 64 == 0 && a.lda % 8 == 0) {
+    // one full wave of 256x256 tiles fills the 256 CUs; otherwise 128x128
+    // tiles (two workgroups per CU) balance better
+    const GemmParams<bf16> p = make_params<bf16>(a);
+    const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (t256 >= 224 && t256 <= 256) return gemm32_go<256, 256, 2, 4>(p, a.epi, s, ev);
+    return gemm32_go<128, 128, 2, 2>(p, a.epi, s, ev);
+  }
   const int64_t big_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
   if (big_tiles >= 512) return gemm_go<bf16, 128, 128, 4, 4>(a, s, ev);
   return gemm_go<bf16, 64, 64, 2, 2>(a, s, ev);
