@@ -30,6 +30,13 @@
 namespace vit {
 
 constexpr int KT = 64;   // keys per tile
+#ifndef ATTN_NW
+#define ATTN_NW 4
+#endif
+#ifndef ATTN_QB
+#define ATTN_QB 1
+#endif
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int HDP = 64;  // padded head dim
 
 template <typename T>
@@ -275,6 +282,330 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams<T> p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel for large windows (>= 128 queries): 32x32x16 MFMA.
+//
+// A workgroup of NW waves takes 64*NW queries of one (frame, window, head);
+// each wave owns 64 queries (two 32-row blocks), so every K and V fragment
+// read from LDS feeds two MFMAs. Per 64-key tile: K goes global -> LDS
+// directly (global_load_lds, XOR-swizzled rows), V goes through registers
+// and is written transposed ([d][key]); both are double-buffered and the
+// next tile is fetched while this one is multiplied.
+//   S^T = K Q^T    lane (q = l%32, h = l/32) receives the 16 keys
+//                  32kb + 8(r/4) + 4h + r%4 of query q (r = register)
+//   softmax        row max = in-lane max + one xor-32 shuffle; exponentials
+//                  exp2(s*c - m*c) with c = scale*log2(e); the rescale of
+//                  the output is skipped when no row max moved
+//   O^T += V^T P^T registers 8s..8s+7 of a 32-key block are exactly the
+//                  8 keys one lane supplies for MFMA k-step s, so P goes to
+//                  the MFMA without any data movement; V^T supplies the same
+//                  keys from two 8-byte LDS reads
+// ---------------------------------------------------------------------------
+
+__host__ __device__ constexpr int attn_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+__device__ __forceinline__ int kswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+typedef __attribute__((address_space(3))) void* attn_lds_ptr;
+
+// Token index of in-window position i, kept as (x, y) in the window and
+// advanced by a fixed step without divisions: GLOBAL windows are the frame
+// (token = i), SPATIAL windows are win_h x win_w blocks of the grid.
+struct WinCursor {
+  int x, y;
+  __device__ __forceinline__ void init(int i, int ww) {
+    y = i / ww;
+    x = i - y * ww;
+  }
+  __device__ __forceinline__ void step(int dx, int dy, int ww) {
+    x += dx;
+    y += dy;
+    if (x >= ww) {
+      x -= ww;
+      y += 1;
+    }
+  }
+};
+
+template <int NW, int QB, int MODE, bool POOL>
+__global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf16> p) {
+  constexpr int NT = 64 * NW;
+  constexpr int QW = 32 * QB;       // queries per wave
+  constexpr int VROW2 = KT + 4;     // V^T row stride (elements): 136 B, conflict-free 8-byte reads
+  static_assert(MODE == ATTN_GLOBAL || MODE == ATTN_SPATIAL, "large-window kernel");
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][KT * 64];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][64 * VROW2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 31, h = lane >> 5;
+  int bid = blockIdx.x;
+  const int head = bid % p.heads;
+  bid /= p.heads;
+  const int qt = bid % p.q_tiles;
+  bid /= p.q_tiles;
+  const int win = bid % p.windows;
+  const int b = bid / p.windows;
+  const int hd = p.head_dim, D = p.dim;
+  const int ld = (int)p.ld_qkv;
+  // element offset of this frame + window origin in qkv (fits 32 bits: the
+  // host checks the buffer size); token (x, y) of the window is at
+  // base + (y * grid_w + x) * ld
+  int origin = 0, ww = p.n_kv, gw = 0;
+  if (MODE == ATTN_SPATIAL) {
+    const int nwx = p.grid_w / p.win_w;
+    const int wy = win / nwx, wx = win - wy * nwx;
+    origin = (wy * p.win_h) * p.grid_w + wx * p.win_w;
+    ww = p.win_w;
+    gw = p.grid_w;
+  }
+  const bf16* base = p.qkv + (int64_t)b * p.tokens_in * ld;
+  auto tok = [&](const WinCursor& cur) { return MODE == ATTN_SPATIAL ? origin + cur.y * gw + cur.x : cur.x; };
+  // per-tile cursor step: KT positions = dy rows + dx columns of the window
+  const int step_dy = MODE == ATTN_SPATIAL ? KT / ww : 0;
+  const int step_dx = MODE == ATTN_SPATIAL ? KT - step_dy * ww : KT;
+  const int wwx = MODE == ATTN_SPATIAL ? ww : 0x7fffffff;
+
+  // ---- Q fragments: B operand of S^T; lane holds Q[q][16ks + 8h .. +7]
+  u32x4 qf[QB][4];
+  int qrow_out[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int i = qt * NW * QW + wave * QW + qb * 32 + fr;
+    const bool valid = i < p.n_q;
+    WinCursor cur;
+    cur.init(valid ? i : 0, wwx);
+    const int tq = tok(cur);
+    qrow_out[qb] = valid ? tq : -1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int off = ks * 16 + h * 8;
+      if (!valid || off >= hd) {
+        qf[qb][ks] = u32x4{0, 0, 0, 0};
+      } else if (!POOL) {
+        qf[qb][ks] = ld16(base + tq * ld + head * hd + off);
+      } else {
+        const int quarter = p.tokens_in / 4;
+        float mx[8], v[8];
+        unpack16<bf16>(ld16(base + tq * ld + head * hd + off), mx);
+#pragma unroll
+        for (int s = 1; s < 4; ++s) {
+          unpack16<bf16>(ld16(base + (tq + s * quarter) * ld + head * hd + off), v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], v[e]);
+        }
+        qf[qb][ks] = pack16<bf16>(mx);
+      }
+    }
+  }
+
+  // ---- K: direct to LDS. Wave instruction j covers key rows 8j .. 8j+7.
+  constexpr int KLOADS = KT / 8 / NW;
+  static_assert(KT % (8 * NW) == 0, "key rows must split over the waves");
+  WinCursor kcur[KLOADS];
+  int kchunk[KLOADS];
+#pragma unroll
+  for (int j = 0; j < KLOADS; ++j) {
+    const int row = (wave * KLOADS + j) * 8 + lane / 8;
+    kcur[j].init(row, wwx);
+    // chunks past head_dim read neighbouring finite values (Q is zero there)
+    kchunk[j] = min(((lane & 7) ^ kswz(row)) * 8, 2 * D - head * hd - 8) + D + head * hd;
+  }
+  const int last_kv = p.n_kv - 1;
+  WinCursor last_cur;
+  last_cur.init(last_kv, wwx);
+  auto issue_k = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < KLOADS; ++j) {
+      const int row = (wave * KLOADS + j) * 8 + lane / 8;
+      // keys past the window read the last key (masked out of the softmax)
+      const int t = kt * KT + row <= last_kv ? tok(kcur[j]) : tok(last_cur);
+      __builtin_amdgcn_global_load_lds((const void*)(base + t * ld + kchunk[j]),
+                                       (attn_lds_ptr)(&Ks[kt & 1][(wave * KLOADS + j) * 512]), 16, 0, 0);
+      kcur[j].step(step_dx, step_dy, wwx);
+    }
+  };
+  // ---- V: through registers, written transposed as packed key pairs.
+  // Work unit u -> (key pair jp = u % 32, 16-byte chunk c): lanes 0-31 and
+  // 32-63 of a wave take chunks two apart, so each ds_write_b32 of a wave
+  // (one d row per chunk, 32 consecutive key pairs) covers all 64 banks.
+  constexpr int VUNITS = 32 * 8 / NT;
+  static_assert(32 * 8 % NT == 0, "V units must split over the threads");
+  u32x4 vreg[VUNITS][2];
+  WinCursor vcur[VUNITS][2];
+  int vcol[VUNITS], vjp[VUNITS];
+  bool vok[VUNITS];
+#pragma unroll
+  for (int it = 0; it < VUNITS; ++it) {
+    const int u = tid + NT * it;
+    const int w = u >> 6, half = (u >> 5) & 1;
+    const int c = (w & 1) + ((w >> 1) << 2) + 2 * half;  // wave slots -> chunks {0,2},{1,3},{4,6},{5,7}
+    vjp[it] = u & 31;
+    vok[it] = c * 8 < hd;
+    vcol[it] = c * 8;
+    vcur[it][0].init(2 * vjp[it], wwx);
+    vcur[it][1].init(2 * vjp[it] + 1, wwx);
+  }
+  auto load_v = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < VUNITS; ++it)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kv = kt * KT + 2 * vjp[it] + e;
+        vreg[it][e] = (kv <= last_kv && vok[it]) ? ld16(base + tok(vcur[it][e]) * ld + 2 * D + head * hd + vcol[it])
+                                                  : u32x4{0, 0, 0, 0};
+        vcur[it][e].step(step_dx, step_dy, wwx);
+      }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < VUNITS; ++it) {
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, vreg[it][0]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, vreg[it][1]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bf16 pr[2] = {a0[k], a1[k]};
+        *reinterpret_cast<uint32_t*>(&Vt[buf][(vcol[it] + k) * VROW2 + 2 * vjp[it]]) =
+            *reinterpret_cast<const uint32_t*>(pr);
+      }
+    }
+  };
+
+  f32x16 acc_o[QB][2];  // [qb][db]: O^T[d = 32db + 8(r/4) + 4h + r%4][q]
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) acc_o[qb][db] = f32x16{};
+  float m_run[QB], l_part[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -1e30f;
+    l_part[qb] = 0.f;
+  }
+  const float c = p.scale_log2;
+
+  const int ntiles = (p.n_kv + KT - 1) / KT;
+  issue_k(0);
+  load_v(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
+    store_v(buf);
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      issue_k(kt + 1);
+      load_v(kt + 1);
+    }
+    f32x16 sacc[QB][2];  // [qb][kb]
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[qb][kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + fr;
+        const u32x4 kfr = ld16(&Ks[buf][row * 64 + ((ks * 2 + h) ^ kswz(row)) * 8]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfr),
+                                                                __builtin_bit_cast(bf16x8, qf[qb][ks]), sacc[qb][kb], 0, 0, 0);
+      }
+    }
+    const int kv_left = p.n_kv - kt * KT;
+    if (kv_left < KT) {  // uniform: only the last tile of a ragged window
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= kv_left) sacc[qb][kb][r] = -1e30f;
+    }
+    u32x4 pf[QB][2][2];  // [qb][kb][s]: bf16 P for MFMA k-step s of key block kb
+    bool moved = false;
+    float alpha[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = fmaxf(sacc[qb][0][0], sacc[qb][0][1]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[qb], mx);
+      moved |= m_new > m_run[qb];
+      alpha[qb] = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
+      m_run[qb] = m_new;
+      const float mc = m_new * c;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bf16x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][8 * s + e], c, -mc));
+            ls += pe;
+            pv[e] = (bf16)pe;
+          }
+          pf[qb][kb][s] = __builtin_bit_cast(u32x4, pv);
+        }
+      }
+      l_part[qb] = l_part[qb] * alpha[qb] + ls;
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) acc_o[qb][db] = acc_o[qb][db] * alpha[qb];
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const bf16* vrow = &Vt[buf][(db * 32 + fr) * VROW2 + kb * 32 + s * 16 + 4 * h];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+          const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
+                                                                   __builtin_bit_cast(bf16x8, pf[qb][kb][s]), acc_o[qb][db], 0, 0, 0);
+        }
+  }
+
+  // ---- normalise and store: lane holds ctx[q][32db + 8g + 4h .. +3], g = r/4
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
+    if (qrow_out[qb] < 0) continue;
+    const float inv = 1.0f / l;
+    bf16* out = p.ctx + ((int64_t)b * p.tokens_out + qrow_out[qb]) * p.ld_ctx + head * hd;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = db * 32 + 8 * gq + 4 * h;
+        if (d < hd)
+          store4<bf16>(out + d, f32x4{acc_o[qb][db][4 * gq], acc_o[qb][db][4 * gq + 1], acc_o[qb][db][4 * gq + 2],
+                                      acc_o[qb][db][4 * gq + 3]} * inv);
+      }
+  }
+}
+
+template <int NW, int QB, int MODE, bool POOL>
+static hipError_t attn32_go(AttnParams<bf16> p, int batch, hipStream_t s, StageEvents ev) {
+  p.q_tiles = (p.n_q + 32 * QB * NW - 1) / (32 * QB * NW);
+  const int64_t blocks = (int64_t)batch * p.windows * p.q_tiles * p.heads;
+  if (blocks == 0) return hipSuccess;
+  hipExtLaunchKernelGGL((attention_mfma32_kernel<NW, QB, MODE, POOL>), dim3((unsigned)blocks), dim3(64 * NW), 0, s,
+                        ev.start, ev.stop, 0, p);
+  return hipGetLastError();
+}
+
 template <typename T, int QB, int HPW, bool POOL>
 static hipError_t attn_go(const AttnArgs& a, AttnParams<T> p, hipStream_t s, StageEvents ev) {
   constexpr int rows = (4 / HPW) * 16 * QB;
@@ -318,6 +649,17 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
     p.n_kv = a.tokens_in;
   }
   const bool pool = a.q_stride == 4;
+  if constexpr (std::is_same<T, bf16>::value) {
+    // large global or spatial windows: 32x32 MFMA kernel (32-bit element
+    // offsets into the qkv buffer)
+    const int64_t qkv_elems = (int64_t)a.batch * a.tokens_in * a.ld_qkv;
+    if (p.n_q >= 128 && a.head_dim <= 64 && a.mode != ATTN_MASK_UNIT && qkv_elems < (1LL << 31)) {
+      if (a.mode == ATTN_SPATIAL)
+        return attn32_go<ATTN_NW, ATTN_QB, ATTN_SPATIAL, false>(p, a.batch, s, ev);
+      return pool ? attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, true>(p, a.batch, s, ev)
+                  : attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, false>(p, a.batch, s, ev);
+    }
+  }
   // small query sets: several heads per workgroup, one wave each
   if (p.n_q <= 16 && a.heads % 4 == 0) {
     return pool ? attn_go<T, 1, 4, true>(a, p, s, ev) : attn_go<T, 1, 4, false>(a, p, s, ev);
