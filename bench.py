@@ -31,7 +31,8 @@ DEFAULT_CONFIG = "c2_hiera_s0"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "vision_transformer_encoder_vit_amd", "csrc")
 STAGE_SOURCE = {"ln1": "rowops.hip", "ln2": "rowops.hip", "qkv": "gemm.hip", "residual": "gemm.hip",
-                "attn": "attention.hip", "proj": "gemm.hip", "fc1": "gemm.hip", "fc2": "gemm.hip"}
+                "attn": "attention.hip", "proj": "gemm.hip", "fc1": "gemm.hip", "fc2": "gemm.hip",
+                "fused": "fused_mu.hip"}
 
 
 def describe(spec):
@@ -74,6 +75,8 @@ def stage_work(spec):
     w["proj"] = (work.gemm_flops(*g["proj"]), work.gemm_bytes(*g["proj"], spec["dtype"], extra_rows_in=m_out))
     w["fc1"] = (work.gemm_flops(*g["fc1"]), work.gemm_bytes(*g["fc1"], spec["dtype"]))
     w["fc2"] = (work.gemm_flops(*g["fc2"]), work.gemm_bytes(*g["fc2"], spec["dtype"], extra_rows_in=m_out))
+    # whole block in one kernel: x in, y out, every weight once
+    w["fused"] = (work.block_flops(spec), work.block_min_bytes(spec))
     return w
 
 
@@ -139,6 +142,7 @@ def run(spec, steps, warmup, with_cpu):
         t = torch.from_numpy(np.ascontiguousarray(a))
         dev[k] = (t.to(dt) if (k == "x" or k.endswith("_w")) else t).cuda()
     plan = vb.Plan(vb.desc_from_spec(spec))
+    active = [n for i, n in enumerate(vb.STAGES) if plan.stage_mask() >> i & 1]
     w = vb.weights_struct(dev)
     y = torch.empty((spec["batch"], synth.out_tokens(spec), spec["dim_out"]), dtype=dt, device="cuda")
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
@@ -187,11 +191,11 @@ def run(spec, steps, warmup, with_cpu):
     ms_step = 1e3 * elapsed / steps
     tokens = spec["batch"] * spec["grid_h"] * spec["grid_w"]
     wk = stage_work(spec)
-    mfma_stages = [st for st in ("qkv", "residual", "attn", "proj", "fc1", "fc2") if wk[st][0] > 0]
+    mfma_stages = [st for st in ("qkv", "residual", "attn", "proj", "fc1", "fc2", "fused") if st in active]
     flops = sum(wk[s][0] for s in mfma_stages)
     t_mfma = sum(stage_us[s] for s in mfma_stages) * 1e-6
     peak_c = PEAK_BF16_TFLOPS if spec["dtype"] == "bf16" else PEAK_F32_TFLOPS
-    dom = max((st for st in stage_us if wk[st][1] > 0), key=lambda st: stage_us[st])
+    dom = max(active, key=lambda st: stage_us[st])
     f, by = wk[dom]
     t = stage_us[dom] * 1e-6
     ridge = peak_c * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -210,7 +214,7 @@ def run(spec, steps, warmup, with_cpu):
                    spec["grid_h"] * spec["grid_w"], "parallelism": "none (1 GPU)"},
         "attn_gemm_tflops": flops / t_mfma / 1e12,
         "attn_gemm_pct_of_peak": 100.0 * flops / t_mfma / 1e12 / peak_c,
-        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items() if k in active},
         "ms_per_step_with_stage_events": 1e3 * elapsed_timed / steps,
         "roofline": roof,
     }

@@ -177,8 +177,11 @@ vit_status vit_block_forward(vit_block_t plan, const vit_block_weights* w,
                              const void* x, void* y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* As vit_block_forward, and also writes every non-NULL seam buffer. The
- * result y is bit-identical to vit_block_forward's. */
+/* As vit_block_forward, and also writes every non-NULL seam buffer. It
+ * always runs the step-by-step kernels (one per stage), so where
+ * vit_block_forward uses the single fused kernel (bf16 mask units of 64
+ * tokens, width <= 128, q_stride 1) y differs from it by rounding only;
+ * otherwise the two are bit-identical. */
 vit_status vit_block_forward_seams(vit_block_t plan, const vit_block_weights* w,
                                    const void* x, void* y,
                                    const vit_block_seams* seams, void* workspace,
@@ -194,7 +197,9 @@ enum {
   VIT_STAGE_LN2 = 5,      /* LayerNorm of x1                              */
   VIT_STAGE_FC1 = 6,      /* fc1 + bias + GELU                            */
   VIT_STAGE_FC2 = 7,      /* fc2 + bias + residual                        */
-  VIT_NSTAGES = 8
+  VIT_STAGE_FUSED = 8,    /* the whole block in one kernel (small mask units;
+                             the other stages are then empty)              */
+  VIT_NSTAGES = 9
 };
 
 /* As vit_block_forward, for measurement: `events` holds n_events hipEvent_t
@@ -210,6 +215,11 @@ vit_status vit_block_forward_timed(vit_block_t plan, const vit_block_weights* w,
                                    const void* x, void* y, void* workspace,
                                    size_t workspace_bytes, void* stream,
                                    void* const* events, int32_t n_events);
+
+/* Which stages (bit i = VIT_STAGE_i) launch kernels in vit_block_forward
+ * and vit_block_forward_timed for this plan; the others record empty
+ * events. */
+vit_status vit_block_stage_mask(vit_block_t plan, uint32_t* mask);
 
 vit_status vit_block_destroy(vit_block_t plan);
 

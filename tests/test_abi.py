@@ -174,3 +174,14 @@ def test_single_step_validation():
     assert L.vit_pool4(P, 16, Q, 16, 1, 6, 16, vb.VIT_DTYPE_BF16, None) == vb.VIT_ERR_INVALID_ARG
     assert L.vit_pool4(P, 8, Q, 16, 1, 8, 16, vb.VIT_DTYPE_BF16, None) == vb.VIT_ERR_INVALID_ARG
     assert L.vit_pool4(None, 16, None, 16, 1, 0, 16, vb.VIT_DTYPE_BF16, None) == vb.VIT_OK
+
+
+def test_stage_mask():
+    names = vb.STAGES
+    m = vb.Plan(vb.desc_from_spec(synth.CONFIGS["c2_hiera_s0"])).stage_mask()
+    assert m == 1 << names.index("fused")
+    m = vb.Plan(vb.desc_from_spec(synth.CONFIGS["c5w_sam3_win"])).stage_mask()
+    assert not m >> names.index("residual") & 1 and m >> names.index("attn") & 1
+    assert not m >> names.index("fused") & 1
+    m = vb.Plan(vb.desc_from_spec(synth.CONFIGS["c3a_hiera_trans"])).stage_mask()
+    assert m >> names.index("residual") & 1

@@ -17,7 +17,7 @@ VIT_ATTN_GLOBAL, VIT_ATTN_MASK_UNIT, VIT_ATTN_SPATIAL = 0, 1, 2
 VIT_GELU_ERF, VIT_GELU_TANH = 0, 1
 VIT_QKV_FUSED, VIT_QKV_SEPARATE = 0, 1
 VIT_ROPE_NONE, VIT_ROPE_AXIAL_TABLE = 0, 1
-STAGES = ["ln1", "qkv", "residual", "attn", "proj", "ln2", "fc1", "fc2"]
+STAGES = ["ln1", "qkv", "residual", "attn", "proj", "ln2", "fc1", "fc2", "fused"]
 VIT_NSTAGES = len(STAGES)
 
 _i32, _f32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
@@ -72,6 +72,7 @@ def _load():
                                     ctypes.c_size_t, _vp],
         "vit_block_forward_timed": [_vp, P(vit_block_weights), _vp, _vp, _vp, ctypes.c_size_t, _vp,
                                     P(_vp), _i32],
+        "vit_block_stage_mask": [_vp, P(ctypes.c_uint32)],
         "vit_block_destroy": [_vp],
         "vit_layernorm": [_vp, _vp, _vp, _vp, ctypes.c_int64, _i32, _f32, _i32, _vp],
         "vit_unroll": [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
@@ -157,6 +158,11 @@ class Plan:
         n = ctypes.c_size_t()
         check(lib.vit_block_workspace_size(h, ctypes.byref(n)))
         self.workspace_bytes = n.value
+
+    def stage_mask(self):
+        m = ctypes.c_uint32()
+        check(lib.vit_block_stage_mask(self.handle, ctypes.byref(m)))
+        return m.value
 
     def forward(self, weights, x, y, workspace, stream=None):
         check(lib.vit_block_forward(self.handle, ctypes.byref(weights), _ptr(x), _ptr(y),

@@ -55,6 +55,7 @@ struct vit_block_plan {
   size_t esize;
   // workspace layout (byte offsets)
   size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, ws_bytes;
+  bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
 };
 
 static vit_status validate_desc(const vit_block_desc* d) {
@@ -141,6 +142,10 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   p->off_h2 = take(p->m_out, d.dim_out);
   p->off_u = take(p->m_out, d.mlp_hidden);
   p->ws_bytes = o;
+  p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 && d.attn_mode == VIT_ATTN_MASK_UNIT && d.q_stride == 1 &&
+                       d.rope == VIT_ROPE_NONE &&
+                       vit::fused_mask_unit_supported(d.dim_out, d.heads, p->head_dim, d.mlp_hidden, p->n_in / d.n_windows) &&
+                       vit::fused_mask_unit_lds_bytes(d.dim_out, d.mlp_hidden) <= 160 * 1024;
   *out = p;
   return ok();
 }
@@ -148,6 +153,16 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
 VIT_API vit_status vit_block_workspace_size(vit_block_t plan, size_t* bytes) {
   if (!plan || !bytes) return fail(VIT_ERR_INVALID_ARG, "plan or bytes pointer is NULL");
   *bytes = plan->ws_bytes;
+  return ok();
+}
+
+VIT_API vit_status vit_block_stage_mask(vit_block_t plan, uint32_t* mask) {
+  if (!plan || !mask) return fail(VIT_ERR_INVALID_ARG, "plan or mask pointer is NULL");
+  if (plan->fused_mask_unit) {
+    *mask = 1u << VIT_STAGE_FUSED;
+  } else {
+    *mask = ((1u << VIT_STAGE_FUSED) - 1) & ~(plan->d.q_stride == 4 ? 0u : 1u << VIT_STAGE_RESIDUAL);
+  }
   return ok();
 }
 
@@ -249,6 +264,61 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     return ev;
   };
   auto only_start = [](vit::StageEvents ev) { ev.stop = nullptr; return ev; };
+  auto mark_empty = [&](int stage) -> vit_status {
+    const vit::StageEvents ev = stage_ev(stage);
+    if (!ev.start) return VIT_OK;
+    vit_status r = device_status(hipEventRecord(ev.start, s), "hipEventRecord");
+    return r != VIT_OK ? r : device_status(hipEventRecord(ev.stop, s), "hipEventRecord");
+  };
+
+  // Small mask units: the whole block in one kernel per window (no seams:
+  // the step-by-step path below produces those).
+  if (!seams && P.fused_mask_unit) {
+    vit::FusedMUArgs f;
+    f.x = x;
+    f.y = y;
+    f.ln1_g = w->ln1_gamma;
+    f.ln1_b = w->ln1_beta;
+    f.ln2_g = w->ln2_gamma;
+    f.ln2_b = w->ln2_beta;
+    if (d.qkv_layout == VIT_QKV_FUSED) {
+      const size_t wseg = (size_t)Do * Di * P.esize;
+      f.wq = w->w_qkv;
+      f.wk = (const char*)w->w_qkv + wseg;
+      f.wv = (const char*)w->w_qkv + 2 * wseg;
+      f.bq = w->b_qkv;
+      f.bk = w->b_qkv + Do;
+      f.bv = w->b_qkv + 2 * Do;
+    } else {
+      f.wq = w->w_q;
+      f.wk = w->w_k;
+      f.wv = w->w_v;
+      f.bq = w->b_q;
+      f.bk = w->b_k;
+      f.bv = w->b_v;
+    }
+    f.wo = w->w_o;
+    f.bo = w->b_o;
+    f.w1 = w->w_fc1;
+    f.b1 = w->b_fc1;
+    f.w2 = w->w_fc2;
+    f.b2 = w->b_fc2;
+    f.batch = d.batch;
+    f.tokens = P.n_in;
+    f.n_windows = d.n_windows;
+    f.dim = Do;
+    f.heads = d.heads;
+    f.head_dim = hd;
+    f.mlp = F;
+    f.eps = d.ln_eps;
+    f.scale = d.attn_scale > 0.f ? d.attn_scale : 1.0f / std::sqrt((float)hd);
+    f.gelu_tanh = d.gelu == VIT_GELU_TANH;
+    for (int stg = 0; stg < VIT_STAGE_FUSED; ++stg)
+      if ((st = mark_empty(stg)) != VIT_OK) return st;
+    e = vit::launch_block_mask_unit_fused(f, s, stage_ev(VIT_STAGE_FUSED));
+    if ((st = device_status(e, "fused mask-unit block")) != VIT_OK) return st;
+    return ok();
+  }
   auto only_stop = [](vit::StageEvents ev) { ev.start = nullptr; return ev; };
 
   // 1. LN1
@@ -321,11 +391,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     }
   } else {
     // no kernel in this stage: mark it empty
-    const vit::StageEvents ev = stage_ev(VIT_STAGE_RESIDUAL);
-    if (ev.start) {
-      if ((st = device_status(hipEventRecord(ev.start, s), "hipEventRecord")) != VIT_OK) return st;
-      if ((st = device_status(hipEventRecord(ev.stop, s), "hipEventRecord")) != VIT_OK) return st;
-    }
+    if ((st = mark_empty(VIT_STAGE_RESIDUAL)) != VIT_OK) return st;
     if (S.r) {
       e = hipMemcpyAsync(S.r, x, x_bytes, hipMemcpyDeviceToDevice, s);
       if ((st = device_status(e, "copy (r seam)")) != VIT_OK) return st;
@@ -415,6 +481,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g2.ldbranch = Do;
   e = vit::launch_gemm(g2, dt, s, stage_ev(VIT_STAGE_FC2));
   if ((st = device_status(e, "gemm (fc2)")) != VIT_OK) return st;
+  if ((st = mark_empty(VIT_STAGE_FUSED)) != VIT_OK) return st;
   return ok();
 }
 

@@ -1,0 +1,340 @@
+// Whole encoder block for one Hiera mask unit in one workgroup.
+//
+// Mask-unit windows are independent through the entire block: LayerNorm,
+// the projections and the MLP act on token rows, and attention never leaves
+// the window (Hiera plan, "MaskUnitAttention"). So for small mask units
+// (64 tokens, width <= 128) a workgroup reads the window's 64 token rows
+// once, keeps every intermediate in LDS (h, q|k|v, V^T, ctx, x1, h2, u) and
+// writes the 64 output rows once: HBM traffic is x in, y out and the
+// (L2-resident) weights, instead of seven kernels' worth of round trips.
+//
+// Weights are read straight from global memory into MFMA fragments (each
+// 16-row weight tile is fetched once per workgroup and reused for all four
+// 16-token tiles); activations come from LDS. All products are 16x16x32
+// bf16 MFMAs with fp32 accumulation, with the weight tile as the A operand
+// so that a lane ends with 4 consecutive output columns of one token.
+#include "common.h"
+#include "launch.h"
+
+#include <hip/hip_ext.h>
+
+namespace vit {
+
+namespace {
+
+constexpr int TW = 64;             // tokens per mask unit
+constexpr int DP = 128;            // padded width (K of the D-wide products)
+constexpr int NWF = 8;             // waves per workgroup
+constexpr int XS = DP + 8;         // LDS row stride of the D-wide buffers (elements)
+constexpr int VTS = TW + 8;        // V^T row stride
+
+struct FusedParams {
+  const bf16* x;
+  bf16* y;
+  const float *ln1_g, *ln1_b, *ln2_g, *ln2_b;
+  const bf16 *wq, *wk, *wv;  // qkv weight rows for q, k and v (each [D, D])
+  const float *bq, *bk, *bv;
+  const bf16* wo;
+  const float* bo;
+  const bf16* w1;
+  const float* b1;
+  const bf16* w2;
+  const float* b2;
+  int tokens, n_windows, dim, heads, head_dim, mlp, qs, us;  // qs/us: LDS row strides of q|k|v and u
+  float eps, scale_log2;
+};
+
+__device__ __forceinline__ float gelu_erf_d(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_tanh_d(float v) {
+  return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
+}
+
+// Row LayerNorm of the window's 64 rows (src -> dst, both LDS, stride XS),
+// 8 lanes per row; columns D..DP-1 of dst are written as zeros so that dst
+// can feed a K=DP product.
+__device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float* g, const float* bta, int D, float eps) {
+  const int tid = threadIdx.x;
+  const int row = tid >> 3, l8 = tid & 7;
+  const int nch = D / 8;
+  float v[2][8];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = l8 + 8 * i;
+    if (c < nch) {
+      unpack16<bf16>(ld16(src + row * XS + c * 8), v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[i][e];
+    }
+  }
+#pragma unroll
+  for (int m = 4; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+  const float mean = s / (float)D;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (l8 + 8 * i < nch)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
+#pragma unroll
+  for (int m = 4; m > 0; m >>= 1) q += __shfl_xor(q, m, 64);
+  const float inv = 1.0f / sqrtf(q / (float)D + eps);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = l8 + 8 * i;
+    float o[8];
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (v[i][e] - mean) * inv * g[c * 8 + e] + bta[c * 8 + e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    }
+    st16(dst + row * XS + c * 8, pack16<bf16>(o));
+  }
+}
+
+// C[64, N] = act(LDS A[64, K] * W[N, K]^T): each wave takes 16-row weight
+// tiles nt = wave, wave + NWF, ...; the tile's fragments are fetched four K
+// steps at a time (zero past kreal) and each is reused for the four 16-token
+// tiles. epi(m, n, v) receives 4 consecutive output columns n..n+3 of token m.
+template <typename Wsel, typename Epi>
+__device__ __forceinline__ void window_gemm(const bf16* As, int lda, int N, int kreal, Wsel wrow, Epi epi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 15, g = lane >> 4;
+  const int ksteps = (kreal + 31) / 32;
+  for (int nt = wave; nt * 16 < N; nt += NWF) {
+    const bf16* wr = wrow(nt * 16 + fr);
+    f32x4 acc[TW / 16];
+#pragma unroll
+    for (int mt = 0; mt < TW / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ksteps; k0 += 4) {
+      u32x4 wf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = (k0 + kk) * 32 + g * 8;
+        wf[kk] = k < kreal ? ld16(wr + k) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int mt = 0; mt < TW / 16; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          if (k0 + kk < ksteps)
+            acc[mt] = Mma<bf16>::step(wf[kk], ld16(As + (mt * 16 + fr) * lda + (k0 + kk) * 32 + g * 8), acc[mt]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < TW / 16; ++mt) epi(mt * 16 + fr, nt * 16 + 4 * g, acc[mt]);
+  }
+}
+
+template <bool TANH>
+__global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p) {
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  bf16* xs = smem;                   // x rows            [TW][XS]
+  bf16* cs = xs + TW * XS;           // h, then ctx, then h2
+  bf16* x1s = cs + TW * XS;          // x1 rows
+  bf16* qkvs = x1s + TW * XS;        // q|k|v rows        [TW][qs]
+  bf16* vts = qkvs + TW * p.qs;      // V^T per head pair [2][64][VTS]
+  bf16* uss = qkvs;                  // u rows (after attention) [TW][us]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = p.dim, hd = p.head_dim;
+  const int win = blockIdx.x % p.n_windows, b = blockIdx.x / p.n_windows;
+  const int64_t row0 = (int64_t)b * p.tokens + win;  // global row of token t: row0 + t * n_windows
+
+  // ---- x rows of the window -> LDS
+  const int nch = D / 8;
+  for (int e = tid; e < TW * nch; e += 64 * NWF) {
+    const int t = e / nch, c = e - t * nch;
+    st16(xs + t * XS + c * 8, ld16(p.x + (row0 + (int64_t)t * p.n_windows) * D + c * 8));
+  }
+  __syncthreads();
+  // ---- LN1 -> cs
+  ln_rows(xs, cs, p.ln1_g, p.ln1_b, D, p.eps);
+  __syncthreads();
+  // ---- q|k|v = h W^T + b -> qkvs
+  window_gemm(cs, XS, 3 * D, D,
+      [&](int n) { return n < D ? p.wq + (int64_t)n * D : (n < 2 * D ? p.wk + (int64_t)(n - D) * D : p.wv + (int64_t)(n - 2 * D) * D); },
+      [&](int m, int n, f32x4 v) {
+        const float* bb = n < D ? p.bq + n : (n < 2 * D ? p.bk + (n - D) : p.bv + (n - 2 * D));
+        store4<bf16>(qkvs + m * p.qs + n, v + *reinterpret_cast<const f32x4*>(bb));
+      });
+  __syncthreads();
+
+  // ---- attention, two heads per round (waves 0-3: head h0, waves 4-7: h0+1)
+  const int fr = lane & 15, g = lane >> 4;
+  for (int h0 = 0; h0 < p.heads; h0 += 2) {
+    // V^T of the two heads: [hl][d][key], zero past head_dim
+    for (int e = tid; e < 2 * TW * 8; e += 64 * NWF) {
+      const int hl = e / (TW * 8), rem = e - hl * TW * 8;
+      const int key = rem >> 3, c = rem & 7;
+      const int head = h0 + hl;
+      u32x4 v = {0, 0, 0, 0};
+      if (head < p.heads && c * 8 < hd) v = ld16(qkvs + key * p.qs + 2 * D + head * hd + c * 8);
+      const bf16x8 vv = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vts[(hl * 64 + c * 8 + k) * VTS + key] = vv[k];
+    }
+    __syncthreads();
+    const int hl = wave >> 2, qb = wave & 3, head = h0 + hl;
+    if (head < p.heads) {
+      // S^T = K Q^T: s[kb][r] = S[q = qb*16 + fr][key = kb*16 + 4g + r]
+      u32x4 qf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int off = (ks * 4 + g) * 8;
+        qf[ks] = off < hd ? ld16(qkvs + (qb * 16 + fr) * p.qs + head * hd + off) : u32x4{0, 0, 0, 0};
+      }
+      f32x4 s[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int off = (ks * 4 + g) * 8;
+          const u32x4 kf = off < hd ? ld16(qkvs + (kb * 16 + fr) * p.qs + D + head * hd + off) : u32x4{0, 0, 0, 0};
+          s[kb] = Mma<bf16>::step(kf, qf[ks], s[kb]);
+        }
+      }
+      float mx = -1e30f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float c = p.scale_log2, mc = mx * c;
+      float l = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+          s[kb][r] = e;
+          l += e;
+        }
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      // O^T = V^T P^T over two 32-key steps
+      f32x4 o[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[r] = (bf16)s[2 * c2][r];
+          pv[4 + r] = (bf16)s[2 * c2 + 1][r];
+        }
+        const u32x4 pf = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16* vr = vts + (hl * 64 + db * 16 + fr) * VTS + 32 * c2 + 4 * g;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16);
+          o[db] = Mma<bf16>::step(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, o[db]);
+        }
+      }
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int d = db * 16 + 4 * g;
+        if (d < hd) store4<bf16>(cs + (qb * 16 + fr) * XS + head * hd + d, o[db] * inv);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- x1 = x + ctx W_o^T + b_o -> x1s (cs columns D..DP-1 are still zero)
+  window_gemm(cs, XS, D, D, [&](int n) { return p.wo + (int64_t)n * D; },
+      [&](int m, int n, f32x4 v) {
+        v = v + *reinterpret_cast<const f32x4*>(p.bo + n) + load4<bf16>(xs + m * XS + n);
+        store4<bf16>(x1s + m * XS + n, v);
+      });
+  __syncthreads();
+  // ---- LN2 -> cs
+  ln_rows(x1s, cs, p.ln2_g, p.ln2_b, D, p.eps);
+  __syncthreads();
+  // ---- u = GELU(h2 W_1^T + b_1) -> uss
+  window_gemm(cs, XS, p.mlp, D, [&](int n) { return p.w1 + (int64_t)n * D; },
+      [&](int m, int n, f32x4 v) {
+        v = v + *reinterpret_cast<const f32x4*>(p.b1 + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = TANH ? gelu_tanh_d(v[e]) : gelu_erf_d(v[e]);
+        store4<bf16>(uss + m * p.us + n, v);
+      });
+  __syncthreads();
+  // ---- y = x1 + u W_2^T + b_2 -> global
+  window_gemm(uss, p.us, D, p.mlp, [&](int n) { return p.w2 + (int64_t)n * p.mlp; },
+      [&](int m, int n, f32x4 v) {
+        v = v + *reinterpret_cast<const f32x4*>(p.b2 + n) + load4<bf16>(x1s + m * XS + n);
+        store4<bf16>(p.y + (row0 + (int64_t)m * p.n_windows) * D + n, v);
+      });
+}
+
+}  // namespace
+
+bool fused_mask_unit_supported(int dim, int heads, int head_dim, int mlp, int window_tokens) {
+  return window_tokens == TW && dim % 16 == 0 && dim <= DP && head_dim % 8 == 0 && head_dim <= 64 &&
+         heads * head_dim == dim && mlp % 32 == 0 && mlp <= 512;
+}
+
+size_t fused_mask_unit_lds_bytes(int dim, int mlp) {
+  const size_t qs = 3 * dim + 8, us = mlp + 8;
+  const size_t a = TW * qs + 2 * 64 * VTS, u = TW * us;
+  return 2 * (3 * TW * XS + (a > u ? a : u));
+}
+
+hipError_t launch_block_mask_unit_fused(const FusedMUArgs& a, hipStream_t s, StageEvents ev) {
+  FusedParams p;
+  p.x = (const bf16*)a.x;
+  p.y = (bf16*)a.y;
+  p.ln1_g = a.ln1_g;
+  p.ln1_b = a.ln1_b;
+  p.ln2_g = a.ln2_g;
+  p.ln2_b = a.ln2_b;
+  p.wq = (const bf16*)a.wq;
+  p.wk = (const bf16*)a.wk;
+  p.wv = (const bf16*)a.wv;
+  p.bq = a.bq;
+  p.bk = a.bk;
+  p.bv = a.bv;
+  p.wo = (const bf16*)a.wo;
+  p.bo = a.bo;
+  p.w1 = (const bf16*)a.w1;
+  p.b1 = a.b1;
+  p.w2 = (const bf16*)a.w2;
+  p.b2 = a.b2;
+  p.tokens = a.tokens;
+  p.n_windows = a.n_windows;
+  p.dim = a.dim;
+  p.heads = a.heads;
+  p.head_dim = a.head_dim;
+  p.mlp = a.mlp;
+  p.qs = 3 * a.dim + 8;
+  p.us = a.mlp + 8;
+  p.eps = a.eps;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  const size_t lds = fused_mask_unit_lds_bytes(a.dim, a.mlp);
+  const int64_t blocks = (int64_t)a.batch * a.n_windows;
+  if (blocks == 0) return hipSuccess;
+  // allow more than the default dynamic LDS (once per process; idempotent)
+  static const hipError_t attr_ok = [] {
+    hipError_t e1 = hipFuncSetAttribute((const void*)block_mask_unit_kernel<true>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e2 = hipFuncSetAttribute((const void*)block_mask_unit_kernel<false>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return e1 != hipSuccess ? e1 : e2;
+  }();
+  if (attr_ok != hipSuccess) return attr_ok;
+  if (a.gelu_tanh)
+    hipExtLaunchKernelGGL((block_mask_unit_kernel<true>), dim3((unsigned)blocks), dim3(64 * NWF), lds, s, ev.start,
+                          ev.stop, 0, p);
+  else
+    hipExtLaunchKernelGGL((block_mask_unit_kernel<false>), dim3((unsigned)blocks), dim3(64 * NWF), lds, s, ev.start,
+                          ev.stop, 0, p);
+  return hipGetLastError();
+}
+
+}  // namespace vit

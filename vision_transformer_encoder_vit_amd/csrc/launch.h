@@ -63,6 +63,28 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 
+// Whole block for 64-token mask units of width <= 128 in one kernel
+// (q_stride 1): x [B*tokens, dim] -> y, one workgroup per (frame, window).
+struct FusedMUArgs {
+  const void* x = nullptr;
+  void* y = nullptr;
+  const float *ln1_g = nullptr, *ln1_b = nullptr, *ln2_g = nullptr, *ln2_b = nullptr;
+  const void *wq = nullptr, *wk = nullptr, *wv = nullptr;
+  const float *bq = nullptr, *bk = nullptr, *bv = nullptr;
+  const void* wo = nullptr;
+  const float* bo = nullptr;
+  const void* w1 = nullptr;
+  const float* b1 = nullptr;
+  const void* w2 = nullptr;
+  const float* b2 = nullptr;
+  int batch = 1, tokens = 0, n_windows = 1, dim = 0, heads = 1, head_dim = 0, mlp = 0;
+  float eps = 1e-6f, scale = 1.f;
+  bool gelu_tanh = false;
+};
+bool fused_mask_unit_supported(int dim, int heads, int head_dim, int mlp, int window_tokens);
+size_t fused_mask_unit_lds_bytes(int dim, int mlp);
+hipError_t launch_block_mask_unit_fused(const FusedMUArgs& a, hipStream_t s, StageEvents ev = {});
+
 hipError_t launch_layernorm(const void* x, void* y, const float* g, const float* b,
                             int64_t rows, int dim, float eps, DType dt, hipStream_t s,
                             StageEvents ev = {});

@@ -80,6 +80,21 @@ def gemm_bytes(m, n, k, dtype, extra_rows_in=0):
     return float(e * (m * k + n * k + m * n + extra_rows_in * n))
 
 
+def block_min_bytes(spec):
+    """Minimum HBM traffic of a whole block: x read once, y written once,
+    every weight matrix and vector read once."""
+    from . import synth
+    e = DTYPE_BYTES[spec["dtype"]]
+    total = 0.0
+    for name, shape in synth.tensor_shapes(spec).items():
+        n = 1
+        for s in shape:
+            n *= s
+        total += n * (e if (name == "x" or name.endswith("_w")) else 4)
+    total += spec["batch"] * synth.out_tokens(spec) * spec["dim_out"] * e  # y
+    return total
+
+
 def block_tokens(spec):
     return spec["batch"] * spec["grid_h"] * spec["grid_w"]
 
