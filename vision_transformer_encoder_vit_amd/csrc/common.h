@@ -97,6 +97,23 @@ template <> struct Mma<float> {
   }
 };
 
+// erf-form GELU, 0.5 v (1 + erf(v / sqrt 2)). erf(z), z >= 0, by the
+// rational approximation of Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (|error| <= 1.5e-7): with t = 1 / (1 + p z),
+// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2); erf is odd.
+// Two hardware transcendentals (reciprocal, exp2) and six FMAs.
+__device__ __forceinline__ float gelu_erf_as(float v) {
+  const float z = fabsf(v) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
+  float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+  poly = __builtin_fmaf(t, poly, 1.421413741f);
+  poly = __builtin_fmaf(t, poly, -0.284496736f);
+  poly = __builtin_fmaf(t, poly, 0.254829592f);
+  poly *= t;
+  const float erf_z = __builtin_fmaf(-poly, __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f), 1.0f);
+  return 0.5f * v * (1.0f + copysignf(erf_z, v));
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -25,8 +25,13 @@ namespace {
 constexpr int TW = 64;             // tokens per mask unit
 constexpr int DP = 128;            // padded width (K of the D-wide products)
 constexpr int NWF = 8;             // waves per workgroup
+constexpr int HPR = NWF / 4;       // heads per attention round (4 waves of 16 queries each)
 constexpr int XS = DP + 8;         // LDS row stride of the D-wide buffers (elements)
 constexpr int VTS = TW + 8;        // V^T row stride
+constexpr int QS_MAX = 3 * DP + 8;  // q|k|v row stride for the widest supported block
+constexpr int US_MAX = 512 + 8;     // u row stride for the widest supported MLP
+constexpr int A_MAX = (TW * QS_MAX + 2 * 64 * VTS) > (TW * US_MAX) ? (TW * QS_MAX + 2 * 64 * VTS) : (TW * US_MAX);
+constexpr int LDS_ELEMS = 3 * TW * XS + A_MAX + 2 * 4 * DP;  // bf16 elements, LN parameters (fp32) last
 
 struct FusedParams {
   const bf16* x;
@@ -44,7 +49,7 @@ struct FusedParams {
   float eps, scale_log2;
 };
 
-__device__ __forceinline__ float gelu_erf_d(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_erf_d(float v) { return gelu_erf_as(v); }
 __device__ __forceinline__ float gelu_tanh_d(float v) {
   return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
 }
@@ -94,72 +99,109 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
   }
 }
 
-// C[64, N] = act(LDS A[64, K] * W[N, K]^T): each wave takes 16-row weight
-// tiles nt = wave, wave + NWF, ...; the tile's fragments are fetched four K
-// steps at a time (zero past kreal) and each is reused for the four 16-token
-// tiles. epi(m, n, v) receives 4 consecutive output columns n..n+3 of token m.
-template <typename Wsel, typename Epi>
-__device__ __forceinline__ void window_gemm(const bf16* As, int lda, int N, int kreal, Wsel wrow, Epi epi) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int fr = lane & 15, g = lane >> 4;
-  const int ksteps = (kreal + 31) / 32;
-  for (int nt = wave; nt * 16 < N; nt += NWF) {
-    const bf16* wr = wrow(nt * 16 + fr);
-    f32x4 acc[TW / 16];
+// Weight fragments of one product, held in registers: this wave's 16-row
+// weight tiles nt = wave + i*NWF (i < NTM) for K steps kk < KSM (16x32 each,
+// zero past N or kreal). Loading them one phase ahead hides the L2 latency
+// behind the previous phase's work.
+template <int NTM, int KSM>
+struct WFrags {
+  u32x4 f[NTM][KSM];
+  template <typename Wsel>
+  __device__ __forceinline__ void load(Wsel wrow, int N, int kreal) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int fr = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int mt = 0; mt < TW / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < ksteps; k0 += 4) {
-      u32x4 wf[4];
+    for (int i = 0; i < NTM; ++i) {
+      const int nt = wave + i * NWF;
+      const bool nok = nt * 16 < N;
+      const bf16* wr = wrow(nok ? nt * 16 + fr : 0);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int k = (k0 + kk) * 32 + g * 8;
-        wf[kk] = k < kreal ? ld16(wr + k) : u32x4{0, 0, 0, 0};
+      for (int kk = 0; kk < KSM; ++kk) {
+        const int k = kk * 32 + g * 8;
+        f[i][kk] = (nok && k < kreal) ? ld16(wr + k) : u32x4{0, 0, 0, 0};
       }
-#pragma unroll
-      for (int mt = 0; mt < TW / 16; ++mt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          if (k0 + kk < ksteps)
-            acc[mt] = Mma<bf16>::step(wf[kk], ld16(As + (mt * 16 + fr) * lda + (k0 + kk) * 32 + g * 8), acc[mt]);
     }
-#pragma unroll
-    for (int mt = 0; mt < TW / 16; ++mt) epi(mt * 16 + fr, nt * 16 + 4 * g, acc[mt]);
   }
+  // C[64, N] = LDS A[64, K] * W^T; epi(m, n, v) gets 4 consecutive columns
+  // n..n+3 of token m; each weight fragment is reused for 4 token tiles.
+  template <typename Epi>
+  __device__ __forceinline__ void gemm(const bf16* As, int lda, int N, int kreal, Epi epi) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int fr = lane & 15, g = lane >> 4;
+    const int ksteps = (kreal + 31) / 32;
+#pragma unroll
+    for (int i = 0; i < NTM; ++i) {
+      const int nt = wave + i * NWF;
+      if (nt * 16 >= N) break;
+#pragma unroll
+      for (int mt = 0; mt < TW / 16; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KSM; ++kk)
+          if (kk < ksteps) acc = Mma<bf16>::step(f[i][kk], ld16(As + (mt * 16 + fr) * lda + kk * 32 + g * 8), acc);
+        epi(mt * 16 + fr, nt * 16 + 4 * g, acc);
+      }
+    }
+  }
+};
+
+// Workgroup barrier that waits only for this wave's LDS operations, so
+// weight loads issued for a later phase stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <bool TANH>
 __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p) {
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  // one static allocation sized for the largest supported block (static LDS
+  // can use the CU's full 160 KB)
+  __shared__ __attribute__((aligned(16))) bf16 smem[LDS_ELEMS];
   bf16* xs = smem;                   // x rows            [TW][XS]
   bf16* cs = xs + TW * XS;           // h, then ctx, then h2
   bf16* x1s = cs + TW * XS;          // x1 rows
   bf16* qkvs = x1s + TW * XS;        // q|k|v rows        [TW][qs]
   bf16* vts = qkvs + TW * p.qs;      // V^T per head pair [2][64][VTS]
   bf16* uss = qkvs;                  // u rows (after attention) [TW][us]
+  float* lnp = reinterpret_cast<float*>(smem + 3 * TW * XS + A_MAX);  // LN1/LN2 g, b [4][DP]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = p.dim, hd = p.head_dim;
   const int win = blockIdx.x % p.n_windows, b = blockIdx.x / p.n_windows;
   const int64_t row0 = (int64_t)b * p.tokens + win;  // global row of token t: row0 + t * n_windows
 
-  // ---- x rows of the window -> LDS
+  // ---- x rows of the window and the LN parameters -> LDS; q|k|v weights
   const int nch = D / 8;
   for (int e = tid; e < TW * nch; e += 64 * NWF) {
     const int t = e / nch, c = e - t * nch;
     st16(xs + t * XS + c * 8, ld16(p.x + (row0 + (int64_t)t * p.n_windows) * D + c * 8));
   }
-  __syncthreads();
+  for (int e = tid; e < 4 * D; e += 64 * NWF) {
+    const int which = e / D, c = e - which * D;
+    const float* src = which == 0 ? p.ln1_g : which == 1 ? p.ln1_b : which == 2 ? p.ln2_g : p.ln2_b;
+    lnp[which * DP + c] = src[c];
+  }
+  WFrags<3, DP / 32> wqkv;
+  wqkv.load([&](int n) { return n < D ? p.wq + (int64_t)n * D : (n < 2 * D ? p.wk + (int64_t)(n - D) * D : p.wv + (int64_t)(n - 2 * D) * D); },
+            3 * D, D);
+  lds_barrier();
   // ---- LN1 -> cs
-  ln_rows(xs, cs, p.ln1_g, p.ln1_b, D, p.eps);
-  __syncthreads();
+  ln_rows(xs, cs, lnp, lnp + DP, D, p.eps);
+  WFrags<1, DP / 32> wo;
+  wo.load([&](int n) { return p.wo + (int64_t)n * D; }, D, D);
+  lds_barrier();
   // ---- q|k|v = h W^T + b -> qkvs
-  window_gemm(cs, XS, 3 * D, D,
-      [&](int n) { return n < D ? p.wq + (int64_t)n * D : (n < 2 * D ? p.wk + (int64_t)(n - D) * D : p.wv + (int64_t)(n - 2 * D) * D); },
+  wqkv.gemm(cs, XS, 3 * D, D,
       [&](int m, int n, f32x4 v) {
         const float* bb = n < D ? p.bq + n : (n < 2 * D ? p.bk + (n - D) : p.bv + (n - 2 * D));
         store4<bf16>(qkvs + m * p.qs + n, v + *reinterpret_cast<const f32x4*>(bb));
       });
-  __syncthreads();
+  WFrags<4, DP / 32> w1;
+  w1.load([&](int n) { return p.w1 + (int64_t)n * D; }, p.mlp, D);
+  lds_barrier();
 
   // ---- attention, two heads per round (waves 0-3: head h0, waves 4-7: h0+1)
   const int fr = lane & 15, g = lane >> 4;
@@ -175,7 +217,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
 #pragma unroll
       for (int k = 0; k < 8; ++k) vts[(hl * 64 + c * 8 + k) * VTS + key] = vv[k];
     }
-    __syncthreads();
+    lds_barrier();
     const int hl = wave >> 2, qb = wave & 3, head = h0 + hl;
     if (head < p.heads) {
       // S^T = K Q^T: s[kb][r] = S[q = qb*16 + fr][key = kb*16 + 4g + r]
@@ -243,30 +285,32 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
         if (d < hd) store4<bf16>(cs + (qb * 16 + fr) * XS + head * hd + d, o[db] * inv);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- x1 = x + ctx W_o^T + b_o -> x1s (cs columns D..DP-1 are still zero)
-  window_gemm(cs, XS, D, D, [&](int n) { return p.wo + (int64_t)n * D; },
+  wo.gemm(cs, XS, D, D,
       [&](int m, int n, f32x4 v) {
         v = v + *reinterpret_cast<const f32x4*>(p.bo + n) + load4<bf16>(xs + m * XS + n);
         store4<bf16>(x1s + m * XS + n, v);
       });
-  __syncthreads();
+  lds_barrier();
   // ---- LN2 -> cs
-  ln_rows(x1s, cs, p.ln2_g, p.ln2_b, D, p.eps);
-  __syncthreads();
+  ln_rows(x1s, cs, lnp + 2 * DP, lnp + 3 * DP, D, p.eps);
+  WFrags<1, 16> w2;
+  w2.load([&](int n) { return p.w2 + (int64_t)n * p.mlp; }, D, p.mlp);
+  lds_barrier();
   // ---- u = GELU(h2 W_1^T + b_1) -> uss
-  window_gemm(cs, XS, p.mlp, D, [&](int n) { return p.w1 + (int64_t)n * D; },
+  w1.gemm(cs, XS, p.mlp, D,
       [&](int m, int n, f32x4 v) {
         v = v + *reinterpret_cast<const f32x4*>(p.b1 + n);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = TANH ? gelu_tanh_d(v[e]) : gelu_erf_d(v[e]);
         store4<bf16>(uss + m * p.us + n, v);
       });
-  __syncthreads();
+  lds_barrier();
   // ---- y = x1 + u W_2^T + b_2 -> global
-  window_gemm(uss, p.us, D, p.mlp, [&](int n) { return p.w2 + (int64_t)n * p.mlp; },
+  w2.gemm(uss, p.us, D, p.mlp,
       [&](int m, int n, f32x4 v) {
         v = v + *reinterpret_cast<const f32x4*>(p.b2 + n) + load4<bf16>(x1s + m * XS + n);
         store4<bf16>(p.y + (row0 + (int64_t)m * p.n_windows) * D + n, v);
@@ -316,23 +360,13 @@ hipError_t launch_block_mask_unit_fused(const FusedMUArgs& a, hipStream_t s, Sta
   p.us = a.mlp + 8;
   p.eps = a.eps;
   p.scale_log2 = a.scale * 1.4426950408889634f;
-  const size_t lds = fused_mask_unit_lds_bytes(a.dim, a.mlp);
   const int64_t blocks = (int64_t)a.batch * a.n_windows;
   if (blocks == 0) return hipSuccess;
-  // allow more than the default dynamic LDS (once per process; idempotent)
-  static const hipError_t attr_ok = [] {
-    hipError_t e1 = hipFuncSetAttribute((const void*)block_mask_unit_kernel<true>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    hipError_t e2 = hipFuncSetAttribute((const void*)block_mask_unit_kernel<false>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    return e1 != hipSuccess ? e1 : e2;
-  }();
-  if (attr_ok != hipSuccess) return attr_ok;
   if (a.gelu_tanh)
-    hipExtLaunchKernelGGL((block_mask_unit_kernel<true>), dim3((unsigned)blocks), dim3(64 * NWF), lds, s, ev.start,
+    hipExtLaunchKernelGGL((block_mask_unit_kernel<true>), dim3((unsigned)blocks), dim3(64 * NWF), 0, s, ev.start,
                           ev.stop, 0, p);
   else
-    hipExtLaunchKernelGGL((block_mask_unit_kernel<false>), dim3((unsigned)blocks), dim3(64 * NWF), lds, s, ev.start,
+    hipExtLaunchKernelGGL((block_mask_unit_kernel<false>), dim3((unsigned)blocks), dim3(64 * NWF), 0, s, ev.start,
                           ev.stop, 0, p);
   return hipGetLastError();
 }

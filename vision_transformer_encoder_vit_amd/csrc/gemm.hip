@@ -40,7 +40,7 @@ struct GemmParams {
   int rope_cols, head_dim, rope_mode, tokens_per_frame, grid_w, win_h, win_w;
 };
 
-__device__ __forceinline__ float gelu_erf_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_erf_f(float v) { return gelu_erf_as(v); }
 __device__ __forceinline__ float gelu_tanh_f(float v) {
   return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
 }
