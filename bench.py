@@ -223,6 +223,25 @@ def run(spec, steps, warmup, with_cpu):
     return line
 
 
+COPY_ROWS, COPY_COLS = 65536, 512  # 64 MiB of bf16 read and 64 MiB written per copy
+
+
+def copy_calibration(steps):
+    """K launches of a plain row copy (the unroll kernel with zero levels is
+    the identity permutation): each reads and writes exactly
+    COPY_ROWS * COPY_COLS * 2 bytes. Prints those bytes per launch."""
+    import torch
+    from vision_transformer_encoder_vit_amd import binding as vb
+    x = torch.randn(1, COPY_ROWS, COPY_COLS, device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        vb.vit_unroll(x, y, COPY_ROWS, 1, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)
+    print(json.dumps({"copy_bytes_read_per_launch": COPY_ROWS * COPY_COLS * 2,
+                      "copy_bytes_written_per_launch": COPY_ROWS * COPY_COLS * 2, "launches": steps}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +249,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=DEFAULT_CONFIG, help="workload name, or 'all'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (vit_unroll with 0 levels), to scale "
+                         "rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported (use --gpus 1)" % args.gpus,
@@ -237,6 +259,9 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         ap.error("steps >= 1 and warmup >= 0")
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     from vision_transformer_encoder_vit_amd import synth
     names = list(synth.CONFIGS) if args.config == "all" else [args.config]
     for n in names:
