@@ -24,14 +24,18 @@ namespace {
 
 constexpr int TW = 64;             // tokens per mask unit
 constexpr int DP = 128;            // padded width (K of the D-wide products)
-constexpr int NWF = 8;             // waves per workgroup
+#ifndef FUSED_WAVES
+#define FUSED_WAVES 16
+#endif
+constexpr int NWF = FUSED_WAVES;   // waves per workgroup
 constexpr int HPR = NWF / 4;       // heads per attention round (4 waves of 16 queries each)
 constexpr int XS = DP + 8;         // LDS row stride of the D-wide buffers (elements)
 constexpr int VTS = TW + 8;        // V^T row stride
 constexpr int QS_MAX = 3 * DP + 8;  // q|k|v row stride for the widest supported block
 constexpr int US_MAX = 512 + 8;     // u row stride for the widest supported MLP
-constexpr int A_MAX = (TW * QS_MAX + 2 * 64 * VTS) > (TW * US_MAX) ? (TW * QS_MAX + 2 * 64 * VTS) : (TW * US_MAX);
-constexpr int LDS_ELEMS = 3 * TW * XS + A_MAX + 2 * 4 * DP;  // bf16 elements, LN parameters (fp32) last
+constexpr int A_MAX = (TW * QS_MAX + HPR * 64 * VTS) > (TW * US_MAX) ? (TW * QS_MAX + HPR * 64 * VTS) : (TW * US_MAX);
+constexpr int BIAS_MAX = 3 * DP + DP + 512 + DP;  // b_q|b_k|b_v, b_o, b_1, b_2 (fp32)
+constexpr int LDS_ELEMS = 3 * TW * XS + A_MAX + 2 * 4 * DP + 2 * BIAS_MAX;  // bf16 elements; fp32 LN params and biases last
 
 struct FusedParams {
   const bf16* x;
@@ -58,14 +62,17 @@ __device__ __forceinline__ float gelu_tanh_d(float v) {
 // 8 lanes per row; columns D..DP-1 of dst are written as zeros so that dst
 // can feed a K=DP product.
 __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float* g, const float* bta, int D, float eps) {
+  constexpr int LPR = NWF;             // lanes per row: 64 rows over 64*NWF threads
+  constexpr int CPL = (DP / 8) / LPR;  // 16-byte chunks per lane
+  static_assert(CPL >= 1 && LPR <= 64, "LayerNorm lane split");
   const int tid = threadIdx.x;
-  const int row = tid >> 3, l8 = tid & 7;
+  const int row = tid / LPR, l8 = tid % LPR;
   const int nch = D / 8;
-  float v[2][8];
+  float v[CPL][8];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = l8 + 8 * i;
+  for (int i = 0; i < CPL; ++i) {
+    const int c = l8 + LPR * i;
     if (c < nch) {
       unpack16<bf16>(ld16(src + row * XS + c * 8), v[i]);
 #pragma unroll
@@ -73,20 +80,20 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
     }
   }
 #pragma unroll
-  for (int m = 4; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+  for (int m = LPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
   const float mean = s / (float)D;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (l8 + 8 * i < nch)
+  for (int i = 0; i < CPL; ++i)
+    if (l8 + LPR * i < nch)
 #pragma unroll
       for (int e = 0; e < 8; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
 #pragma unroll
-  for (int m = 4; m > 0; m >>= 1) q += __shfl_xor(q, m, 64);
+  for (int m = LPR / 2; m > 0; m >>= 1) q += __shfl_xor(q, m, 64);
   const float inv = 1.0f / sqrtf(q / (float)D + eps);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = l8 + 8 * i;
+  for (int i = 0; i < CPL; ++i) {
+    const int c = l8 + LPR * i;
     float o[8];
     if (c < nch) {
 #pragma unroll
@@ -164,9 +171,13 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   bf16* cs = xs + TW * XS;           // h, then ctx, then h2
   bf16* x1s = cs + TW * XS;          // x1 rows
   bf16* qkvs = x1s + TW * XS;        // q|k|v rows        [TW][qs]
-  bf16* vts = qkvs + TW * p.qs;      // V^T per head pair [2][64][VTS]
+  bf16* vts = qkvs + TW * p.qs;      // V^T of one round's heads [HPR][64][VTS]
   bf16* uss = qkvs;                  // u rows (after attention) [TW][us]
   float* lnp = reinterpret_cast<float*>(smem + 3 * TW * XS + A_MAX);  // LN1/LN2 g, b [4][DP]
+  float* bqkv = lnp + 4 * DP;          // [3D] biases of q|k|v
+  float* bo_s = bqkv + 3 * DP;         // [D]
+  float* b1_s = bo_s + DP;             // [mlp]
+  float* b2_s = b1_s + 512;            // [D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = p.dim, hd = p.head_dim;
@@ -184,30 +195,39 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
     const float* src = which == 0 ? p.ln1_g : which == 1 ? p.ln1_b : which == 2 ? p.ln2_g : p.ln2_b;
     lnp[which * DP + c] = src[c];
   }
-  WFrags<3, DP / 32> wqkv;
+  // biases, so that no epilogue waits on a global load
+  for (int e = tid; e < 5 * D + p.mlp; e += 64 * NWF) {
+    if (e < 3 * D) {
+      bqkv[e] = e < D ? p.bq[e] : (e < 2 * D ? p.bk[e - D] : p.bv[e - 2 * D]);
+    } else if (e < 4 * D) {
+      bo_s[e - 3 * D] = p.bo[e - 3 * D];
+    } else if (e < 5 * D) {
+      b2_s[e - 4 * D] = p.b2[e - 4 * D];
+    } else {
+      b1_s[e - 5 * D] = p.b1[e - 5 * D];
+    }
+  }
+  WFrags<(3 * DP / 16 + NWF - 1) / NWF, DP / 32> wqkv;
   wqkv.load([&](int n) { return n < D ? p.wq + (int64_t)n * D : (n < 2 * D ? p.wk + (int64_t)(n - D) * D : p.wv + (int64_t)(n - 2 * D) * D); },
             3 * D, D);
   lds_barrier();
   // ---- LN1 -> cs
   ln_rows(xs, cs, lnp, lnp + DP, D, p.eps);
-  WFrags<1, DP / 32> wo;
+  WFrags<(DP / 16 + NWF - 1) / NWF, DP / 32> wo;
   wo.load([&](int n) { return p.wo + (int64_t)n * D; }, D, D);
   lds_barrier();
   // ---- q|k|v = h W^T + b -> qkvs
   wqkv.gemm(cs, XS, 3 * D, D,
-      [&](int m, int n, f32x4 v) {
-        const float* bb = n < D ? p.bq + n : (n < 2 * D ? p.bk + (n - D) : p.bv + (n - 2 * D));
-        store4<bf16>(qkvs + m * p.qs + n, v + *reinterpret_cast<const f32x4*>(bb));
-      });
-  WFrags<4, DP / 32> w1;
+      [&](int m, int n, f32x4 v) { store4<bf16>(qkvs + m * p.qs + n, v + *reinterpret_cast<const f32x4*>(bqkv + n)); });
+  WFrags<(512 / 16 + NWF - 1) / NWF, DP / 32> w1;
   w1.load([&](int n) { return p.w1 + (int64_t)n * D; }, p.mlp, D);
   lds_barrier();
 
-  // ---- attention, two heads per round (waves 0-3: head h0, waves 4-7: h0+1)
+  // ---- attention, HPR heads per round (waves 4j..4j+3: head h0 + j)
   const int fr = lane & 15, g = lane >> 4;
-  for (int h0 = 0; h0 < p.heads; h0 += 2) {
-    // V^T of the two heads: [hl][d][key], zero past head_dim
-    for (int e = tid; e < 2 * TW * 8; e += 64 * NWF) {
+  for (int h0 = 0; h0 < p.heads; h0 += HPR) {
+    // V^T of the round's heads: [hl][d][key], zero past head_dim
+    for (int e = tid; e < HPR * TW * 8; e += 64 * NWF) {
       const int hl = e / (TW * 8), rem = e - hl * TW * 8;
       const int key = rem >> 3, c = rem & 7;
       const int head = h0 + hl;
@@ -291,7 +311,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   // ---- x1 = x + ctx W_o^T + b_o -> x1s (cs columns D..DP-1 are still zero)
   wo.gemm(cs, XS, D, D,
       [&](int m, int n, f32x4 v) {
-        v = v + *reinterpret_cast<const f32x4*>(p.bo + n) + load4<bf16>(xs + m * XS + n);
+        v = v + *reinterpret_cast<const f32x4*>(bo_s + n) + load4<bf16>(xs + m * XS + n);
         store4<bf16>(x1s + m * XS + n, v);
       });
   lds_barrier();
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   // ---- u = GELU(h2 W_1^T + b_1) -> uss
   w1.gemm(cs, XS, p.mlp, D,
       [&](int m, int n, f32x4 v) {
-        v = v + *reinterpret_cast<const f32x4*>(p.b1 + n);
+        v = v + *reinterpret_cast<const f32x4*>(b1_s + n);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = TANH ? gelu_tanh_d(v[e]) : gelu_erf_d(v[e]);
         store4<bf16>(uss + m * p.us + n, v);
@@ -312,7 +332,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   // ---- y = x1 + u W_2^T + b_2 -> global
   w2.gemm(uss, p.us, D, p.mlp,
       [&](int m, int n, f32x4 v) {
-        v = v + *reinterpret_cast<const f32x4*>(p.b2 + n) + load4<bf16>(x1s + m * XS + n);
+        v = v + *reinterpret_cast<const f32x4*>(b2_s + n) + load4<bf16>(x1s + m * XS + n);
         store4<bf16>(p.y + (row0 + (int64_t)m * p.n_windows) * D + n, v);
       });
 }
