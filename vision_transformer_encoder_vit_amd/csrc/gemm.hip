@@ -216,6 +216,22 @@ __device__ __forceinline__ void xcd_tile(int bid, int nwg, int tiles_m, int tile
   tn = in / gm;
 }
 
+// Scheduling hint for one K step of the main loop: alternate the step's
+// MFMAs with the vector-memory loads of the next tile (NV) and the LDS
+// fragment reads of the next K step (ND), so that neither the memory nor the
+// LDS queue backs up behind a burst of issues while the matrix core idles.
+template <int M, int NM, int NV, int ND>
+struct Interleave {
+  __device__ __forceinline__ static void go() {
+    if constexpr (M < NM) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+      if constexpr (M < NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one VMEM
+      if constexpr (M < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      Interleave<M + 1, NM, NV, ND>::go();
+    }
+  }
+};
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(GemmParams<bf16> p) {
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
@@ -249,11 +265,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       src[j] = base + (int64_t)(n - seg * p.seg_cols) * p.K + chunk * 8;
     }
   }
-  auto issue = [&](int kt) {
-    bf16* st = sm + (kt % ST) * STAGE;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_ptr)(st + (wave * LPW + j) * 512), 16, 0, 0);
+  // load j of tile kt (LPW per wave per tile)
+  auto load = [&](int j, int kt) {
+    __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_ptr)(sm + (kt % ST) * STAGE + (wave * LPW + j) * 512),
+                                     16, 0, 0);
   };
 
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -281,7 +296,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   };
 
   const int nk = p.K / BK;
-  issue(0);
+  constexpr int KS = BK / 16;              // MFMA K steps per tile
+  constexpr int LPK = (LPW + 1) / 2;       // next-tile loads per K step, over the first two steps
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) load(j, 0);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of tile kt have landed; after the barrier every
     // wave's have, and every wave is done reading the stage refilled next
@@ -289,19 +307,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 1 < nk) issue(kt + 1);
+    const bool more = kt + 1 < nk;
     const int stage = kt % ST;
     frags(0, stage, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) frags((ks + 1) & 1, stage, ks + 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the next fragment reads ahead of these MFMAs
+    for (int ks = 0; ks < KS; ++ks) {
+      if (more) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j)
+          if (j / LPK == ks) load(j, kt + 1);
+      }
+      if (ks + 1 < KS) frags((ks + 1) & 1, stage, ks + 1);
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ks & 1][i]),
                                                              __builtin_bit_cast(bf16x8, bfr[ks & 1][j]), acc[i][j], 0, 0, 0);
+      if (ks + 1 < KS)
+        Interleave<0, TN * TM, LPK, TN + TM>::go();
+      else
+        Interleave<0, TN * TM, LPK, 0>::go();
       __builtin_amdgcn_sched_barrier(0);
     }
   }
