@@ -30,8 +30,10 @@ def hipcc():
 
 
 # attention keeps its MFMA accumulators in VGPRs: the softmax reads every
-# score element, and AGPR accumulators would cost a copy per element
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# score element, and AGPR accumulators would cost a copy per element. Its
+# scores are finite (masked keys are -1e30), so NaN semantics are dropped:
+# in IEEE mode every max() would first canonicalise both inputs.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src):

@@ -285,22 +285,29 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams<T> p) {
 // ---------------------------------------------------------------------------
 // bf16 kernel for large windows (>= 128 queries): 32x32x16 MFMA.
 //
-// A workgroup of NW waves takes 64*NW queries of one (frame, window, head);
-// each wave owns 64 queries (two 32-row blocks), so every K and V fragment
-// read from LDS feeds two MFMAs. Per 64-key tile: K goes global -> LDS
+// A workgroup of NW waves takes 32*QB*NW queries of one (frame, window,
+// head); each wave owns QB blocks of 32 queries, and every K and V fragment
+// read from LDS feeds QB MFMAs. Per 64-key tile: K goes global -> LDS
 // directly (global_load_lds, XOR-swizzled rows), V goes through registers
 // and is written transposed ([d][key]); both are double-buffered and the
 // next tile is fetched while this one is multiplied.
 //   S^T = K Q^T    lane (q = l%32, h = l/32) receives the 16 keys
 //                  32kb + 8(r/4) + 4h + r%4 of query q (r = register)
-//   softmax        row max = in-lane max + one xor-32 shuffle; exponentials
-//                  exp2(s*c - m*c) with c = scale*log2(e); the rescale of
-//                  the output is skipped when no row max moved
+//   softmax        row max = in-lane max + one swap of the wave halves
+//                  (permlane32); exponentials exp2(s*c - m*c) with
+//                  c = scale*log2(e); the output is rescaled every tile
+//                  (a branch around it costs more in register copies)
 //   O^T += V^T P^T registers 8s..8s+7 of a 32-key block are exactly the
 //                  8 keys one lane supplies for MFMA k-step s, so P goes to
 //                  the MFMA without any data movement; V^T supplies the same
 //                  keys from two 8-byte LDS reads
 // ---------------------------------------------------------------------------
+
+// max of x over lanes l and l ^ 32 (the two halves of the wave)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 __host__ __device__ constexpr int attn_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 __device__ __forceinline__ int kswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -521,7 +528,6 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
             if (kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= kv_left) sacc[qb][kb][r] = -1e30f;
     }
     u32x4 pf[QB][2][2];  // [qb][kb][s]: bf16 P for MFMA k-step s of key block kb
-    bool moved = false;
     float alpha[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -530,9 +536,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[qb], mx);
-      moved |= m_new > m_run[qb];
+      const float m_new = fmaxf(m_run[qb], halves_max(mx));
       alpha[qb] = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
       m_run[qb] = m_new;
       const float mc = m_new * c;
@@ -553,12 +557,10 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
       }
       l_part[qb] = l_part[qb] * alpha[qb] + ls;
     }
-    if (__any(moved)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) acc_o[qb][db] = acc_o[qb][db] * alpha[qb];
-    }
+      for (int db = 0; db < 2; ++db) acc_o[qb][db] = acc_o[qb][db] * alpha[qb];
     // O^T += V^T P^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
