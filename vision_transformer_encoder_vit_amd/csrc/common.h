@@ -114,6 +114,16 @@ __device__ __forceinline__ float gelu_erf_as(float v) {
   return 0.5f * v * (1.0f + copysignf(erf_z, v));
 }
 
+// tanh-approximated GELU, 0.5 v (1 + tanh(u)) with u = sqrt(2/pi)(v + 0.044715 v^3),
+// written through 1 + tanh(u) = 2 / (1 + e^(-2u)): v / (1 + 2^(-2u log2 e)).
+// One exp2 and one reciprocal (hardware, ~1 ulp each); saturates to v and -0
+// for large |u| without overflow trouble (2^+inf -> inf -> reciprocal 0).
+__device__ __forceinline__ float gelu_tanh_fast(float v) {
+  const float u = 0.79788456080286536f * __builtin_fmaf(0.044715f * v, v * v, v);
+  const float e = __builtin_amdgcn_exp2f(u * -2.8853900817779268f);  // 2 log2(e)
+  return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -54,9 +54,7 @@ struct FusedParams {
 };
 
 __device__ __forceinline__ float gelu_erf_d(float v) { return gelu_erf_as(v); }
-__device__ __forceinline__ float gelu_tanh_d(float v) {
-  return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
-}
+__device__ __forceinline__ float gelu_tanh_d(float v) { return gelu_tanh_fast(v); }
 
 // Row LayerNorm of the window's 64 rows (src -> dst, both LDS, stride XS),
 // 8 lanes per row; columns D..DP-1 of dst are written as zeros so that dst

@@ -41,9 +41,7 @@ struct GemmParams {
 };
 
 __device__ __forceinline__ float gelu_erf_f(float v) { return gelu_erf_as(v); }
-__device__ __forceinline__ float gelu_tanh_f(float v) {
-  return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
-}
+__device__ __forceinline__ float gelu_tanh_f(float v) { return gelu_tanh_fast(v); }
 
 template <typename T, int BM, int BN, int WTM, int WTN, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
