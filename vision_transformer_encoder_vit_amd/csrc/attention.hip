@@ -49,6 +49,7 @@ struct AttnParams {
   int mode, n_windows, grid_w, win_h, win_w;
   int n_q, n_kv, q_tiles, head_groups, windows;
   float scale_log2;
+  const T* vt;  // V transposed [B, heads, head_dim, tokens_in] (large-window kernel)
 };
 
 __device__ __forceinline__ int window_token(int mode, int w, int i, int n_windows, int grid_w, int win_h,
@@ -287,20 +288,23 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams<T> p) {
 //
 // A workgroup of NW waves takes 32*QB*NW queries of one (frame, window,
 // head); each wave owns QB blocks of 32 queries, and every K and V fragment
-// read from LDS feeds QB MFMAs. Per 64-key tile: K goes global -> LDS
-// directly (global_load_lds, XOR-swizzled rows), V goes through registers
-// and is written transposed ([d][key]); both are double-buffered and the
-// next tile is fetched while this one is multiplied.
-//   S^T = K Q^T    lane (q = l%32, h = l/32) receives the 16 keys
-//                  32kb + 8(r/4) + 4h + r%4 of query q (r = register)
+// read from LDS feeds QB MFMAs. Per 64-key tile, K rows ([key][d]) and V^T
+// rows ([d][key], written transposed by the qkv projection) go global ->
+// LDS directly (global_load_lds, XOR-swizzled 16-byte chunks), double
+// buffered: the next tile is in flight while this one is multiplied.
+//   S^T = K Q^T    lane (q = l%32, h = l/32) receives S^T rows
+//                  R = 32kb + 8(r/4) + 4h + r%4 (r = register)
+//   key order      LDS row R of the K tile holds key pi(R), pi swapping bits
+//                  2 and 3 of R; then registers 8s..8s+7 of lane half h are
+//                  keys 32kb + 16s + 8h + 0..7, i.e. 8 consecutive keys
 //   softmax        row max = in-lane max + one swap of the wave halves
 //                  (permlane32); exponentials exp2(s*c - m*c) with
 //                  c = scale*log2(e); the output is rescaled every tile
 //                  (a branch around it costs more in register copies)
-//   O^T += V^T P^T registers 8s..8s+7 of a 32-key block are exactly the
-//                  8 keys one lane supplies for MFMA k-step s, so P goes to
-//                  the MFMA without any data movement; V^T supplies the same
-//                  keys from two 8-byte LDS reads
+//   O^T += V^T P^T P goes to the MFMA as the B operand straight from the
+//                  softmax registers; its k-slots 8h..8h+7 are the 8
+//                  consecutive keys above, so the V^T operand is one
+//                  16-byte LDS chunk of row d
 // ---------------------------------------------------------------------------
 
 // max of x over lanes l and l ^ 32 (the two halves of the wave)
@@ -311,6 +315,8 @@ __device__ __forceinline__ float halves_max(float x) {
 
 __host__ __device__ constexpr int attn_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 __device__ __forceinline__ int kswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// key held by LDS row R of a K tile: R with bits 2 and 3 swapped (an involution)
+__device__ __forceinline__ int key_of_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 typedef __attribute__((address_space(3))) void* attn_lds_ptr;
 
 // Token index of in-window position i, kept as (x, y) in the window and
@@ -334,12 +340,10 @@ struct WinCursor {
 
 template <int NW, int QB, int MODE, bool POOL>
 __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf16> p) {
-  constexpr int NT = 64 * NW;
-  constexpr int QW = 32 * QB;       // queries per wave
-  constexpr int VROW2 = KT + 4;     // V^T row stride (elements): 136 B, conflict-free 8-byte reads
+  constexpr int QW = 32 * QB;  // queries per wave
   static_assert(MODE == ATTN_GLOBAL || MODE == ATTN_SPATIAL, "large-window kernel");
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][KT * 64];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][64 * VROW2];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][64 * KT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, h = lane >> 5;
@@ -364,6 +368,8 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
     gw = p.grid_w;
   }
   const bf16* base = p.qkv + (int64_t)b * p.tokens_in * ld;
+  // V^T rows of this (frame, head): row d holds V[token][d] over the frame's tokens
+  const bf16* vt_base = p.vt + ((int64_t)b * p.heads + head) * hd * p.tokens_in;
   auto tok = [&](const WinCursor& cur) { return MODE == ATTN_SPATIAL ? origin + cur.y * gw + cur.x : cur.x; };
   // per-tile cursor step: KT positions = dy rows + dx columns of the window
   const int step_dy = MODE == ATTN_SPATIAL ? KT / ww : 0;
@@ -403,75 +409,54 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
     }
   }
 
-  // ---- K: direct to LDS. Wave instruction j covers key rows 8j .. 8j+7.
-  constexpr int KLOADS = KT / 8 / NW;
-  static_assert(KT % (8 * NW) == 0, "key rows must split over the waves");
-  WinCursor kcur[KLOADS];
-  int kchunk[KLOADS];
-#pragma unroll
-  for (int j = 0; j < KLOADS; ++j) {
-    const int row = (wave * KLOADS + j) * 8 + lane / 8;
-    kcur[j].init(row, wwx);
-    // chunks past head_dim read neighbouring finite values (Q is zero there)
-    kchunk[j] = min(((lane & 7) ^ kswz(row)) * 8, 2 * D - head * hd - 8) + D + head * hd;
-  }
+  // ---- K tile: wave instruction j fills LDS rows 8j .. 8j+7 (16 bytes per
+  // lane); LDS row R holds key pi(R) of the tile.
+  constexpr int LOADS = KT / 8 / NW;
+  static_assert(KT % (8 * NW) == 0, "tile rows must split over the waves");
   const int last_kv = p.n_kv - 1;
   WinCursor last_cur;
   last_cur.init(last_kv, wwx);
-  auto issue_k = [&](int kt) {
+  WinCursor kcur[LOADS];
+  int kchunk[LOADS], kkey[LOADS];
 #pragma unroll
-    for (int j = 0; j < KLOADS; ++j) {
-      const int row = (wave * KLOADS + j) * 8 + lane / 8;
+  for (int j = 0; j < LOADS; ++j) {
+    const int row = (wave * LOADS + j) * 8 + lane / 8;
+    kkey[j] = key_of_row(row);
+    kcur[j].init(kkey[j], wwx);
+    // chunks past head_dim read neighbouring finite values (Q is zero there)
+    kchunk[j] = min(((lane & 7) ^ kswz(row)) * 8, 2 * D - head * hd - 8) + D + head * hd;
+  }
+  // ---- V^T tile: LDS row d = V^T row min(d, hd - 1) (rows past head_dim
+  // only feed output rows that are never stored); 16-byte chunk c of a row
+  // is keys 8c .. 8c+7 of the tile, which are consecutive tokens (the window
+  // width is a multiple of 8). Chunks past the window repeat its last chunk
+  // (finite values under P = 0).
+  WinCursor vcur[LOADS];
+  int vrow_off[LOADS], vpos[LOADS];
+  WinCursor vlast;
+  vlast.init(p.n_kv - 8, wwx);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int row = (wave * LOADS + j) * 8 + lane / 8;
+    vpos[j] = ((lane & 7) ^ kswz(row)) * 8;
+    vcur[j].init(vpos[j], wwx);
+    vrow_off[j] = min(row, hd - 1) * p.tokens_in;
+  }
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
       // keys past the window read the last key (masked out of the softmax)
-      const int t = kt * KT + row <= last_kv ? tok(kcur[j]) : tok(last_cur);
+      const int t = kt * KT + kkey[j] <= last_kv ? tok(kcur[j]) : tok(last_cur);
       __builtin_amdgcn_global_load_lds((const void*)(base + t * ld + kchunk[j]),
-                                       (attn_lds_ptr)(&Ks[kt & 1][(wave * KLOADS + j) * 512]), 16, 0, 0);
+                                       (attn_lds_ptr)(&Ks[kt & 1][(wave * LOADS + j) * 512]), 16, 0, 0);
       kcur[j].step(step_dx, step_dy, wwx);
     }
-  };
-  // ---- V: through registers, written transposed as packed key pairs.
-  // Work unit u -> (key pair jp = u % 32, 16-byte chunk c): lanes 0-31 and
-  // 32-63 of a wave take chunks two apart, so each ds_write_b32 of a wave
-  // (one d row per chunk, 32 consecutive key pairs) covers all 64 banks.
-  constexpr int VUNITS = 32 * 8 / NT;
-  static_assert(32 * 8 % NT == 0, "V units must split over the threads");
-  u32x4 vreg[VUNITS][2];
-  WinCursor vcur[VUNITS][2];
-  int vcol[VUNITS], vjp[VUNITS];
-  bool vok[VUNITS];
 #pragma unroll
-  for (int it = 0; it < VUNITS; ++it) {
-    const int u = tid + NT * it;
-    const int w = u >> 6, half = (u >> 5) & 1;
-    const int c = (w & 1) + ((w >> 1) << 2) + 2 * half;  // wave slots -> chunks {0,2},{1,3},{4,6},{5,7}
-    vjp[it] = u & 31;
-    vok[it] = c * 8 < hd;
-    vcol[it] = c * 8;
-    vcur[it][0].init(2 * vjp[it], wwx);
-    vcur[it][1].init(2 * vjp[it] + 1, wwx);
-  }
-  auto load_v = [&](int kt) {
-#pragma unroll
-    for (int it = 0; it < VUNITS; ++it)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int kv = kt * KT + 2 * vjp[it] + e;
-        vreg[it][e] = (kv <= last_kv && vok[it]) ? ld16(base + tok(vcur[it][e]) * ld + 2 * D + head * hd + vcol[it])
-                                                  : u32x4{0, 0, 0, 0};
-        vcur[it][e].step(step_dx, step_dy, wwx);
-      }
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < VUNITS; ++it) {
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, vreg[it][0]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, vreg[it][1]);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const bf16 pr[2] = {a0[k], a1[k]};
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(vcol[it] + k) * VROW2 + 2 * vjp[it]]) =
-            *reinterpret_cast<const uint32_t*>(pr);
-      }
+    for (int j = 0; j < LOADS; ++j) {
+      const int t = kt * KT + vpos[j] <= p.n_kv - 8 ? tok(vcur[j]) : tok(vlast);
+      __builtin_amdgcn_global_load_lds((const void*)(vt_base + vrow_off[j] + t),
+                                       (attn_lds_ptr)(&Vs[kt & 1][(wave * LOADS + j) * 512]), 16, 0, 0);
+      vcur[j].step(step_dx, step_dy, wwx);
     }
   };
 
@@ -489,17 +474,14 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   const float c = p.scale_log2;
 
   const int ntiles = (p.n_kv + KT - 1) / KT;
-  issue_k(0);
-  load_v(0);
+  issue(0);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int buf = kt & 1;
+    // this wave's loads of tile kt have landed; after the barrier every
+    // wave's have, and every wave is done with the buffer refilled next
     __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
-    store_v(buf);
     __syncthreads();
-    if (kt + 1 < ntiles) {
-      issue_k(kt + 1);
-      load_v(kt + 1);
-    }
+    if (kt + 1 < ntiles) issue(kt + 1);
     f32x16 sacc[QB][2];  // [qb][kb]
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -525,7 +507,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= kv_left) sacc[qb][kb][r] = -1e30f;
+            if (key_of_row(kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) >= kv_left) sacc[qb][kb][r] = -1e30f;
     }
     u32x4 pf[QB][2][2];  // [qb][kb][s]: bf16 P for MFMA k-step s of key block kb
     float alpha[QB];
@@ -561,17 +543,15 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int db = 0; db < 2; ++db) acc_o[qb][db] = acc_o[qb][db] * alpha[qb];
-    // O^T += V^T P^T
+    // O^T += V^T P^T: k-step s of key block kb covers keys 32kb + 16s + 8h + 0..7
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const bf16* vrow = &Vt[buf][(db * 32 + fr) * VROW2 + kb * 32 + s * 16 + 4 * h];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          const int row = db * 32 + fr;
+          const u32x4 vf = ld16(&Vs[buf][row * 64 + ((4 * kb + 2 * s + h) ^ kswz(row)) * 8]);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
@@ -597,7 +577,6 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
       }
   }
 }
-
 template <int NW, int QB, int MODE, bool POOL>
 static hipError_t attn32_go(AttnParams<bf16> p, int batch, hipStream_t s, StageEvents ev) {
   p.q_tiles = (p.n_q + 32 * QB * NW - 1) / (32 * QB * NW);
@@ -651,11 +630,14 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
     p.n_kv = a.tokens_in;
   }
   const bool pool = a.q_stride == 4;
-  if constexpr (std::is_same<T, bf16>::value) {
-    // large global or spatial windows: 32x32 MFMA kernel (32-bit element
-    // offsets into the qkv buffer)
-    const int64_t qkv_elems = (int64_t)a.batch * a.tokens_in * a.ld_qkv;
-    if (p.n_q >= 128 && a.head_dim <= 64 && a.mode != ATTN_MASK_UNIT && qkv_elems < (1LL << 31)) {
+  p.vt = (const T*)a.vt;
+  if (a.vt) {
+    // large global or spatial windows: 32x32 MFMA kernel on K and V^T
+    if (!std::is_same<T, bf16>::value ||
+        !attention_takes_vt(DType::BF16, a.mode, p.n_q, a.head_dim, a.win_w, a.tokens_in,
+                            (int64_t)a.batch * a.tokens_in * a.ld_qkv))
+      return hipErrorInvalidValue;
+    if constexpr (std::is_same<T, bf16>::value) {
       if (a.mode == ATTN_SPATIAL)
         return attn32_go<ATTN_NW, ATTN_QB, ATTN_SPATIAL, false>(p, a.batch, s, ev);
       return pool ? attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, true>(p, a.batch, s, ev)

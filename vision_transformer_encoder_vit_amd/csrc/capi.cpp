@@ -54,8 +54,9 @@ struct vit_block_plan {
   int64_t m_in, m_out;
   size_t esize;
   // workspace layout (byte offsets)
-  size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, ws_bytes;
+  size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, off_vt, ws_bytes;
   bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
+  bool attn_vt;          // qkv projection also writes V^T for the large-window attention kernel
 };
 
 static vit_status validate_desc(const vit_block_desc* d) {
@@ -141,6 +142,12 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   p->off_x1 = take(p->m_out, d.dim_out);
   p->off_h2 = take(p->m_out, d.dim_out);
   p->off_u = take(p->m_out, d.mlp_hidden);
+  const int64_t n_q = d.attn_mode == VIT_ATTN_SPATIAL ? (int64_t)d.win_h * d.win_w : p->n_out;
+  p->attn_vt = vit::attention_takes_vt(d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32,
+                                       d.attn_mode, n_q, p->head_dim, d.win_w, p->n_in,
+                                       p->m_in * 3LL * d.dim_out) &&
+               d.dim_in % 64 == 0;  // the qkv projection on the MFMA path writes V^T
+  p->off_vt = p->attn_vt ? take(p->m_in, d.dim_out) : 0;
   p->ws_bytes = o;
   p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 && d.attn_mode == VIT_ATTN_MASK_UNIT && d.q_stride == 1 &&
                        d.rope == VIT_ROPE_NONE &&
@@ -360,6 +367,14 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   } else {
     g.epi = vit::EPI_BIAS;
   }
+  if (P.attn_vt) {
+    g.vt = base + P.off_vt;
+    g.vt_col0 = 2 * Do;
+    g.vt_tokens = P.n_in;
+    g.vt_heads = d.heads;
+    g.vt_hd = hd;
+    g.vt_only = !seams;  // the qkv seam keeps V in row layout too
+  }
   e = vit::launch_gemm(g, dt, s, stage_ev(VIT_STAGE_QKV));
   if ((st = device_status(e, "gemm (qkv)")) != VIT_OK) return st;
 
@@ -403,6 +418,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   vit::AttnArgs a;
   a.qkv = qkv;
   a.ld_qkv = 3 * Do;
+  a.vt = P.attn_vt ? base + P.off_vt : nullptr;
   a.ctx = ctx;
   a.ld_ctx = Do;
   a.batch = d.batch;

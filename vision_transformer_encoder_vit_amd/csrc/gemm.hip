@@ -38,6 +38,9 @@ struct GemmParams {
   int64_t ldbranch;
   const float* rope;
   int rope_cols, head_dim, rope_mode, tokens_per_frame, grid_w, win_h, win_w;
+  T* vt;  // transposed copy of columns >= vt_col0 (MFMA path only)
+  int vt_col0, vt_tokens, vt_heads, vt_hd;
+  bool vt_only;
 };
 
 __device__ __forceinline__ float gelu_erf_f(float v) { return gelu_erf_as(v); }
@@ -359,10 +362,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       }
     }
     __syncthreads();
+    if ((EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) && p.vt != nullptr && n0 + BN > p.vt_col0) {
+      // transposed copy of the V columns: one column x 8 consecutive token
+      // rows per thread (a 16-byte run of one V^T row); rows are within one
+      // frame since vt_tokens % 8 == 0
+      for (int e = tid; e < (PR / 8) * BN; e += NT) {
+        const int cc = e % BN, rg = e / BN;
+        const int m = m0 + pass * PR + rg * 8, n = n0 + cc;
+        if (m >= p.M || n >= p.N || n < p.vt_col0) continue;
+        const int seg = n / p.seg_cols;
+        const float bn = (seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2))[n - seg * p.seg_cols];
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = cs[(rg * 8 + k) * CROW + cc] + bn;
+        const int vv = n - p.vt_col0, hh = vv / p.vt_hd, d = vv - hh * p.vt_hd;
+        const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
+        st16(p.vt + (((int64_t)fb * p.vt_heads + hh) * p.vt_hd + d) * p.vt_tokens + t, pack16<bf16>(v));
+      }
+    }
     for (int e = tid; e < PR * G8; e += NT) {
       const int r = e / G8, c8 = (e - r * G8) * 8;
       const int m = m0 + pass * PR + r, n = n0 + c8;
       if (m >= p.M || n >= p.N) continue;
+      if (p.vt_only && n >= p.vt_col0) continue;
       float v[8];
       *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8);
       *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4);
@@ -454,6 +476,12 @@ static GemmParams<T> make_params(const GemmArgs& a) {
   p.grid_w = a.grid_w;
   p.win_h = a.win_h;
   p.win_w = a.win_w;
+  p.vt = (T*)a.vt;
+  p.vt_col0 = a.vt ? a.vt_col0 : a.N;
+  p.vt_tokens = a.vt_tokens;
+  p.vt_heads = a.vt_heads;
+  p.vt_hd = a.vt_hd;
+  p.vt_only = a.vt != nullptr && a.vt_only;
   return p;
 }
 
@@ -475,8 +503,12 @@ static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  const bool mfma32 = dt == DType::BF16 && a.K % 64 == 0 && a.lda % 8 == 0;
+  if (a.vt && (!mfma32 || (a.epi != EPI_BIAS && a.epi != EPI_BIAS_ROPE) || a.M % 8 || a.vt_tokens <= 0 ||
+               a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 || (a.N - a.vt_col0) != a.vt_heads * a.vt_hd))
+    return hipErrorInvalidValue;
   if (dt == DType::F32) return gemm_go<float, 64, 64, 2, 2>(a, s, ev);
-  if (a.K % 64 == 0 && a.lda % 8 == 0) {
+  if (mfma32) {
     // one full wave of 256x256 tiles fills the 256 CUs; otherwise 128x128
     // tiles (two workgroups per CU) balance better
     const GemmParams<bf16> p = make_params<bf16>(a);

@@ -46,6 +46,13 @@ struct GemmArgs {
   const float* rope = nullptr;
   int rope_cols = 0, head_dim = 0, rope_mode = 0;
   int tokens_per_frame = 1, grid_w = 1, win_h = 1, win_w = 1;
+  // EPI_BIAS / EPI_BIAS_ROPE: columns >= vt_col0 (V, bias only) are also
+  // written transposed to vt [M / vt_tokens, vt_heads, vt_hd, vt_tokens];
+  // with vt_only they are not written to C. Needs the bf16 MFMA path
+  // (K % 64 == 0), M and vt_tokens multiples of 8, vt_col0 a multiple of 8.
+  void* vt = nullptr;
+  int vt_col0 = 0, vt_tokens = 0, vt_heads = 0, vt_hd = 0;
+  bool vt_only = false;
 };
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 
@@ -53,6 +60,9 @@ enum AttnMode { ATTN_GLOBAL = 0, ATTN_MASK_UNIT = 1, ATTN_SPATIAL = 2 };
 
 struct AttnArgs {
   const void* qkv = nullptr;  // [B * tokens_in, 3 * dim], rows [q | k | v]
+  // V transposed, [B, heads, head_dim, tokens_in]: given exactly when
+  // attention_takes_vt() holds, and then read in place of qkv's V columns
+  const void* vt = nullptr;
   int64_t ld_qkv = 0;
   void* ctx = nullptr;        // [B * tokens_out, dim]
   int64_t ld_ctx = 0;
@@ -62,6 +72,17 @@ struct AttnArgs {
   float scale = 1.f;
 };
 hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
+
+// Large global or spatial windows go to the 32x32-MFMA attention kernel,
+// which streams K and V^T tiles straight into LDS: bf16, >= 128 queries per
+// window, head_dim <= 64, frame token count and (spatial) window width
+// multiples of 8 (16-byte runs of consecutive keys in V^T), 32-bit element
+// offsets into qkv.
+inline bool attention_takes_vt(DType dt, int mode, int64_t n_q, int head_dim, int win_w, int64_t tokens_in,
+                               int64_t qkv_elems) {
+  return dt == DType::BF16 && (mode == ATTN_GLOBAL || (mode == ATTN_SPATIAL && win_w % 8 == 0)) && n_q >= 128 &&
+         head_dim <= 64 && tokens_in % 8 == 0 && qkv_elems < (1LL << 31);
+}
 
 // Whole block for 64-token mask units of width <= 128 in one kernel
 // (q_stride 1): x [B*tokens, dim] -> y, one workgroup per (frame, window).
