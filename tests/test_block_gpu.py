@@ -53,11 +53,20 @@ def _sample_rows(n, count, seed):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", list(C))
+# Large shapes beside the benchmark's: ragged token counts through the
+# 128x192 / 192x128 GEMM tiles (8000 rows; a 4712-wide MLP), the V^T attention
+# path with a ragged last key tile (1000 keys), and K % 64 != 0 at full size.
+LARGE = {
+    "c4_b8_25x40": d(C["c4_siglip_b8"], grid_h=25, grid_w=40),
+    "c5w_mlp4712": d(C["c5w_sam3_win"], mlp=4712),
+}
+
+
+@pytest.mark.parametrize("name", list(C) + list(LARGE))
 def test_block_parity_full_size_sampled_rows(name):
     # the configuration the benchmark times, at full size; the oracle
     # evaluates every frame at sampled output rows
-    spec = C[name]
+    spec = C[name] if name in C else LARGE[name]
     print("case", name, flush=True)
     inp = synth.make_inputs(spec, seed=0)
     y, seams = gu.run_block(spec, gu.to_device(inp, spec))
@@ -120,12 +129,18 @@ def test_rerun_is_bitwise_identical():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-def test_forward_equals_forward_seams():
-    spec = SMALL["c5g_18x22"]
-    dev = gu.to_device(synth.make_inputs(spec, seed=0), spec)
+@pytest.mark.parametrize("name", ["c5g_18x22", "c5w_48x48", "c3b_12x12"])
+def test_forward_equals_forward_seams(name):
+    # c5w_48x48 and c3b_12x12 take the V^T attention path, where the plain
+    # forward skips qkv's row-layout V and the seams forward writes both
+    spec = SMALL[name]
+    print("case", name, flush=True)
+    inp = synth.make_inputs(spec, seed=0)
+    dev = gu.to_device(inp, spec)
     y1, _ = gu.run_block(spec, dev, seams=False)
     y2, _ = gu.run_block(spec, dev, seams=True)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    gu.check(name + ":y (forward)", gu.to64(y1), ob.block_forward(inp["x"], inp, spec)["y"], spec)
 
 
 def test_batched_frame_equals_single_frame():

@@ -509,11 +509,18 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
     return hipErrorInvalidValue;
   if (dt == DType::F32) return gemm_go<float, 64, 64, 2, 2>(a, s, ev);
   if (mfma32) {
-    // one full wave of 256x256 tiles fills the 256 CUs; otherwise 128x128
-    // tiles (two workgroups per CU) balance better
+    // One full wave of 256x256 tiles fills the 256 CUs. Otherwise two
+    // workgroups per CU: 128x128 tiles, or for large products (>= 2e10 FLOP)
+    // 128x192 / 192x128 tiles where 192 divides N / M exactly (fewer, larger
+    // tiles with no ragged edge; 3-8 % faster on the SigLIP and SAM3 MLP and
+    // qkv shapes, slower on the small projections)
     const GemmParams<bf16> p = make_params<bf16>(a);
     const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (t256 >= 224 && t256 <= 256) return gemm32_go<256, 256, 2, 4>(p, a.epi, s, ev);
+    if (2.0 * a.M * a.N * a.K >= 2e10) {
+      if (a.N % 192 == 0) return gemm32_go<128, 192, 2, 2>(p, a.epi, s, ev);
+      if (a.M % 192 == 0) return gemm32_go<192, 128, 2, 2>(p, a.epi, s, ev);
+    }
     return gemm32_go<128, 128, 2, 2>(p, a.epi, s, ev);
   }
   const int64_t big_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
