@@ -521,6 +521,10 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
       if (a.N % 192 == 0) return gemm32_go<128, 192, 2, 2>(p, a.epi, s, ev);
       if (a.M % 192 == 0) return gemm32_go<192, 128, 2, 2>(p, a.epi, s, ev);
     }
+    // small products (e.g. 1024 tokens x 448 columns): 128x128 tiles would
+    // leave most CUs idle, so 64x64 tiles (one 32x32 block per wave)
+    const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+    if (t128 < 192) return gemm32_go<64, 64, 2, 2>(p, a.epi, s, ev);
     return gemm32_go<128, 128, 2, 2>(p, a.epi, s, ev);
   }
   const int64_t big_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
