@@ -37,6 +37,7 @@ constexpr int KT = 64;   // keys per tile
 #define ATTN_QB 1
 #endif
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int HDP = 64;  // padded head dim
 
 template <typename T>
@@ -50,6 +51,12 @@ struct AttnParams {
   int n_q, n_kv, q_tiles, head_groups, windows;
   float scale_log2;
   const T* vt;  // V transposed [B, heads, head_dim, tokens_in] (large-window kernel)
+  // key-split partials (splits > 1): unnormalised O [split][B*tokens_out][dim]
+  // and (row max, row sum) [split][B*tokens_out][heads][2], fp32
+  int splits;
+  int64_t batch_rows;  // B * tokens_out
+  float* part_o;
+  float* part_ml;
 };
 
 __device__ __forceinline__ int window_token(int mode, int w, int i, int n_windows, int grid_w, int win_h,
@@ -348,6 +355,8 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, h = lane >> 5;
   int bid = blockIdx.x;
+  const int split = bid % p.splits;  // key split: tiles [t0, t1) of the window
+  bid /= p.splits;
   const int head = bid % p.heads;
   bid /= p.heads;
   const int qt = bid % p.q_tiles;
@@ -356,6 +365,9 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   const int b = bid / p.windows;
   const int hd = p.head_dim, D = p.dim;
   const int ld = (int)p.ld_qkv;
+  const int ntiles = (p.n_kv + KT - 1) / KT;
+  const int per = (ntiles + p.splits - 1) / p.splits;
+  const int t0 = split * per, t1 = min(ntiles, t0 + per);
   // element offset of this frame + window origin in qkv (fits 32 bits: the
   // host checks the buffer size); token (x, y) of the window is at
   // base + (y * grid_w + x) * ld
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   for (int j = 0; j < LOADS; ++j) {
     const int row = (wave * LOADS + j) * 8 + lane / 8;
     kkey[j] = key_of_row(row);
-    kcur[j].init(kkey[j], wwx);
+    kcur[j].init(t0 * KT + kkey[j], wwx);
     // chunks past head_dim read neighbouring finite values (Q is zero there)
     kchunk[j] = min(((lane & 7) ^ kswz(row)) * 8, 2 * D - head * hd - 8) + D + head * hd;
   }
@@ -439,7 +451,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   for (int j = 0; j < LOADS; ++j) {
     const int row = (wave * LOADS + j) * 8 + lane / 8;
     vpos[j] = ((lane & 7) ^ kswz(row)) * 8;
-    vcur[j].init(vpos[j], wwx);
+    vcur[j].init(t0 * KT + vpos[j], wwx);
     vrow_off[j] = min(row, hd - 1) * p.tokens_in;
   }
   auto issue = [&](int kt) {
@@ -473,15 +485,14 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   }
   const float c = p.scale_log2;
 
-  const int ntiles = (p.n_kv + KT - 1) / KT;
-  issue(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  if (t0 < t1) issue(t0);
+  for (int kt = t0; kt < t1; ++kt) {
     const int buf = kt & 1;
     // this wave's loads of tile kt have landed; after the barrier every
     // wave's have, and every wave is done with the buffer refilled next
     __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
     __syncthreads();
-    if (kt + 1 < ntiles) issue(kt + 1);
+    if (kt + 1 < t1) issue(kt + 1);
     f32x16 sacc[QB][2];  // [qb][kb]
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -564,6 +575,22 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   for (int qb = 0; qb < QB; ++qb) {
     float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
     if (qrow_out[qb] < 0) continue;
+    if (p.splits > 1) {
+      // partial over this split's keys: unnormalised O, row max and row sum
+      const int64_t prow = (int64_t)split * p.batch_rows + (int64_t)b * p.tokens_out + qrow_out[qb];
+      float* po = p.part_o + prow * D + head * hd;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = db * 32 + 8 * gq + 4 * h;
+          if (d < hd)
+            *reinterpret_cast<f32x4*>(po + d) = f32x4{acc_o[qb][db][4 * gq], acc_o[qb][db][4 * gq + 1],
+                                                      acc_o[qb][db][4 * gq + 2], acc_o[qb][db][4 * gq + 3]};
+        }
+      if (h == 0) *reinterpret_cast<f32x2*>(p.part_ml + (prow * p.heads + head) * 2) = f32x2{m_run[qb], l};
+      continue;
+    }
     const float inv = 1.0f / l;
     bf16* out = p.ctx + ((int64_t)b * p.tokens_out + qrow_out[qb]) * p.ld_ctx + head * hd;
 #pragma unroll
@@ -577,13 +604,46 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
       }
   }
 }
+// Key-split partials -> ctx: for each (row, head), weights 2^((m_s - m) c)
+// with m the largest split max; ctx = sum_s w_s O_s / sum_s w_s l_s.
+// One thread per 4 consecutive d of one (row, head).
+__global__ __launch_bounds__(256) void attention_combine_kernel(const float* __restrict__ part_o,
+                                                                const float* __restrict__ part_ml, bf16* ctx,
+                                                                int64_t ld_ctx, int64_t rows, int heads, int hd,
+                                                                int dim, int splits, float c) {
+  const int q4 = hd / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = idx / (heads * q4);
+  if (r >= rows) return;
+  const int rem = (int)(idx - r * heads * q4), head = rem / q4, d = (rem - head * q4) * 4;
+  float m = -1e30f;
+  for (int sp = 0; sp < splits; ++sp) m = fmaxf(m, part_ml[((sp * rows + r) * heads + head) * 2]);
+  float l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < splits; ++sp) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(part_ml + ((sp * rows + r) * heads + head) * 2);
+    const float w = __builtin_amdgcn_exp2f((ml[0] - m) * c);
+    l += w * ml[1];
+    o += w * *reinterpret_cast<const f32x4*>(part_o + (sp * rows + r) * dim + head * hd + d);
+  }
+  store4<bf16>(ctx + r * ld_ctx + head * hd + d, o * (1.0f / l));
+}
+
 template <int NW, int QB, int MODE, bool POOL>
 static hipError_t attn32_go(AttnParams<bf16> p, int batch, hipStream_t s, StageEvents ev) {
   p.q_tiles = (p.n_q + 32 * QB * NW - 1) / (32 * QB * NW);
   const int64_t blocks = (int64_t)batch * p.windows * p.q_tiles * p.heads;
   if (blocks == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((attention_mfma32_kernel<NW, QB, MODE, POOL>), dim3((unsigned)blocks), dim3(64 * NW), 0, s,
-                        ev.start, ev.stop, 0, p);
+  p.batch_rows = (int64_t)batch * p.tokens_out;
+  const hipEvent_t stop = p.splits > 1 ? nullptr : ev.stop;
+  hipExtLaunchKernelGGL((attention_mfma32_kernel<NW, QB, MODE, POOL>), dim3((unsigned)(blocks * p.splits)),
+                        dim3(64 * NW), 0, s, ev.start, stop, 0, p);
+  if (p.splits > 1) {
+    const int64_t threads = p.batch_rows * p.heads * (p.head_dim / 4);
+    hipExtLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                          nullptr, ev.stop, 0, (const float*)p.part_o, (const float*)p.part_ml, p.ctx, p.ld_ctx,
+                          p.batch_rows, p.heads, p.head_dim, p.dim, p.splits, p.scale_log2);
+  }
   return hipGetLastError();
 }
 
@@ -631,7 +691,13 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
   }
   const bool pool = a.q_stride == 4;
   p.vt = (const T*)a.vt;
+  p.splits = 1;
+  p.batch_rows = 0;
+  p.part_o = a.part_o;
+  p.part_ml = a.part_ml;
   if (a.vt) {
+    p.splits = attention_splits(a.batch, p.windows, p.n_q, p.n_kv, a.heads);
+    if (p.splits > 1 && (!a.part_o || !a.part_ml || a.head_dim % 4)) return hipErrorInvalidValue;
     // large global or spatial windows: 32x32 MFMA kernel on K and V^T
     if (!std::is_same<T, bf16>::value ||
         !attention_takes_vt(DType::BF16, a.mode, p.n_q, a.head_dim, a.win_w, a.tokens_in,

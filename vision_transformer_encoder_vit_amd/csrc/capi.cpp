@@ -54,7 +54,8 @@ struct vit_block_plan {
   int64_t m_in, m_out;
   size_t esize;
   // workspace layout (byte offsets)
-  size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, off_vt, ws_bytes;
+  size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, off_vt, off_po, off_pml, ws_bytes;
+  int attn_splits;       // key splits of the large-window attention (1: none)
   bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
   bool attn_vt;          // qkv projection also writes V^T for the large-window attention kernel
 };
@@ -148,6 +149,17 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
                                        p->m_in * 3LL * d.dim_out) &&
                d.dim_in % 64 == 0;  // the qkv projection on the MFMA path writes V^T
   p->off_vt = p->attn_vt ? take(p->m_in, d.dim_out) : 0;
+  p->attn_splits = 1;
+  if (p->attn_vt) {
+    const int64_t windows = d.attn_mode == VIT_ATTN_SPATIAL
+                                ? (int64_t)(d.grid_h / d.win_h) * (d.grid_w / d.win_w) : 1;
+    const int64_t n_kv = d.attn_mode == VIT_ATTN_SPATIAL ? (int64_t)d.win_h * d.win_w : p->n_in;
+    p->attn_splits = vit::attention_splits(d.batch, windows, n_q, n_kv, d.heads);
+  }
+  // fp32 partials (sizes in elements of esize bytes, rounded up)
+  const int64_t fp32_cols = 4 / p->esize;
+  p->off_po = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, d.dim_out * fp32_cols) : 0;
+  p->off_pml = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, 2LL * d.heads * fp32_cols) : 0;
   p->ws_bytes = o;
   p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 && d.attn_mode == VIT_ATTN_MASK_UNIT && d.q_stride == 1 &&
                        d.rope == VIT_ROPE_NONE &&
@@ -419,6 +431,10 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   a.qkv = qkv;
   a.ld_qkv = 3 * Do;
   a.vt = P.attn_vt ? base + P.off_vt : nullptr;
+  if (P.attn_splits > 1) {
+    a.part_o = reinterpret_cast<float*>(base + P.off_po);
+    a.part_ml = reinterpret_cast<float*>(base + P.off_pml);
+  }
   a.ctx = ctx;
   a.ld_ctx = Do;
   a.batch = d.batch;

@@ -63,6 +63,10 @@ struct AttnArgs {
   // V transposed, [B, heads, head_dim, tokens_in]: given exactly when
   // attention_takes_vt() holds, and then read in place of qkv's V columns
   const void* vt = nullptr;
+  // key-split partials, needed when attention_splits() > 1 (vt path):
+  // part_o [splits, B*tokens_out, dim], part_ml [splits, B*tokens_out, heads, 2], fp32
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
   int64_t ld_qkv = 0;
   void* ctx = nullptr;        // [B * tokens_out, dim]
   int64_t ld_ctx = 0;
@@ -78,6 +82,19 @@ hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s, StageEve
 // window, head_dim <= 64, frame token count and (spatial) window width
 // multiples of 8 (16-byte runs of consecutive keys in V^T), 32-bit element
 // offsets into qkv.
+// Large-window attention on a small grid (fewer than 256 workgroups of 128
+// queries) splits each window's keys over several workgroups, each with at
+// least two 64-key tiles; a second kernel merges the partial softmaxes.
+inline int attention_splits(int64_t batch, int64_t windows, int64_t n_q, int64_t n_kv, int64_t heads) {
+  const int64_t blocks = batch * windows * ((n_q + 127) / 128) * heads;
+  const int64_t tiles = (n_kv + 63) / 64;
+  if (blocks <= 0 || blocks >= 256) return 1;
+  int64_t s = (256 + blocks - 1) / blocks;
+  s = s < tiles / 2 ? s : tiles / 2;
+  s = s < 8 ? s : 8;
+  return s >= 2 ? (int)s : 1;
+}
+
 inline bool attention_takes_vt(DType dt, int mode, int64_t n_q, int head_dim, int win_w, int64_t tokens_in,
                                int64_t qkv_elems) {
   return dt == DType::BF16 && (mode == ATTN_GLOBAL || (mode == ATTN_SPATIAL && win_w % 8 == 0)) && n_q >= 128 &&
