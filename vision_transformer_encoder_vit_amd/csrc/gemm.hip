@@ -233,10 +233,11 @@ struct Interleave {
   }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(GemmParams<bf16> p) {
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
-  constexpr int BK = 64, ST = 2;
+  constexpr int BK = 64;
+  static_assert(ST >= 2 && ST <= 4, "2 to 4 LDS stages");
   constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;  // 32x32 tiles per wave
   constexpr int STAGE = (BM + BN) * BK;                          // bf16 elements
   constexpr int LPW = (BM + BN) / (8 * NW);                      // load instructions per wave per stage
@@ -298,17 +299,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
 
   const int nk = p.K / BK;
   constexpr int KS = BK / 16;              // MFMA K steps per tile
-  constexpr int LPK = (LPW + 1) / 2;       // next-tile loads per K step, over the first two steps
+  constexpr int LPK = (LPW + 1) / 2;       // tile kt+ST-1's loads per K step, over the first two steps
+  // tiles 0 .. ST-2 in flight before the loop
+  for (int t = 0; t < ST - 1 && t < nk; ++t)
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) load(j, 0);
+    for (int j = 0; j < LPW; ++j) load(j, t);
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of tile kt have landed; after the barrier every
-    // wave's have, and every wave is done reading the stage refilled next
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // this wave's loads of tile kt have landed (the later tiles' loads, issued
+    // after them, may still be in flight); after the barrier every wave's
+    // have, and every wave is done reading the stage refilled next
+    const int ahead = min(ST - 2, nk - 1 - kt);
+    if (ST >= 4 && ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
+    else if (ST >= 3 && ahead >= 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const bool more = kt + 1 < nk;
+    const bool more = kt + ST - 1 < nk;
     const int stage = kt % ST;
     frags(0, stage, 0);
 #pragma unroll
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       if (more) {
 #pragma unroll
         for (int j = 0; j < LPW; ++j)
-          if (j / LPK == ks) load(j, kt + 1);
+          if (j / LPK == ks) load(j, kt + ST - 1);
       }
       if (ks + 1 < KS) frags((ks + 1) & 1, stage, ks + 1);
 #pragma unroll
@@ -433,16 +443,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2>
 static hipError_t gemm32_go(const GemmParams<bf16>& p, int epi, hipStream_t s, StageEvents ev) {
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
   switch (epi) {
-    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_BIAS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_BIAS_ROPE>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_GELU_ERF>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_GELU_TANH>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, EPI_BIAS_RES>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_ROPE>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_ERF>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_TANH>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_RES>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
   }
   return hipGetLastError();
 }
@@ -522,9 +532,11 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
       if (a.M % 192 == 0) return gemm32_go<192, 128, 2, 2>(p, a.epi, s, ev);
     }
     // small products (e.g. 1024 tokens x 448 columns): 128x128 tiles would
-    // leave most CUs idle, so 64x64 tiles (one 32x32 block per wave)
+    // leave most CUs idle, so 64x64 tiles (one 32x32 block per wave) with
+    // four LDS stages: a lone workgroup per CU has nothing else to hide its
+    // load latency behind
     const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (t128 < 192) return gemm32_go<64, 64, 2, 2>(p, a.epi, s, ev);
+    if (t128 < 192) return gemm32_go<64, 64, 2, 2, 4>(p, a.epi, s, ev);
     return gemm32_go<128, 128, 2, 2>(p, a.epi, s, ev);
   }
   const int64_t big_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
