@@ -205,6 +205,17 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
       b1_s[e - 5 * D] = p.b1[e - 5 * D];
     }
   }
+  // with at most HPR heads the qkv epilogue writes V transposed straight into
+  // vts (one attention round); rows head_dim..63 of each head stay zero
+  const bool vt_direct = p.heads <= HPR;
+  if (vt_direct) {
+    const int pad = 64 - hd;  // multiple of 8
+    for (int e = tid; e < p.heads * pad * (TW / 8); e += 64 * NWF) {
+      const int hl = e / (pad * (TW / 8)), rem = e - hl * pad * (TW / 8);
+      const int r = rem / (TW / 8), c = rem - r * (TW / 8);
+      st16(vts + (hl * 64 + hd + r) * VTS + c * 8, u32x4{0, 0, 0, 0});
+    }
+  }
   WFrags<(3 * DP / 16 + NWF - 1) / NWF, DP / 32> wqkv;
   wqkv.load([&](int n) { return n < D ? p.wq + (int64_t)n * D : (n < 2 * D ? p.wk + (int64_t)(n - D) * D : p.wv + (int64_t)(n - 2 * D) * D); },
             3 * D, D);
@@ -215,8 +226,16 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   wo.load([&](int n) { return p.wo + (int64_t)n * D; }, D, D);
   lds_barrier();
   // ---- q|k|v = h W^T + b -> qkvs
-  wqkv.gemm(cs, XS, 3 * D, D,
-      [&](int m, int n, f32x4 v) { store4<bf16>(qkvs + m * p.qs + n, v + *reinterpret_cast<const f32x4*>(bqkv + n)); });
+  wqkv.gemm(cs, XS, 3 * D, D, [&](int m, int n, f32x4 v) {
+    v = v + *reinterpret_cast<const f32x4*>(bqkv + n);
+    if (vt_direct && n >= 2 * D) {  // 4 consecutive d of one head (head_dim % 8 == 0)
+      const int vv = n - 2 * D, head = vv / hd, d = vv - head * hd;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vts[(head * 64 + d + e) * VTS + m] = (bf16)v[e];
+    } else {
+      store4<bf16>(qkvs + m * p.qs + n, v);
+    }
+  });
   WFrags<(512 / 16 + NWF - 1) / NWF, DP / 32> w1;
   w1.load([&](int n) { return p.w1 + (int64_t)n * D; }, p.mlp, D);
   lds_barrier();
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   const int fr = lane & 15, g = lane >> 4;
   for (int h0 = 0; h0 < p.heads; h0 += HPR) {
     // V^T of the round's heads: [hl][d][key], zero past head_dim
-    for (int e = tid; e < HPR * TW * 8; e += 64 * NWF) {
+    for (int e = tid; !vt_direct && e < HPR * TW * 8; e += 64 * NWF) {
       const int hl = e / (TW * 8), rem = e - hl * TW * 8;
       const int key = rem >> 3, c = rem & 7;
       const int head = h0 + hl;
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
 #pragma unroll
       for (int k = 0; k < 8; ++k) vts[(hl * 64 + c * 8 + k) * VTS + key] = vv[k];
     }
-    lds_barrier();
+    if (!vt_direct) lds_barrier();
     const int hl = wave >> 2, qb = wave & 3, head = h0 + hl;
     if (head < p.heads) {
       // S^T = K Q^T: s[kb][r] = S[q = qb*16 + fr][key = kb*16 + 4g + r]
@@ -315,10 +334,11 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   lds_barrier();
   // ---- LN2 -> cs
   ln_rows(x1s, cs, lnp + 2 * DP, lnp + 3 * DP, D, p.eps);
+  lds_barrier();
+  // ---- u = GELU(h2 W_1^T + b_1) -> uss; fc2's weights are requested first
+  // (after LN2's barrier, so issuing them does not hold up LN2)
   WFrags<1, 16> w2;
   w2.load([&](int n) { return p.w2 + (int64_t)n * p.mlp; }, D, p.mlp);
-  lds_barrier();
-  // ---- u = GELU(h2 W_1^T + b_1) -> uss
   w1.gemm(cs, XS, p.mlp, D,
       [&](int m, int n, f32x4 v) {
         v = v + *reinterpret_cast<const f32x4*>(b1_s + n);
@@ -344,7 +364,7 @@ bool fused_mask_unit_supported(int dim, int heads, int head_dim, int mlp, int wi
 
 size_t fused_mask_unit_lds_bytes(int dim, int mlp) {
   const size_t qs = 3 * dim + 8, us = mlp + 8;
-  const size_t a = TW * qs + 2 * 64 * VTS, u = TW * us;
+  const size_t a = TW * qs + HPR * 64 * VTS, u = TW * us;
   return 2 * (3 * TW * XS + (a > u ? a : u));
 }
 
