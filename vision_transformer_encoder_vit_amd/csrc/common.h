@@ -124,6 +124,46 @@ __device__ __forceinline__ float gelu_tanh_fast(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Cross-lane reductions without LDS round trips (ds_bpermute):
+// row16_*  over each row of 16 lanes with DPP: two quad swaps, then the
+//          half-row mirror (lane i <-> 7-i of its 8) and the row mirror
+//          (i <-> 15-i) each pair a lane with one of the other half;
+// pair16_* over lanes l and l^16, pair32_* over l and l^32, with the gfx950
+//          row swaps (v_permlane16_swap / v_permlane32_swap: with both
+//          operands x the two results are the two rows' values).
+#define VIT_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false))
+__device__ __forceinline__ float row16_sum(float x) {
+  x += VIT_DPP(x, 0xB1);   // quad_perm [1,0,3,2]
+  x += VIT_DPP(x, 0x4E);   // quad_perm [2,3,0,1]
+  x += VIT_DPP(x, 0x141);  // row_half_mirror
+  x += VIT_DPP(x, 0x140);  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, VIT_DPP(x, 0xB1));
+  x = fmaxf(x, VIT_DPP(x, 0x4E));
+  x = fmaxf(x, VIT_DPP(x, 0x141));
+  x = fmaxf(x, VIT_DPP(x, 0x140));
+  return x;
+}
+#undef VIT_DPP
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -77,8 +77,8 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
       for (int e = 0; e < 8; ++e) s += v[i][e];
     }
   }
-#pragma unroll
-  for (int m = LPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+  static_assert(LPR == 16, "row reductions are 16-lane DPP");
+  s = row16_sum(s);
   const float mean = s / (float)D;
   float q = 0.f;
 #pragma unroll
@@ -86,8 +86,7 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
     if (l8 + LPR * i < nch)
 #pragma unroll
       for (int e = 0; e < 8; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
-#pragma unroll
-  for (int m = LPR / 2; m > 0; m >>= 1) q += __shfl_xor(q, m, 64);
+  q = row16_sum(q);
   const float inv = 1.0f / sqrtf(q / (float)D + eps);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
@@ -280,8 +279,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = pair32_max(pair16_max(mx));
       const float c = p.scale_log2, mc = mx * c;
       float l = 0.f;
 #pragma unroll
@@ -292,8 +290,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
           s[kb][r] = e;
           l += e;
         }
-      l += __shfl_xor(l, 16, 64);
-      l += __shfl_xor(l, 32, 64);
+      l = pair32_sum(pair16_sum(l));
       // O^T = V^T P^T over two 32-key steps
       f32x4 o[4];
 #pragma unroll
