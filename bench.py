@@ -242,6 +242,57 @@ def copy_calibration(steps):
                       "copy_bytes_written_per_launch": COPY_ROWS * COPY_COLS * 2, "launches": steps}))
 
 
+def rowops_cold(steps):
+    """HBM bandwidth of the memory-bound kernels on working sets larger than
+    the 256 MB Infinity Cache: each launch reads and writes a different one of
+    several buffer sets (about 0.7-0.8 GB in all), so every launch streams
+    from HBM. Prints one JSON line per kernel: algorithmic bytes per launch,
+    mean device time per launch (events around K back-to-back launches) and
+    GB/s as a fraction of the HBM peak."""
+    import torch
+    from vision_transformer_encoder_vit_amd import binding as vb
+    NB = 3
+
+    def timed(fn):
+        for i in range(2 * NB):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def report(name, shape, nbytes, us):
+        gbs = nbytes / us / 1e3
+        print(json.dumps({"kernel": name, "shape": shape, "bytes_per_launch": nbytes, "us_per_launch": round(us, 2),
+                          "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 3),
+                          "working_set_MB": round(NB * nbytes / 1e6)}), flush=True)
+
+    bf = torch.bfloat16
+    rows, dim = 65536, 1024
+    xs = [torch.randn(rows, dim, device="cuda").to(bf) for _ in range(NB)]
+    ys = [torch.empty_like(xs[0]) for _ in range(NB)]
+    g, b = torch.ones(dim, device="cuda"), torch.zeros(dim, device="cuda")
+    report("layernorm", [rows, dim], 2 * rows * dim * 2,
+           timed(lambda i: vb.vit_layernorm(xs[i % NB], ys[i % NB], g, b, 1e-6)))
+    del xs, ys
+    B, H, W, C = 32, 128, 128, 112
+    xs = [torch.randn(B, H * W, C, device="cuda").to(bf) for _ in range(NB)]
+    ys = [torch.empty_like(xs[0]) for _ in range(NB)]
+    report("unroll (3 levels)", [B, H * W, C], 2 * B * H * W * C * 2,
+           timed(lambda i: vb.vit_unroll(xs[i % NB], ys[i % NB], H, W, 3)))
+    report("reroll (3 levels)", [B, H * W, C], 2 * B * H * W * C * 2,
+           timed(lambda i: vb.vit_reroll(xs[i % NB], ys[i % NB], H, W, 3)))
+    del xs, ys
+    B, N, C = 16, 16384, 224
+    xs = [torch.randn(B, N, C, device="cuda").to(bf) for _ in range(NB)]
+    ys = [torch.empty(B, N // 4, C, device="cuda", dtype=bf) for _ in range(NB)]
+    report("pool4", [B, N, C], 5 * B * (N // 4) * C * 2, timed(lambda i: vb.vit_pool4(xs[i % NB], ys[i % NB])))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +300,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=DEFAULT_CONFIG, help="workload name, or 'all'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rowops", action="store_true",
+                    help="only time LayerNorm, unroll, reroll and pool4 on HBM-resident working sets")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (vit_unroll with 0 levels), to scale "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
@@ -259,6 +312,9 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         ap.error("steps >= 1 and warmup >= 0")
+    if args.rowops:
+        rowops_cold(args.steps)
+        return
     if args.copy_calibration:
         copy_calibration(args.steps)
         return
