@@ -215,13 +215,23 @@ hipError_t launch_pool4(const void* x, int64_t xs, void* y, int64_t ys, int batc
                         int channels, DType dt, hipStream_t s, StageEvents ev) {
   const int64_t rows = (int64_t)batch * (tokens / 4);
   if (rows == 0) return hipSuccess;
-  auto go = [&](auto ttag) {
+  // G lanes per output row: the smallest group that covers the row in one
+  // pass of 16-byte vectors (all four source loads of a lane in flight at once)
+  auto launch = [&](auto ttag, auto gtag) {
     using T = decltype(ttag);
-    constexpr int G = 16;
+    constexpr int G = decltype(gtag)::value;
     const int64_t blocks = (rows + (256 / G) - 1) / (256 / G);
     hipExtLaunchKernelGGL((pool4_kernel<T, G>), dim3((unsigned)blocks), dim3(256), 0, s, ev.start, ev.stop, 0,
                           (const T*)x, xs, (T*)y, ys, batch, tokens, channels);
     return hipGetLastError();
+  };
+  auto go = [&](auto ttag) {
+    using T = decltype(ttag);
+    const int nvec = channels / Vec<T>::N;
+    if (nvec <= 8) return launch(ttag, std::integral_constant<int, 8>());
+    if (nvec <= 16) return launch(ttag, std::integral_constant<int, 16>());
+    if (nvec <= 32) return launch(ttag, std::integral_constant<int, 32>());
+    return launch(ttag, std::integral_constant<int, 64>());
   };
   return dt == DType::BF16 ? go(bf16()) : go(float());
 }
