@@ -361,3 +361,77 @@ def test_block_rows_equals_full_block():
         part = ob.block_forward_rows(inp["x"], inp, spec, rows)
         for k, v in part.items():
             np.testing.assert_allclose(v, full[k][:, rows], atol=1e-12, err_msg=k)
+
+
+# ---- Hiera stage stack (oracle/stack.py) ----
+
+def test_stack_shape_contract_512():
+    # the plan's per-stage feature shapes at a 512x512 input (128x128 tokens)
+    from oracle import stack as ost
+    rows = np.loadtxt(os.path.join(GOLDEN, "hiera_stage_shapes.txt"), dtype=np.int64)
+    specs, levels, taps = synth.hiera_stack(side=128)
+    assert len(specs) == 24 and taps == [1, 4, 20, 23]
+    assert [i for i, s in enumerate(specs) if s["q_stride"] == 4] == [2, 5, 21]
+    for (stage, grid, dim, heads, win, mu), t in zip(rows, taps):
+        sp = specs[t]
+        assert (sp["dim_out"], sp["heads"]) == (dim, heads)
+        assert (sp["mode"] == "mask_unit") == bool(mu)
+        n_out = sp["grid_h"] * sp["grid_w"] // sp["q_stride"]
+        assert n_out == grid * grid
+        if mu:
+            assert n_out // sp["n_windows"] == win
+    # shapes through the oracle itself, on a 4x narrower grid with the same
+    # stage structure (one block per stage)
+    small, levels, taps = synth.hiera_stack(side=32, stage_blocks=(1, 1, 1, 1))
+    x, blocks = synth.make_stack_inputs(small, seed=3)
+    feats = ost.stack_forward(x, blocks, small, levels, taps)
+    assert [f.shape for f in feats] == [(1, 32 * 32, 112), (1, 16 * 16, 224), (1, 8 * 8, 448), (1, 4 * 4, 896)]
+
+
+def test_stack_global_blocks_do_not_see_token_order():
+    # global attention and the row-wise steps are permutation-equivariant:
+    # through unroll -> blocks -> reroll the stack must equal the same blocks
+    # on raster-order tokens, exactly (float64, same arithmetic per row)
+    from oracle import stack as ost
+    base = synth.derive(synth.CONFIGS["c3b_hiera_s2"], grid_h=16, grid_w=16, dim_in=112, dim_out=112, heads=2,
+                        mlp=224, dtype="f32")
+    specs = [dict(base, name="g%d" % i) for i in range(3)]
+    x, blocks = synth.make_stack_inputs(specs, seed=5)
+    for levels in (1, 2, 3):
+        f = ost.stack_forward(x, blocks, specs, levels, [0, 2])
+        ref = x.astype(np.float64)
+        outs = []
+        for i, (w, sp) in enumerate(zip(blocks, specs)):
+            ref = ob.block_forward(ref, w, sp)["y"]
+            if i in (0, 2):
+                outs.append(ref)
+        for a, b in zip(f, outs):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_stack_pooled_features_independent_of_unroll_depth():
+    # a global block with the 2x2 query pool: the pool groups are the 2x2
+    # cells for any unroll depth >= 1 (finest level outermost), and the
+    # feature is rerolled with one level fewer; so the raster-order feature
+    # must not depend on the depth. A stack that forgot to drop the level
+    # (or pooled the wrong groups) differs.
+    from oracle import stack as ost
+    sp = synth.derive(synth.CONFIGS["c3b_hiera_s2"], grid_h=16, grid_w=16, dim_in=112, dim_out=224, heads=4,
+                      mlp=448, q_stride=4, dtype="f32")
+    nxt = synth.derive(synth.CONFIGS["c3b_hiera_s2"], grid_h=8, grid_w=8, dim_in=224, dim_out=224, heads=4,
+                       mlp=448, dtype="f32")
+    specs = [dict(sp, name="p"), dict(nxt, name="q")]
+    x, blocks = synth.make_stack_inputs(specs, seed=7)
+    feats = [ost.stack_forward(x, blocks, specs, levels, [0, 1]) for levels in (1, 2, 3)]
+    for other in feats[1:]:
+        for a, b in zip(feats[0], other):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    # and the pooled residual of the unrolled tokens, rerolled, is the 2x2
+    # spatial max of the raster-order projection
+    h_rast = ob.layer_norm(x[0].astype(np.float64), blocks[0]["ln1_g"].astype(np.float64),
+                           blocks[0]["ln1_b"].astype(np.float64), sp["eps"])
+    proj = ob.linear(h_rast, blocks[0]["res_w"], blocks[0]["res_b"].astype(np.float64)).reshape(16, 16, -1)
+    pooled = proj.reshape(8, 2, 8, 2, -1).max(axis=(1, 3)).reshape(64, -1)
+    t = im.unroll(x.astype(np.float64), 16, 16, 2)
+    r = ob.block_forward(t, blocks[0], sp)["r"]
+    np.testing.assert_allclose(im.reroll(r, 8, 8, 1)[0], pooled, rtol=1e-12, atol=1e-12)

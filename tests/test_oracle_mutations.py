@@ -78,6 +78,23 @@ def _unroll_coarse_first(H, W, L):
 _orig_rope = ob.apply_rope
 _orig_attention = ob.attention
 
+def _stack_levels_kept(x, blocks, specs, levels, taps):
+    # forgets that a 2x2 pool consumes one unroll level
+    from oracle import stack as ost
+    H, W = specs[0]["grid_h"], specs[0]["grid_w"]
+    t = im.unroll(np.asarray(x, dtype=np.float64), H, W, levels)
+    feats = []
+    for i, (w, sp) in enumerate(zip(blocks, specs)):
+        t = ob.block_forward(t, w, sp)["y"]
+        if sp["q_stride"] == 4:
+            H, W = H // 2, W // 2
+        if i in taps:
+            feats.append(im.reroll(t, H, W, levels))
+    return feats
+
+
+from oracle import stack as ost  # noqa: E402
+
 MUTATIONS = [
     ("layer_norm unbiased variance", ob, "layer_norm", _ln_unbiased, pins.test_layer_norm_closed_form),
     ("layer_norm eps outside sqrt", ob, "layer_norm", _ln_eps_outside, pins.test_layer_norm_closed_form),
@@ -89,6 +106,8 @@ MUTATIONS = [
     ("attention scale dropped", ob, "attention", _attention_no_scale, pins.test_attention_vs_torch_sdpa),
     ("pool over adjacent rows", ob, "pool4", _pool_adjacent, pins.test_pool4_definition),
     ("unroll coarse level first", im, "unroll_positions", _unroll_coarse_first, pins.test_mask_unit_is_spatial_block_and_pool_is_2x2_cell),
+    ("stack keeps unroll levels after a pool", ost, "stack_forward", _stack_levels_kept,
+     pins.test_stack_pooled_features_independent_of_unroll_depth),
 ]
 
 

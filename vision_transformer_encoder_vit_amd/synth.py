@@ -170,6 +170,52 @@ def make_inputs(spec, seed=0, qk_gain=1.0):
     return out
 
 
+# Hiera stage stack (the Hiera plan's "Architecture Summary"): 24 blocks in
+# four stages; stage s has width 112*2^s, 2^(s+1) heads of 56, mask units of
+# 64/4^s tokens (mask-unit attention in stages 0-1, global in 2-3); the first
+# block of stages 1-3 is a transition (projection + 2x2 max-pool, q_stride 4);
+# features are taken after the last block of each stage. MLP ratio 4.
+HIERA_STAGE_BLOCKS = (2, 3, 16, 3)
+HIERA_UNROLL_LEVELS = 3
+
+
+def hiera_stack(side=128, batch=1, stage_blocks=HIERA_STAGE_BLOCKS, dtype="bf16"):
+    """Block specs of a Hiera stage stack on a side x side token grid (128 at a
+    512x512 input), the unroll levels and the feature taps (block indices)."""
+    specs, taps = [], []
+    dim, grid = 112, side
+    for stage, nb in enumerate(stage_blocks):
+        for j in range(nb):
+            trans = stage > 0 and j == 0
+            d_in = dim // 2 if trans else dim
+            g_in = grid * 2 if trans else grid
+            mask_unit = stage < 2
+            window = 64 // 4 ** stage  # tokens per mask unit at this stage's grid
+            sp = _spec("hiera_b%d" % len(specs), batch=batch, grid_h=g_in, grid_w=g_in,
+                       dim_in=d_in, dim_out=dim, heads=2 ** (stage + 1), mlp=4 * dim,
+                       mode="mask_unit" if mask_unit else "global",
+                       n_windows=(grid * grid) // window if mask_unit else 1,
+                       q_stride=4 if trans else 1, dtype=dtype)
+            specs.append(sp)
+        taps.append(len(specs) - 1)
+        dim, grid = dim * 2, grid // 2
+    return specs, HIERA_UNROLL_LEVELS, taps
+
+
+def make_stack_inputs(specs, seed=0):
+    """Raster-order token input of the first block and every block's weights
+    (block i draws with seed (seed, i) through make_inputs)."""
+    blocks = []
+    x = None
+    for i, sp in enumerate(specs):
+        w = make_inputs(sp, seed=seed * 1000 + i)
+        if i == 0:
+            x = w["x"]
+        del w["x"]
+        blocks.append(w)
+    return x, blocks
+
+
 def out_tokens(spec):
     """Tokens per frame leaving the block (4x fewer at a pooled transition)."""
     return spec["grid_h"] * spec["grid_w"] // spec["q_stride"]
