@@ -225,6 +225,40 @@ vit_status vit_block_destroy(vit_block_t plan);
 
 const char* vit_last_error(void);
 
+/* ---- a stack of blocks over one token grid (Hiera plan, "Architecture
+ * Summary" and "Implementation Plan" item 8: Unroll once, the blocks in
+ * order, Reroll at each stage end) ---- */
+
+typedef struct vit_stack_plan* vit_stack_t;
+
+/* Plan `n_blocks` blocks applied in order. Block 0 reads x [B, grid_h*grid_w,
+ * dim_in] in raster order, which is first unrolled with `unroll_levels` 2x2
+ * levels (the block descriptors see the unrolled order, as MASK_UNIT needs);
+ * every block with q_stride 4 halves the grid and uses up one level. After
+ * block taps[k] (increasing) its output is rerolled with the levels left
+ * into feature k, raster order [B, H_k*W_k, dim_out]. Block i+1 must take
+ * block i's output: same batch and dtype, its grid_h/grid_w the halved grid
+ * after a transition, dim_in = dim_out. Errors as vit_block_create, plus a
+ * chain that does not connect, levels that run out (q_stride 4 or
+ * MASK_UNIT with no level left) or bad taps. Holds no device memory. */
+vit_status vit_stack_create(const vit_block_desc* blocks, int32_t n_blocks,
+                            int32_t unroll_levels, const int32_t* taps,
+                            int32_t n_taps, vit_stack_t* out);
+
+/* Bytes of device workspace a stack forward needs (two activation buffers
+ * and the largest block workspace; a multiple of 256). */
+vit_status vit_stack_workspace_size(vit_stack_t plan, size_t* bytes);
+
+/* Run the stack: weights[i] for block i; features[k] receives tap k (all
+ * 16-byte aligned, not overlapping x or the workspace). Asynchronous on
+ * `stream`, like vit_block_forward. */
+vit_status vit_stack_forward(vit_stack_t plan, const vit_block_weights* weights,
+                             const void* x, void* const* features,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+vit_status vit_stack_destroy(vit_stack_t plan);
+
 /* ---- single steps (same kernels the block uses) ---- */
 
 /* Row LayerNorm (SAM3 `layer_norm_rows`): y = (x - mean) / sqrt(var + eps)

@@ -185,3 +185,39 @@ def test_stage_mask():
     assert not m >> names.index("fused") & 1
     m = vb.Plan(vb.desc_from_spec(synth.CONFIGS["c3a_hiera_trans"])).stage_mask()
     assert m >> names.index("residual") & 1
+
+
+def _stack_descs(**kw):
+    specs, levels, taps = synth.hiera_stack(**kw)
+    return [vb.desc_from_spec(s) for s in specs], levels, taps
+
+
+def test_stack_create_hiera_512():
+    descs, levels, taps = _stack_descs()
+    st = vb.Stack(descs, levels, taps)
+    # two activation buffers of the largest token tensor (16384 x 224 bf16
+    # entering/leaving block 2 is the largest) plus a block workspace
+    assert st.workspace_bytes >= 2 * 16384 * 224 * 2
+    st.close()
+
+
+def test_stack_create_rejects():
+    descs, levels, taps = _stack_descs(side=32, stage_blocks=(1, 1, 1, 1))
+    cases = [
+        (dict(levels=3, taps=[1, 0]), "taps must be increasing"),
+        (dict(levels=3, taps=[4]), "taps must be increasing"),
+        (dict(levels=2, taps=taps), "none left"),          # three pools, two levels
+        (dict(levels=6, taps=taps), "not divisible"),      # 32x32 grid, 2^6
+    ]
+    for kw, msg in cases:
+        with pytest.raises(vb.VitError) as e:
+            vb.Stack(descs, kw["levels"], kw["taps"])
+        assert msg in str(e.value), (kw, str(e.value))
+    bad = list(descs)
+    d = vb.desc_from_spec(synth.derive(synth.hiera_stack(side=32, stage_blocks=(1, 1, 1, 1))[0][1], dim_in=112 + 8))
+    bad[1] = d
+    with pytest.raises(vb.VitError) as e:
+        vb.Stack(bad, levels, taps)
+    assert "does not take block 0" in str(e.value)
+    with pytest.raises(vb.VitError):
+        vb.Stack([], levels, [])

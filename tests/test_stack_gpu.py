@@ -1,0 +1,85 @@
+"""Hiera stage stack on the GPU (vit_stack_* through the C ABI) against the
+float64 stack oracle: Unroll once, the blocks in order, Reroll at each
+stage end."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import stack as ost
+from tests import gpu_util as gu
+from vision_transformer_encoder_vit_amd import binding as vb
+from vision_transformer_encoder_vit_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_stack(specs, levels, taps, x, blocks):
+    dt = gu.torch_dtype(specs[0])
+    dev_w = [gu.to_device(w, sp) for w, sp in zip(blocks, specs)]
+    weights = [vb.weights_struct(w) for w in dev_w]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(dt).cuda()
+    st = vb.Stack([vb.desc_from_spec(s) for s in specs], levels, taps)
+    feats = []
+    for t in taps:
+        sp = specs[t]
+        feats.append(torch.empty((sp["batch"], synth.out_tokens(sp), sp["dim_out"]), dtype=dt, device="cuda"))
+    ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+    st.forward(weights, xd, feats, ws)
+    torch.cuda.synchronize()
+    st.close()
+    return feats, dev_w, xd
+
+
+@pytest.mark.parametrize("side,stage_blocks", [(32, (2, 2, 2, 2)), (128, synth.HIERA_STAGE_BLOCKS)],
+                         ids=["32x32_8blocks", "hiera_512_24blocks"])
+def test_stack_vs_oracle(side, stage_blocks):
+    specs, levels, taps = synth.hiera_stack(side=side, stage_blocks=stage_blocks)
+    print("case stack", side, stage_blocks, flush=True)
+    x, blocks = synth.make_stack_inputs(specs, seed=0)
+    feats, _, _ = _run_stack(specs, levels, taps, x, blocks)
+    ref = ost.stack_forward(x, blocks, specs, levels, taps)
+    for k, (got, want) in enumerate(zip(feats, ref)):
+        g = gu.to64(got)
+        assert g.shape == want.shape and np.all(np.isfinite(g))
+        # Gate of a stack of bf16 blocks (a reading): the bf16 roundings of
+        # the residual stream add up over the blocks, and each transition
+        # replaces the stream by a projection about 5x smaller, so errors
+        # made before it grow relative to what follows (measured: norm-wise
+        # 3e-3 after 2 blocks, ~6e-3 after the first transition, ~1.2e-2
+        # after the second and third, whether 8 or 24 blocks). Taken: the
+        # tower gate form of the SigLIP page (cosine >= 0.9999 per output)
+        # and the single block's 2e-2 applied norm-wise.
+        a, b = g.ravel(), want.ravel()
+        cos = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+        nrel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        mrel = float(np.abs(a - b).max() / np.abs(b).max())
+        print("feature %d (after block %d): cos %.7f norm-rel %.2e max-rel %.2e" % (k, taps[k], cos, nrel, mrel))
+        assert cos >= 0.9999 and nrel <= 2e-2, (k, cos, nrel)
+
+
+def test_stack_equals_chained_single_calls():
+    # the native stack is exactly vit_unroll -> vit_block_forward per block ->
+    # vit_reroll at the taps, bit for bit
+    specs, levels, taps = synth.hiera_stack(side=32, stage_blocks=(1, 2, 2, 1))
+    x, blocks = synth.make_stack_inputs(specs, seed=1)
+    feats, dev_w, xd = _run_stack(specs, levels, taps, x, blocks)
+    H = W = specs[0]["grid_h"]
+    cur = torch.empty_like(xd)
+    vb.vit_unroll(xd, cur, H, W, levels)
+    k = 0
+    for i, (sp, w) in enumerate(zip(specs, dev_w)):
+        plan = vb.Plan(vb.desc_from_spec(sp))
+        out = torch.empty((sp["batch"], synth.out_tokens(sp), sp["dim_out"]), dtype=xd.dtype, device="cuda")
+        ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+        plan.forward(vb.weights_struct(w), cur, out, ws)
+        plan.close()
+        cur = out
+        if sp["q_stride"] == 4:
+            levels -= 1
+            H, W = H // 2, W // 2
+        if i in taps:
+            f = torch.empty_like(cur)
+            vb.vit_reroll(cur, f, H, W, levels)
+            torch.cuda.synchronize()
+            assert torch.equal(f.view(torch.int16), feats[k].view(torch.int16)), i
+            k += 1

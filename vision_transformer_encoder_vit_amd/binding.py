@@ -78,6 +78,10 @@ def _load():
         "vit_unroll": [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
         "vit_reroll": [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
         "vit_pool4": [_vp, ctypes.c_int64, _vp, ctypes.c_int64, _i32, _i32, _i32, _i32, _vp],
+        "vit_stack_create": [P(vit_block_desc), _i32, _i32, P(_i32), _i32, P(_vp)],
+        "vit_stack_workspace_size": [_vp, P(ctypes.c_size_t)],
+        "vit_stack_forward": [_vp, P(vit_block_weights), _vp, P(_vp), _vp, ctypes.c_size_t, _vp],
+        "vit_stack_destroy": [_vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -188,6 +192,41 @@ class Plan:
     def close(self):
         if self.handle is not None:
             lib.vit_block_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Stack:
+    """A created vit_stack plan: blocks applied in order to one token grid,
+    unrolled once and rerolled after each tap (vit_stack_create)."""
+
+    def __init__(self, descs, unroll_levels, taps):
+        arr = (vit_block_desc * len(descs))(*descs)
+        t = (_i32 * max(len(taps), 1))(*taps)
+        h = ctypes.c_void_p()
+        check(lib.vit_stack_create(arr, len(descs), unroll_levels, t, len(taps), ctypes.byref(h)))
+        self.handle = h
+        self.n_blocks, self.n_taps = len(descs), len(taps)
+        n = ctypes.c_size_t()
+        check(lib.vit_stack_workspace_size(h, ctypes.byref(n)))
+        self.workspace_bytes = n.value
+
+    def forward(self, weights, x, features, workspace, stream=None):
+        """weights: list of vit_block_weights (one per block); features: list
+        of output tensors (one per tap)."""
+        w = (vit_block_weights * self.n_blocks)(*weights)
+        f = (_vp * max(self.n_taps, 1))(*[t.data_ptr() for t in features])
+        check(lib.vit_stack_forward(self.handle, w, _ptr(x), f, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+    def close(self):
+        if self.handle is not None:
+            lib.vit_stack_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

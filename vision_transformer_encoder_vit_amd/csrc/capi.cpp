@@ -8,8 +8,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/vit_block.h"
 #include "launch.h"
@@ -536,6 +538,144 @@ VIT_API vit_status vit_block_forward_seams(vit_block_t plan, const vit_block_wei
                                            void* stream) {
   if (!seams) return fail(VIT_ERR_INVALID_ARG, "seams struct is NULL");
   return forward_impl(plan, w, x, y, seams, workspace, workspace_bytes, stream);
+}
+
+// ---- stack of blocks
+
+struct vit_stack_plan {
+  std::vector<vit_block_plan*> blocks;
+  std::vector<int> taps, tap_levels, tap_grid_h, tap_grid_w;
+  int levels0 = 0, batch = 0, esize = 2;
+  int64_t tokens0 = 0;
+  int dim0 = 0;
+  size_t act_bytes = 0, ws_block = 0, ws_bytes = 0;
+  ~vit_stack_plan() {
+    for (vit_block_plan* b : blocks) delete b;
+  }
+};
+
+VIT_API vit_status vit_stack_create(const vit_block_desc* blocks, int32_t n_blocks, int32_t unroll_levels,
+                                    const int32_t* taps, int32_t n_taps, vit_stack_t* out) {
+  if (!out) return fail(VIT_ERR_INVALID_ARG, "out handle pointer is NULL");
+  if (!blocks || n_blocks < 1) return fail(VIT_ERR_INVALID_ARG, "need at least one block descriptor");
+  if (unroll_levels < 0 || unroll_levels > 8) return fail(VIT_ERR_INVALID_ARG, "unroll_levels %d outside 0..8", unroll_levels);
+  if (n_taps < 0 || (n_taps > 0 && !taps)) return fail(VIT_ERR_INVALID_ARG, "bad taps array");
+  for (int k = 0; k < n_taps; ++k)
+    if (taps[k] < 0 || taps[k] >= n_blocks || (k > 0 && taps[k] <= taps[k - 1]))
+      return fail(VIT_ERR_INVALID_ARG, "taps must be increasing block indices (tap %d = %d)", k, taps[k]);
+  const vit_block_desc& b0 = blocks[0];
+  if (b0.grid_h % (1 << unroll_levels) || b0.grid_w % (1 << unroll_levels))
+    return fail(VIT_ERR_INVALID_ARG, "grid %dx%d not divisible by 2^%d", b0.grid_h, b0.grid_w, unroll_levels);
+  auto* sp = new (std::nothrow) vit_stack_plan();
+  if (!sp) return fail(VIT_ERR_INVALID_ARG, "out of host memory");
+  std::unique_ptr<vit_stack_plan> guard(sp);
+  sp->levels0 = unroll_levels;
+  sp->batch = b0.batch;
+  sp->esize = b0.act_dtype == VIT_DTYPE_BF16 ? 2 : 4;
+  sp->tokens0 = (int64_t)b0.grid_h * b0.grid_w;
+  sp->dim0 = b0.dim_in;
+  int levels = unroll_levels, k = 0;
+  size_t act = 0;
+  for (int i = 0; i < n_blocks; ++i) {
+    const vit_block_desc& d = blocks[i];
+    if (i > 0) {
+      const vit_block_desc& pd = blocks[i - 1];
+      const int gh = pd.grid_h / (pd.q_stride == 4 ? 2 : 1), gw = pd.grid_w / (pd.q_stride == 4 ? 2 : 1);
+      if (d.batch != pd.batch || d.act_dtype != pd.act_dtype || d.grid_h != gh || d.grid_w != gw ||
+          d.dim_in != pd.dim_out)
+        return fail(VIT_ERR_INVALID_ARG, "block %d does not take block %d's output (batch, dtype, %dx%d grid, dim %d)",
+                    i, i - 1, gh, gw, pd.dim_out);
+    }
+    if (d.attn_mode == VIT_ATTN_MASK_UNIT && levels < 1)
+      return fail(VIT_ERR_INVALID_ARG, "block %d: mask units need an unrolled order, no level left", i);
+    if (d.q_stride == 4 && levels < 1)
+      return fail(VIT_ERR_INVALID_ARG, "block %d: a 2x2 pool needs an unroll level, none left", i);
+    vit_block_t bp = nullptr;
+    vit_status st = vit_block_create(&d, &bp);
+    if (st != VIT_OK) {
+      const std::string msg = g_err;
+      return fail(st, "block %d: %s", i, msg.c_str());
+    }
+    sp->blocks.push_back(bp);
+    const int64_t n_in = (int64_t)d.grid_h * d.grid_w, n_out = n_in / d.q_stride;
+    act = std::max(act, (size_t)d.batch * n_in * d.dim_in * sp->esize);
+    act = std::max(act, (size_t)d.batch * n_out * d.dim_out * sp->esize);
+    sp->ws_block = std::max(sp->ws_block, bp->ws_bytes);
+    if (d.q_stride == 4) --levels;
+    if (k < n_taps && taps[k] == i) {
+      sp->taps.push_back(i);
+      sp->tap_levels.push_back(levels);
+      sp->tap_grid_h.push_back(d.grid_h / (d.q_stride == 4 ? 2 : 1));
+      sp->tap_grid_w.push_back(d.grid_w / (d.q_stride == 4 ? 2 : 1));
+      ++k;
+    }
+  }
+  sp->act_bytes = round256(act);
+  sp->ws_bytes = 2 * sp->act_bytes + round256(sp->ws_block);
+  *out = guard.release();
+  return ok();
+}
+
+VIT_API vit_status vit_stack_workspace_size(vit_stack_t plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(VIT_ERR_INVALID_ARG, "plan or bytes pointer is NULL");
+  *bytes = plan->ws_bytes;
+  return ok();
+}
+
+VIT_API vit_status vit_stack_forward(vit_stack_t plan, const vit_block_weights* weights, const void* x,
+                                     void* const* features, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(VIT_ERR_INVALID_ARG, "plan is NULL");
+  const vit_stack_plan& P = *plan;
+  if (!weights || !x) return fail(VIT_ERR_INVALID_ARG, "weights or x is NULL");
+  if (!P.taps.empty() && !features) return fail(VIT_ERR_INVALID_ARG, "features array is NULL");
+  if (workspace_bytes < P.ws_bytes) return fail(VIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, P.ws_bytes);
+  if (!workspace || !aligned16(workspace)) return fail(VIT_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+  if (!aligned16(x)) return fail(VIT_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  const size_t x_bytes = (size_t)P.batch * P.tokens0 * P.dim0 * P.esize;
+  if (overlaps(workspace, P.ws_bytes, x, x_bytes)) return fail(VIT_ERR_INVALID_ARG, "workspace overlaps x");
+  for (size_t k = 0; k < P.taps.size(); ++k) {
+    const vit_block_desc& d = P.blocks[P.taps[k]]->d;
+    const size_t fb = (size_t)P.blocks[P.taps[k]]->m_out * d.dim_out * P.esize;
+    if (!features[k] || !aligned16(features[k])) return fail(VIT_ERR_INVALID_ARG, "feature %zu is NULL or misaligned", k);
+    if (overlaps(features[k], fb, workspace, P.ws_bytes) || overlaps(features[k], fb, x, x_bytes))
+      return fail(VIT_ERR_INVALID_ARG, "feature %zu overlaps x or the workspace", k);
+  }
+  for (size_t i = 0; i < P.blocks.size(); ++i) {
+    vit_status st = check_weights(P.blocks[i], &weights[i]);
+    if (st != VIT_OK) {
+      const std::string msg = g_err;
+      return fail(st, "block %zu: %s", i, msg.c_str());
+    }
+  }
+  char* base = (char*)workspace;
+  void* buf[2] = {base, base + P.act_bytes};
+  void* ws_b = base + 2 * P.act_bytes;
+  const int32_t dt = P.blocks[0]->d.act_dtype;
+  const vit_block_desc& b0 = P.blocks[0]->d;
+  vit_status st = vit_unroll(x, buf[0], P.batch, b0.grid_h, b0.grid_w, P.levels0, P.dim0, dt, stream);
+  if (st != VIT_OK) return st;
+  int cur = 0;
+  size_t k = 0;
+  for (size_t i = 0; i < P.blocks.size(); ++i) {
+    st = vit_block_forward(P.blocks[i], &weights[i], buf[cur], buf[cur ^ 1], ws_b, P.ws_block, stream);
+    if (st != VIT_OK) {
+      const std::string msg = g_err;
+      return fail(st, "block %zu: %s", i, msg.c_str());
+    }
+    cur ^= 1;
+    if (k < P.taps.size() && P.taps[k] == (int)i) {
+      st = vit_reroll(buf[cur], features[k], P.batch, P.tap_grid_h[k], P.tap_grid_w[k], P.tap_levels[k],
+                      P.blocks[i]->d.dim_out, dt, stream);
+      if (st != VIT_OK) return st;
+      ++k;
+    }
+  }
+  return ok();
+}
+
+VIT_API vit_status vit_stack_destroy(vit_stack_t plan) {
+  delete plan;
+  return ok();
 }
 
 // ---- single steps
