@@ -242,6 +242,55 @@ def copy_calibration(steps):
                       "copy_bytes_written_per_launch": COPY_ROWS * COPY_COLS * 2, "launches": steps}))
 
 
+def run_stack(steps, warmup, with_cpu):
+    """The Hiera stage stack at a 512x512 input (128x128 tokens, 24 blocks,
+    features rerolled after blocks 1, 4, 20 and 23) through vit_stack_forward:
+    K event-free forwards timed like the block workload."""
+    import numpy as np
+    import torch
+    from vision_transformer_encoder_vit_amd import binding as vb
+    from vision_transformer_encoder_vit_amd import synth, work
+    specs, levels, taps = synth.hiera_stack()
+    x, blocks = synth.make_stack_inputs(specs, seed=0)
+    dt = torch.bfloat16
+    dev_w = []
+    for w in blocks:
+        dev_w.append({k: (torch.from_numpy(np.ascontiguousarray(a)).to(dt) if k.endswith("_w")
+                          else torch.from_numpy(np.ascontiguousarray(a))).cuda() for k, a in w.items()})
+    weights = [vb.weights_struct(w) for w in dev_w]
+    xd = torch.from_numpy(x).to(dt).cuda()
+    st = vb.Stack([vb.desc_from_spec(s) for s in specs], levels, taps)
+    feats = [torch.empty((1, synth.out_tokens(specs[t]), specs[t]["dim_out"]), dtype=dt, device="cuda") for t in taps]
+    ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        st.forward(weights, xd, feats, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.forward(weights, xd, feats, ws)
+    torch.cuda.synchronize()
+    dt_step = (time.perf_counter() - t0) / steps
+    st.close()
+    flops = sum(work.block_flops(s) for s in specs)
+    tokens = specs[0]["grid_h"] * specs[0]["grid_w"]
+    line = {"metric": "Hiera stage stack (24 blocks, 512x512 input) input tokens/sec, 1 GPU", "value": tokens / dt_step,
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": 1e3 * dt_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "hiera_stack_512: 128x128 tokens, stages of 2/3/16/3 blocks, D 112/224/448/896",
+                       "batch": 1, "tokens_per_frame": tokens, "parallelism": "none (1 GPU)"},
+            "tflops": flops / dt_step / 1e12, "pct_of_bf16_peak": 100.0 * flops / dt_step / 1e12 / PEAK_BF16_TFLOPS}
+    if with_cpu:
+        from oracle import stack as ost
+        from threadpoolctl import threadpool_info
+        t1 = time.perf_counter()
+        ost.stack_forward(x, blocks, specs, levels, taps)
+        tc = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        line["cpu_baseline"] = {"value": tokens / tc, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                                "sample": "float64 numpy stack oracle, one full 24-block forward, %.1f s" % tc}
+    return line
+
+
 def rowops_cold(steps):
     """HBM bandwidth of the memory-bound kernels on working sets larger than
     the 256 MB Infinity Cache: each launch reads and writes a different one of
@@ -300,6 +349,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=DEFAULT_CONFIG, help="workload name, or 'all'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stack", action="store_true",
+                    help="time the 24-block Hiera stage stack at a 512x512 input instead of one block")
     ap.add_argument("--rowops", action="store_true",
                     help="only time LayerNorm, unroll, reroll and pool4 on HBM-resident working sets")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -314,6 +365,9 @@ def main():
         ap.error("steps >= 1 and warmup >= 0")
     if args.rowops:
         rowops_cold(args.steps)
+        return
+    if args.stack:
+        print(json.dumps(run_stack(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
         return
     if args.copy_calibration:
         copy_calibration(args.steps)

@@ -27,6 +27,11 @@ SMALL = {
                     heads=3, mlp=768),
     "c5w_48x48": d(C["c5w_sam3_win"], grid_h=48, grid_w=48, dim_in=256, dim_out=256, heads=4, mlp=1184),
     "c5g_18x22": d(C["c5g_sam3_global"], grid_h=18, grid_w=22, dim_in=256, dim_out=256, heads=4, mlp=1184),
+    # global attention on V^T from the transpose kernel (qkv projection off
+    # the MFMA path, K = 224): with and without the 2x2 query pool
+    "c3b_pool_global_32": d(C["c3b_hiera_s2"], grid_h=32, grid_w=32, dim_in=224, dim_out=448, q_stride=4),
+    "c4_d224_16x16": d(C["c4_siglip_b8"], batch=2, grid_h=16, grid_w=16, dim_in=224, dim_out=224, heads=4,
+                       mlp=448),
     # 200 keys: V^T path, keys split over two workgroups, ragged last tile
     "c5g_10x20_split": d(C["c5g_sam3_global"], grid_h=10, grid_w=20, dim_in=256, dim_out=256, heads=4, mlp=1024),
     "c5w_f32": d(C["c5w_sam3_win"], grid_h=24, grid_w=48, dim_in=128, dim_out=128, heads=2, mlp=256,
@@ -131,7 +136,7 @@ def test_rerun_is_bitwise_identical():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["c5g_18x22", "c5w_48x48", "c3b_12x12", "c5g_10x20_split"])
+@pytest.mark.parametrize("name", ["c5g_18x22", "c5w_48x48", "c3b_12x12", "c5g_10x20_split", "c4_d224_16x16"])
 def test_forward_equals_forward_seams(name):
     # c5w_48x48 and c3b_12x12 take the V^T attention path, where the plain
     # forward skips qkv's row-layout V and the seams forward writes both

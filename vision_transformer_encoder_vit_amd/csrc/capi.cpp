@@ -59,7 +59,8 @@ struct vit_block_plan {
   size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, off_vt, off_po, off_pml, ws_bytes;
   int attn_splits;       // key splits of the large-window attention (1: none)
   bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
-  bool attn_vt;          // qkv projection also writes V^T for the large-window attention kernel
+  bool attn_vt;          // the large-window attention kernel runs on V^T (workspace off_vt)
+  bool vt_in_gemm;       // ... written by the qkv projection's epilogue (else a transpose kernel)
 };
 
 static vit_status validate_desc(const vit_block_desc* d) {
@@ -148,8 +149,8 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   const int64_t n_q = d.attn_mode == VIT_ATTN_SPATIAL ? (int64_t)d.win_h * d.win_w : p->n_out;
   p->attn_vt = vit::attention_takes_vt(d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32,
                                        d.attn_mode, n_q, p->head_dim, d.win_w, p->n_in,
-                                       p->m_in * 3LL * d.dim_out) &&
-               d.dim_in % 64 == 0;  // the qkv projection on the MFMA path writes V^T
+                                       p->m_in * 3LL * d.dim_out);
+  p->vt_in_gemm = p->attn_vt && d.dim_in % 64 == 0;  // the qkv projection's MFMA path writes V^T
   p->off_vt = p->attn_vt ? take(p->m_in, d.dim_out) : 0;
   p->attn_splits = 1;
   if (p->attn_vt) {
@@ -381,7 +382,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   } else {
     g.epi = vit::EPI_BIAS;
   }
-  if (P.attn_vt) {
+  if (P.vt_in_gemm) {
     g.vt = base + P.off_vt;
     g.vt_col0 = 2 * Do;
     g.vt_tokens = P.n_in;
@@ -389,8 +390,16 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     g.vt_hd = hd;
     g.vt_only = !seams;  // the qkv seam keeps V in row layout too
   }
-  e = vit::launch_gemm(g, dt, s, stage_ev(VIT_STAGE_QKV));
-  if ((st = device_status(e, "gemm (qkv)")) != VIT_OK) return st;
+  if (P.attn_vt && !P.vt_in_gemm) {
+    e = vit::launch_gemm(g, dt, s, only_start(stage_ev(VIT_STAGE_QKV)));
+    if ((st = device_status(e, "gemm (qkv)")) != VIT_OK) return st;
+    e = vit::launch_v_transpose(qkv, 3LL * Do, 2 * Do, base + P.off_vt, d.batch, (int)P.n_in, d.heads, hd, s,
+                                only_stop(stage_ev(VIT_STAGE_QKV)));
+    if ((st = device_status(e, "V transpose")) != VIT_OK) return st;
+  } else {
+    e = vit::launch_gemm(g, dt, s, stage_ev(VIT_STAGE_QKV));
+    if ((st = device_status(e, "gemm (qkv)")) != VIT_OK) return st;
+  }
 
   // 3. residual: x, or pool4(h W_res^T + b_res) at a transition
   const void* r = x;

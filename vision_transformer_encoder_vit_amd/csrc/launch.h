@@ -128,6 +128,10 @@ hipError_t launch_layernorm(const void* x, void* y, const float* g, const float*
                             StageEvents ev = {});
 hipError_t launch_permute(const void* x, void* y, int batch, int grid_h, int grid_w,
                           int levels, int channels, bool inverse, DType dt, hipStream_t s);
+// vt [B, heads, head_dim, tokens] from the V columns (col0 + h*head_dim + d)
+// of qkv rows [B*tokens, ld] (bf16; tokens and head_dim multiples of 8).
+hipError_t launch_v_transpose(const void* qkv, int64_t ld, int col0, void* vt, int batch, int tokens, int heads,
+                              int head_dim, hipStream_t s, StageEvents ev = {});
 hipError_t launch_pool4(const void* x, int64_t x_stride, void* y, int64_t y_stride,
                         int batch, int tokens, int channels, DType dt, hipStream_t s,
                         StageEvents ev = {});

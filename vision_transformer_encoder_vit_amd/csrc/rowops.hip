@@ -236,4 +236,40 @@ hipError_t launch_pool4(const void* x, int64_t xs, void* y, int64_t ys, int batc
   return dt == DType::BF16 ? go(bf16()) : go(float());
 }
 
+// V^T for the large-window attention when the qkv projection cannot write it
+// from its epilogue: vt[b][h][d][t] = qkv[b*T + t][col0 + h*hd + d]. One
+// workgroup per (64 tokens, head, frame): the tile goes through LDS so both
+// the reads (16-byte runs of d) and the writes (16-byte runs of tokens) are
+// full vectors. T % 8 == 0 and hd % 8 == 0, hd <= 64.
+__global__ __launch_bounds__(256) void v_transpose_kernel(const bf16* __restrict__ qkv, int64_t ld, int col0,
+                                                          bf16* __restrict__ vt, int T, int heads, int hd) {
+  constexpr int TT = 64, ROW = 64 + 8;  // tile tokens; LDS row (elements)
+  __shared__ __attribute__((aligned(16))) bf16 tile[TT * ROW];
+  const int t0 = blockIdx.x * TT, h = blockIdx.y, b = blockIdx.z;
+  const int nch = hd / 8;
+  for (int e = threadIdx.x; e < TT * nch; e += 256) {
+    const int t = e / nch, c = e - t * nch;
+    if (t0 + t < T)
+      st16(tile + t * ROW + c * 8, ld16(qkv + ((int64_t)b * T + t0 + t) * ld + col0 + h * hd + c * 8));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < hd * (TT / 8); e += 256) {
+    const int d = e / (TT / 8), tc = e - d * (TT / 8);
+    if (t0 + tc * 8 >= T) continue;
+    bf16 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = tile[(tc * 8 + k) * ROW + d];
+    st16(vt + (((int64_t)b * heads + h) * hd + d) * T + t0 + tc * 8, *reinterpret_cast<const u32x4*>(v));
+  }
+}
+
+hipError_t launch_v_transpose(const void* qkv, int64_t ld, int col0, void* vt, int batch, int tokens, int heads,
+                              int head_dim, hipStream_t s, StageEvents ev) {
+  if (batch == 0 || tokens == 0) return hipSuccess;
+  dim3 grid((unsigned)((tokens + 63) / 64), (unsigned)heads, (unsigned)batch);
+  hipExtLaunchKernelGGL(v_transpose_kernel, grid, dim3(256), 0, s, ev.start, ev.stop, 0, (const bf16*)qkv, ld, col0,
+                        (bf16*)vt, tokens, heads, head_dim);
+  return hipGetLastError();
+}
+
 }  // namespace vit
