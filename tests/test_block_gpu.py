@@ -7,6 +7,7 @@ import torch
 from oracle import block as ob
 from oracle import index_maps as im
 from tests import gpu_util as gu
+from vision_transformer_encoder_vit_amd import binding as vb
 from vision_transformer_encoder_vit_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -269,3 +270,33 @@ def test_fused_agrees_with_stepwise_and_in_place():
     x = dev["x"].clone()
     gu.run_block(spec, dev, seams=False, x=x, out=x)
     assert torch.equal(x.view(torch.int16), y_fused.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["c2_32x32", "c5g_10x20_split"])
+def test_forward_is_graph_capturable(name):
+    # the forward allocates nothing and never synchronises, so it can be
+    # captured into a HIP graph; every replay (with eager work and
+    # synchronisation between them) equals the eager result bit for bit
+    spec = SMALL[name]
+    print("case", name, flush=True)
+    dev = gu.to_device(synth.make_inputs(spec, seed=0), spec)
+    y_eager, _ = gu.run_block(spec, dev, seams=False)
+    plan = vb.Plan(vb.desc_from_spec(spec))
+    w = vb.weights_struct(dev)
+    y = torch.empty_like(y_eager)
+    ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        plan.forward(w, dev["x"], y, ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        plan.forward(w, dev["x"], y, ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), i
+    plan.close()
