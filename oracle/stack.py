@@ -13,6 +13,11 @@ Each 2x2 pooling consumes one level of the unrolled order (the pooled order
 is the (L-1)-level unroll of the half-size grid, see ``index_maps``), so a
 feature map taken after k transitions is rerolled with L - k levels.
 
+A tower without unrolling (levels 0) is the same loop: the SAM3 trunk runs
+its LayerNorm ``ln_pre`` and then the blocks (SAM3 page, trunk block loop);
+the SigLIP tower runs the blocks and then ``post_layernorm`` (SigLIP page,
+``forward_frame``) -- ``tower_forward``.
+
 Pins (tests/test_oracle.py): the 512x512 shape contract of the plan
 ("Sub-phase 4d": 128x128x112, 64x64x224, 32x32x448, 16x16x896); a stack of
 global blocks without pooling equals the same blocks on raster-order tokens
@@ -41,3 +46,15 @@ def stack_forward(x, blocks, specs, levels, taps):
         if i in taps:
             feats.append(im.reroll(t, H, W, levels))
     return feats
+
+
+def tower_forward(x, blocks, specs, pre_ln=None, post_ln=None, eps=1e-6):
+    """Blocks applied in order to raster-order tokens, with an optional
+    LayerNorm (gamma, beta) before the first block and after the last."""
+    t = np.asarray(x, dtype=np.float64)
+    if pre_ln is not None:
+        t = ob.layer_norm(t, np.asarray(pre_ln[0], dtype=np.float64), np.asarray(pre_ln[1], dtype=np.float64), eps)
+    (t,) = stack_forward(t, blocks, specs, 0, [len(specs) - 1])
+    if post_ln is not None:
+        t = ob.layer_norm(t, np.asarray(post_ln[0], dtype=np.float64), np.asarray(post_ln[1], dtype=np.float64), eps)
+    return t

@@ -435,3 +435,29 @@ def test_stack_pooled_features_independent_of_unroll_depth():
     t = im.unroll(x.astype(np.float64), 16, 16, 2)
     r = ob.block_forward(t, blocks[0], sp)["r"]
     np.testing.assert_allclose(im.reroll(r, 8, 8, 1)[0], pooled, rtol=1e-12, atol=1e-12)
+
+
+def test_sam3_trunk_windows_stay_local_until_a_global_layer():
+    # windowed layers never mix 24x24 windows, through any number of layers:
+    # changing one token of window 0 leaves every other window's output
+    # unchanged, exactly; one global layer spreads it everywhere
+    from oracle import stack as ost
+    specs = synth.sam3_trunk(grid=48, layers=3, global_layers=(), dim=64, heads=2, mlp=128)
+    specs = [synth.derive(s, dtype="f32") for s in specs]
+    x, blocks = synth.make_stack_inputs(specs, seed=11)
+    g, b = synth.make_layernorm_params(64, 11)
+    y0 = ost.tower_forward(x, blocks, specs, pre_ln=(g, b))
+    x2 = x.copy()
+    x2[0, 5 * 48 + 7, 3] += 1.0  # token (5, 7): window (0, 0); one channel (a uniform shift is what LN removes)
+    y1 = ost.tower_forward(x2, blocks, specs, pre_ln=(g, b))
+    win = np.zeros(48 * 48, dtype=bool)
+    for t in range(48 * 48):
+        win[t] = (t // 48) < 24 and (t % 48) < 24
+    assert np.abs(y1[0, win] - y0[0, win]).max() > 1e-3
+    assert np.array_equal(y1[0, ~win], y0[0, ~win])
+    specs_g = synth.sam3_trunk(grid=48, layers=3, global_layers=(1,), dim=64, heads=2, mlp=128)
+    specs_g = [synth.derive(s, dtype="f32") for s in specs_g]
+    _, blocks_g = synth.make_stack_inputs(specs_g, seed=11)
+    z0 = ost.tower_forward(x, blocks_g, specs_g, pre_ln=(g, b))
+    z1 = ost.tower_forward(x2, blocks_g, specs_g, pre_ln=(g, b))
+    assert np.all(np.abs(z1[0] - z0[0]).max(axis=-1) > 0)

@@ -83,3 +83,52 @@ def test_stack_equals_chained_single_calls():
             torch.cuda.synchronize()
             assert torch.equal(f.view(torch.int16), feats[k].view(torch.int16)), i
             k += 1
+
+
+def _tower_gpu(specs, x, blocks, pre_ln=None, post_ln=None):
+    """vit_layernorm (ln_pre) -> vit_stack (levels 0, one tap) -> vit_layernorm (post_ln)."""
+    dt = gu.torch_dtype(specs[0])
+    dev_w = [gu.to_device(w, sp) for w, sp in zip(blocks, specs)]
+    weights = [vb.weights_struct(w) for w in dev_w]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(dt).cuda()
+    if pre_ln is not None:
+        g, b = (torch.from_numpy(a).cuda() for a in pre_ln)
+        vb.vit_layernorm(xd, xd, g, b, specs[0]["eps"])
+    st = vb.Stack([vb.desc_from_spec(s) for s in specs], 0, [len(specs) - 1])
+    last = specs[-1]
+    y = torch.empty((last["batch"], synth.out_tokens(last), last["dim_out"]), dtype=dt, device="cuda")
+    ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+    st.forward(weights, xd, [y], ws)
+    if post_ln is not None:
+        g, b = (torch.from_numpy(a).cuda() for a in post_ln)
+        vb.vit_layernorm(y, y, g, b, last["eps"])
+    torch.cuda.synchronize()
+    st.close()
+    return gu.to64(y)
+
+
+def _tower_gate(name, got, want):
+    a, b = got.ravel(), want.ravel()
+    cos = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+    nrel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    print("%s: cos %.7f norm-rel %.2e max-rel %.2e" % (name, cos, nrel, np.abs(a - b).max() / np.abs(b).max()))
+    assert np.all(np.isfinite(got)) and cos >= 0.9999 and nrel <= 2e-2, (name, cos, nrel)
+
+
+def test_sam3_trunk_reduced_vs_oracle():
+    # ln_pre, then windowed layers with in-window RoPE and two global layers
+    # with grid RoPE (the SAM3 trunk pattern at 48x48 tokens, width 256)
+    specs = synth.sam3_trunk(grid=48, layers=8, global_layers=(3, 7), dim=256, heads=4, mlp=1024)
+    x, blocks = synth.make_stack_inputs(specs, seed=2)
+    ln = synth.make_layernorm_params(256, 2)
+    got = _tower_gpu(specs, x, blocks, pre_ln=ln)
+    _tower_gate("sam3 trunk 8 layers", got, ost.tower_forward(x, blocks, specs, pre_ln=ln))
+
+
+def test_siglip_tower_full_frame_vs_oracle():
+    # the SigLIP tower at full size for one frame: 12 blocks + post_layernorm
+    specs = synth.siglip_tower(batch=1)
+    x, blocks = synth.make_stack_inputs(specs, seed=3)
+    ln = synth.make_layernorm_params(768, 3)
+    got = _tower_gpu(specs, x, blocks, post_ln=ln)
+    _tower_gate("siglip tower 12 layers", got, ost.tower_forward(x, blocks, specs, post_ln=ln))

@@ -216,6 +216,39 @@ def make_stack_inputs(specs, seed=0):
     return x, blocks
 
 
+# SAM3 ViT trunk (SAM3 page, trunk constants and block loop): LayerNorm
+# ln_pre, then 32 blocks of width 1024, 16 heads, MLP 4736, 24x24 windows
+# with in-window RoPE except layers 7, 15, 23, 31 (global, grid RoPE).
+SAM3_GLOBAL_LAYERS = (7, 15, 23, 31)
+
+
+def sam3_trunk(grid=72, win=24, layers=32, global_layers=SAM3_GLOBAL_LAYERS, dim=1024, heads=16, mlp=4736):
+    """Block specs of a SAM3-style trunk (ln_pre comes before block 0)."""
+    specs = []
+    for l in range(layers):
+        base = CONFIGS["c5g_sam3_global"] if l in global_layers else CONFIGS["c5w_sam3_win"]
+        kw = dict(name="sam3_l%d" % l, grid_h=grid, grid_w=grid, dim_in=dim, dim_out=dim, heads=heads, mlp=mlp)
+        if l not in global_layers:
+            kw.update(win_h=win, win_w=win)
+        specs.append(derive(base, **kw))
+    return specs
+
+
+# SigLIP tower (SigLIP page, ``forward_frame``): 12 pre-LN blocks of width 768,
+# then the final post_layernorm; frames batched.
+def siglip_tower(batch=8, grid=32, layers=12, dim=768, heads=12, mlp=3072):
+    return [derive(CONFIGS["c4_siglip_b8"], name="siglip_l%d" % l, batch=batch, grid_h=grid, grid_w=grid,
+                   dim_in=dim, dim_out=dim, heads=heads, mlp=mlp) for l in range(layers)]
+
+
+def make_layernorm_params(dim, seed):
+    """gamma 1 + N(0, 0.1), beta N(0, 0.1) (as the blocks' LayerNorms), float32;
+    streams keyed by (seed, 100) and (seed, 101)."""
+    g = 1.0 + np.random.default_rng([seed, 100]).normal(0.0, 0.1, (dim,))
+    b = np.random.default_rng([seed, 101]).normal(0.0, 0.1, (dim,))
+    return g.astype(np.float32), b.astype(np.float32)
+
+
 def out_tokens(spec):
     """Tokens per frame leaving the block (4x fewer at a pooled transition)."""
     return spec["grid_h"] * spec["grid_w"] // spec["q_stride"]
