@@ -242,15 +242,30 @@ def copy_calibration(steps):
                       "copy_bytes_written_per_launch": COPY_ROWS * COPY_COLS * 2, "launches": steps}))
 
 
-def run_stack(steps, warmup, with_cpu):
-    """The Hiera stage stack at a 512x512 input (128x128 tokens, 24 blocks,
-    features rerolled after blocks 1, 4, 20 and 23) through vit_stack_forward:
+TOWERS = {
+    "hiera": "Hiera stage stack at a 512x512 input: 128x128 tokens, 24 blocks (stages of 2/3/16/3, D 112..896), "
+             "features after blocks 1, 4, 20, 23",
+    "sam3": "SAM3 trunk: ln_pre + 32 blocks on 72x72 tokens, D 1024, 24x24 windows, global layers 7/15/23/31",
+    "siglip": "SigLIP tower: 8 frames x 32x32 tokens, 12 blocks D 768 + post_layernorm",
+}
+
+
+def run_tower(kind, steps, warmup, with_cpu):
+    """A chain of blocks through vit_stack_forward (plus the LayerNorm before
+    (SAM3 ln_pre) or after (SigLIP post_layernorm) it through vit_layernorm):
     K event-free forwards timed like the block workload."""
     import numpy as np
     import torch
     from vision_transformer_encoder_vit_amd import binding as vb
     from vision_transformer_encoder_vit_amd import synth, work
-    specs, levels, taps = synth.hiera_stack()
+    pre = post = None
+    if kind == "hiera":
+        specs, levels, taps = synth.hiera_stack()
+    else:
+        specs = synth.sam3_trunk() if kind == "sam3" else synth.siglip_tower()
+        levels, taps = 0, [len(specs) - 1]
+        ln = synth.make_layernorm_params(specs[0]["dim_in"], 0)
+        pre, post = (ln, None) if kind == "sam3" else (None, ln)
     x, blocks = synth.make_stack_inputs(specs, seed=0)
     dt = torch.bfloat16
     dev_w = []
@@ -259,35 +274,57 @@ def run_stack(steps, warmup, with_cpu):
                           else torch.from_numpy(np.ascontiguousarray(a))).cuda() for k, a in w.items()})
     weights = [vb.weights_struct(w) for w in dev_w]
     xd = torch.from_numpy(x).to(dt).cuda()
+    xin = torch.empty_like(xd)
     st = vb.Stack([vb.desc_from_spec(s) for s in specs], levels, taps)
-    feats = [torch.empty((1, synth.out_tokens(specs[t]), specs[t]["dim_out"]), dtype=dt, device="cuda") for t in taps]
+    feats = [torch.empty((specs[t]["batch"], synth.out_tokens(specs[t]), specs[t]["dim_out"]), dtype=dt,
+                         device="cuda") for t in taps]
     ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+    lnd = lambda p: tuple(torch.from_numpy(a).cuda() for a in p) if p is not None else None
+    pre_d, post_d = lnd(pre), lnd(post)
+
+    def forward():
+        src = xd
+        if pre_d is not None:
+            vb.vit_layernorm(xd, xin, pre_d[0], pre_d[1], specs[0]["eps"])
+            src = xin
+        st.forward(weights, src, feats, ws)
+        if post_d is not None:
+            vb.vit_layernorm(feats[-1], feats[-1], post_d[0], post_d[1], specs[-1]["eps"])
+
     for _ in range(warmup):
-        st.forward(weights, xd, feats, ws)
+        forward()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        st.forward(weights, xd, feats, ws)
+        forward()
     torch.cuda.synchronize()
     dt_step = (time.perf_counter() - t0) / steps
     st.close()
     flops = sum(work.block_flops(s) for s in specs)
-    tokens = specs[0]["grid_h"] * specs[0]["grid_w"]
-    line = {"metric": "Hiera stage stack (24 blocks, 512x512 input) input tokens/sec, 1 GPU", "value": tokens / dt_step,
+    tokens = specs[0]["batch"] * specs[0]["grid_h"] * specs[0]["grid_w"]
+    line = {"metric": "%s tower input tokens/sec, 1 GPU" % kind, "value": tokens / dt_step,
             "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": 1e3 * dt_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "hiera_stack_512: 128x128 tokens, stages of 2/3/16/3 blocks, D 112/224/448/896",
-                       "batch": 1, "tokens_per_frame": tokens, "parallelism": "none (1 GPU)"},
+            "config": {"workload": TOWERS[kind], "batch": specs[0]["batch"],
+                       "tokens_per_frame": specs[0]["grid_h"] * specs[0]["grid_w"], "parallelism": "none (1 GPU)"},
             "tflops": flops / dt_step / 1e12, "pct_of_bf16_peak": 100.0 * flops / dt_step / 1e12 / PEAK_BF16_TFLOPS}
-    if with_cpu:
+    if with_cpu and kind in ("hiera", "siglip"):
+        # the float64 oracle on one frame (SigLIP: frame 0 of the 8; the
+        # SAM3 trunk's 32 full-size layers would take minutes and is skipped)
         from oracle import stack as ost
         from threadpoolctl import threadpool_info
+        one = [synth.derive(s, batch=1) for s in specs]
         t1 = time.perf_counter()
-        ost.stack_forward(x, blocks, specs, levels, taps)
+        if kind == "hiera":
+            ost.stack_forward(x[:1], blocks, one, levels, taps)
+        else:
+            ost.tower_forward(x[:1], blocks, one, post_ln=post)
         tc = time.perf_counter() - t1
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-        line["cpu_baseline"] = {"value": tokens / tc, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-                                "sample": "float64 numpy stack oracle, one full 24-block forward, %.1f s" % tc}
+        n1 = one[0]["grid_h"] * one[0]["grid_w"]
+        line["cpu_baseline"] = {"value": n1 / tc, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                                "sample": "float64 numpy oracle, the whole chain on one frame (%d tokens), %.1f s"
+                                          % (n1, tc)}
     return line
 
 
@@ -349,8 +386,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=DEFAULT_CONFIG, help="workload name, or 'all'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stack", action="store_true",
-                    help="time the 24-block Hiera stage stack at a 512x512 input instead of one block")
+    ap.add_argument("--tower", choices=sorted(TOWERS),
+                    help="time a chain of blocks (hiera: the 24-block stage stack at 512x512; sam3: the 32-layer "
+                         "trunk; siglip: the 12-layer tower) instead of one block")
     ap.add_argument("--rowops", action="store_true",
                     help="only time LayerNorm, unroll, reroll and pool4 on HBM-resident working sets")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -366,8 +404,8 @@ def main():
     if args.rowops:
         rowops_cold(args.steps)
         return
-    if args.stack:
-        print(json.dumps(run_stack(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
+    if args.tower:
+        print(json.dumps(run_tower(args.tower, args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
         return
     if args.copy_calibration:
         copy_calibration(args.steps)

@@ -246,6 +246,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
+
+  // Warm the memory-side cache with the whole weight matrix before the first
+  // tile: one 4-byte read per 128-byte line, dealt to the threads of the
+  // first workgroups. In a chain of blocks each block's weights were last
+  // read many blocks ago and sit in HBM; without this every K step of every
+  // tile waits on an HBM miss for its W panel, with it the misses overlap
+  // the prologue and later W reads hit the Infinity Cache. The value is
+  // consumed only by a store that never happens (M >= 1 always).
+  uint32_t touch = 0;
+  {
+    const int lines_per_row = p.K / 64;
+    const int64_t lines = (int64_t)p.N * lines_per_row;
+    for (int64_t g = (int64_t)blockIdx.x * NT + tid; g < lines; g += (int64_t)gridDim.x * NT) {
+      const int n = (int)(g / lines_per_row), kl = (int)(g - (int64_t)n * lines_per_row);
+      const int seg = n / p.seg_cols;
+      const bf16* base = seg == 0 ? p.W0 : (seg == 1 ? p.W1 : p.W2);
+      touch ^= *reinterpret_cast<const uint32_t*>(base + (int64_t)(n - seg * p.seg_cols) * p.K + kl * 64);
+    }
+  }
+
   int tmi, tni;
   xcd_tile<8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tmi, tni);
   const int m0 = tmi * BM, n0 = tni * BN;
@@ -441,6 +461,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       st16(p.C + (int64_t)m * p.ldc + n, pack16<bf16>(v));
     }
   }
+  if (p.M <= 0 && touch == 0x5EEDu) p.C[0] = bf16(0.f);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2>
