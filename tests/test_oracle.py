@@ -461,3 +461,113 @@ def test_sam3_trunk_windows_stay_local_until_a_global_layer():
     z0 = ost.tower_forward(x, blocks_g, specs_g, pre_ln=(g, b))
     z1 = ost.tower_forward(x2, blocks_g, specs_g, pre_ln=(g, b))
     assert np.all(np.abs(z1[0] - z0[0]).max(axis=-1) > 0)
+
+
+# ---------------------------------------------------------------- patch-embedding stems
+
+def _stem_small(kind, **kw):
+    spec = dict(synth.STEMS[kind])
+    spec.update(kw)
+    return spec
+
+
+@pytest.mark.parametrize("kind,kw", [
+    ("hiera", dict(batch=2, in_h=30, in_w=26)),            # k7 s4 p3, NHWC, OHWI, ragged
+    ("siglip", dict(batch=2, in_h=64, in_w=48, pos_side=4)),  # k16 s16, NCHW
+    ("sam3", dict(in_h=70, in_w=56, pos_side=3)),          # k14 s14, no bias
+])
+def test_stem_conv_matches_torch(kind, kw):
+    # the convolution against torch's conv2d (float64, CPU), the pixels and
+    # weights brought to NCHW / OIHW by torch's own permute
+    from oracle import stem
+    spec = _stem_small(kind, dtype="f32", pos_mode="none", **kw)
+    inp = synth.make_stem_inputs(spec, seed=5)
+    P = torch.from_numpy(inp["pixels"]).double()
+    W = torch.from_numpy(inp["weight"]).double()
+    if spec["layout"] == "nhwc":
+        P = P.permute(0, 3, 1, 2)
+    if spec["weight_layout"] == "ohwi":
+        W = W.permute(0, 3, 1, 2)
+    b = torch.from_numpy(inp["bias"]).double() if spec["bias"] else None
+    ref = torch.nn.functional.conv2d(P, W, b, stride=spec["stride"], padding=spec["pad"])
+    B, O, oh, ow = ref.shape
+    assert (oh, ow) == synth.stem_out_grid(spec)
+    got = stem.patch_embed(inp, spec)
+    np.testing.assert_allclose(got, ref.reshape(B, O, oh * ow).permute(0, 2, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["hiera", "siglip"])
+def test_stem_one_hot_weight_selects_the_pixel(kind):
+    # a weight with a single 1 at (o, c, ky, kx) copies pixel
+    # (c, y*s + ky - p, x*s + kx - p) into channel o of token (y, x), zero
+    # where that falls in the padding; a transposed layout or a flipped
+    # kernel picks another pixel
+    from oracle import stem
+    spec = _stem_small(kind, batch=1, in_h=21, in_w=19, dim=3, pos_mode="none", bias=False, dtype="f32")
+    inp = synth.make_stem_inputs(spec, seed=6)
+    C, k, s, p = spec["in_ch"], spec["kernel"], spec["stride"], spec["pad"]
+    P = inp["pixels"][0] if spec["layout"] == "nchw" else inp["pixels"][0].transpose(2, 0, 1)
+    oh, ow = synth.stem_out_grid(spec)
+    for (o, c, ky, kx) in [(0, 0, 0, 0), (1, C - 1, k - 1, 2), (2, 1, 3, k - 1)]:
+        w = np.zeros(inp["weight"].shape, dtype=np.float32)
+        if spec["weight_layout"] == "oihw":
+            w[o, c, ky, kx] = 1.0
+        else:
+            w[o, ky, kx, c] = 1.0
+        got = stem.patch_embed(dict(inp, weight=w), spec)[0]
+        for y in range(oh):
+            for x in range(ow):
+                py, px = y * s + ky - p, x * s + kx - p
+                want = P[c, py, px] if 0 <= py < P.shape[1] and 0 <= px < P.shape[2] else 0.0
+                assert got[y * ow + x, o] == want
+                assert np.all(got[y * ow + x, [i for i in range(3) if i != o]] == 0.0)
+
+
+def test_stem_shape_contracts():
+    # 512^2 -> 128^2 Hiera tokens (the first stage grid of the plan's shape
+    # table), 512^2 -> 32^2 = 1024 SigLIP tokens, 1008^2 -> 72^2 SAM3 tokens
+    rows = np.loadtxt(os.path.join(GOLDEN, "hiera_stage_shapes.txt"), dtype=np.int64)
+    assert synth.stem_out_grid(synth.STEMS["hiera"]) == (rows[0][1], rows[0][1])
+    assert synth.STEMS["hiera"]["dim"] == rows[0][2]
+    assert synth.stem_out_grid(synth.STEMS["siglip"]) == (32, 32)
+    assert synth.stem_out_grid(synth.STEMS["sam3"]) == (72, 72)
+    # and the towers the stems feed start from those grids
+    assert synth.hiera_stack()[0][0]["grid_h"] == 128
+    assert synth.siglip_tower()[0]["grid_h"] * synth.siglip_tower()[0]["grid_w"] == 1024
+    assert synth.sam3_trunk()[0]["grid_h"] == 72
+
+
+def test_siglip_pos_buckets_as_printed():
+    from oracle import stem
+    fx = np.loadtxt(os.path.join(GOLDEN, "siglip_pos_buckets.txt"), dtype=np.int64)
+    rows = stem.pos_rows(32, 32, "bucket", 32)
+    y, x = np.divmod(np.arange(1024), 32)
+    np.testing.assert_array_equal(rows, fx[y, 1] * 32 + fx[x, 1])
+
+
+def test_siglip_pos_buckets_follow_the_bucketize_procedure():
+    # the procedure the SigLIP page describes: fractional coordinates
+    # (i / 32) * (1 - 1e-6) in float32, bucketized against the boundaries
+    # j / 32 (j = 1..31) with right=True (index of the first boundary > value)
+    from oracle import stem
+    n = 32
+    frac = (np.arange(n, dtype=np.float32) / np.float32(n)) * np.float32(1 - 1e-6)
+    bounds = np.arange(1, n, dtype=np.float32) / np.float32(n)
+    b = np.searchsorted(bounds, frac, side="right")
+    y, x = np.divmod(np.arange(n * n), n)
+    np.testing.assert_array_equal(stem.pos_rows(n, n, "bucket", n), b[y] * n + b[x])
+
+
+def test_sam3_pos_table_tiles_the_grid():
+    # zero weights: every token is its table row; the 72x72 grid repeats the
+    # 24x24 table with period 24 on both axes, and the first 24x24 block is
+    # the table in raster order
+    from oracle import stem
+    spec = dict(synth.STEMS["sam3"])
+    inp = synth.make_stem_inputs(spec, seed=7)
+    inp["weight"] = np.zeros_like(inp["weight"])
+    out = stem.patch_embed(inp, spec)[0].reshape(72, 72, 1024)
+    pos = inp["pos"].astype(np.float64).reshape(24, 24, 1024)
+    np.testing.assert_array_equal(out[:24, :24], pos)
+    np.testing.assert_array_equal(out[24:, :], out[:-24, :])
+    np.testing.assert_array_equal(out[:, 24:], out[:, :-24])

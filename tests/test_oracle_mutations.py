@@ -111,6 +111,61 @@ MUTATIONS = [
 ]
 
 
+from oracle import stem as ostem  # noqa: E402
+
+_orig_conv2d = ostem.conv2d
+
+
+def _weight_layout_ignored(weight, layout):
+    # reads an OHWI weight as if it were OIHW (a reshape, no transpose)
+    w = np.asarray(weight, dtype=np.float64)
+    return w.reshape(w.shape[0], w.shape[3], w.shape[1], w.shape[2])
+
+
+def _conv_flipped(P, w, stride, pad):
+    # true convolution (kernel flipped) instead of the cross-correlation
+    return _orig_conv2d(P, w[:, :, ::-1, ::-1], stride, pad)
+
+
+def _conv_pad_one_side(P, w, stride, pad):
+    # zero padding only after the image instead of around it
+    B, C, H, W = P.shape
+    Pp = np.zeros((B, C, H + pad, W + pad))
+    Pp[:, :, :H, :W] = P
+    return _orig_conv2d(Pp, w, stride, 0)[:, :, :(H + 2 * pad - w.shape[2]) // stride + 1,
+                                          :(W + 2 * pad - w.shape[3]) // stride + 1]
+
+
+def _bucket_identity(out_h, out_w, mode, side):
+    y, x = np.divmod(np.arange(out_h * out_w), out_w)
+    if mode == "bucket":
+        return y * side + x
+    return _orig_pos_rows(out_h, out_w, mode, side)
+
+
+def _tile_by_block(out_h, out_w, mode, side):
+    y, x = np.divmod(np.arange(out_h * out_w), out_w)
+    if mode == "tile":
+        return (y // (out_h // side)) * side + x // (out_w // side)
+    return _orig_pos_rows(out_h, out_w, mode, side)
+
+
+_orig_pos_rows = ostem.pos_rows
+
+MUTATIONS += [
+    ("stem OHWI weight read as OIHW", ostem, "weight_oihw", _weight_layout_ignored,
+     lambda: pins.test_stem_conv_matches_torch("hiera", dict(batch=2, in_h=30, in_w=26))),
+    ("stem kernel flipped", ostem, "conv2d", _conv_flipped,
+     lambda: pins.test_stem_one_hot_weight_selects_the_pixel("siglip")),
+    ("stem padding on one side", ostem, "conv2d", _conv_pad_one_side,
+     lambda: pins.test_stem_conv_matches_torch("hiera", dict(batch=2, in_h=30, in_w=26))),
+    ("siglip bucket as identity", ostem, "pos_rows", _bucket_identity, pins.test_siglip_pos_buckets_as_printed),
+    ("siglip bucket as identity (procedure)", ostem, "pos_rows", _bucket_identity,
+     pins.test_siglip_pos_buckets_follow_the_bucketize_procedure),
+    ("sam3 table stretched instead of tiled", ostem, "pos_rows", _tile_by_block, pins.test_sam3_pos_table_tiles_the_grid),
+]
+
+
 @pytest.mark.parametrize("label,mod,attr,bad,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(monkeypatch, label, mod, attr, bad, pin):
     monkeypatch.setattr(mod, attr, bad)

@@ -252,3 +252,66 @@ def make_layernorm_params(dim, seed):
 def out_tokens(spec):
     """Tokens per frame leaving the block (4x fewer at a pooled transition)."""
     return spec["grid_h"] * spec["grid_w"] // spec["q_stride"]
+
+
+# Patch-embedding stems: the step that turns pixels into the token grid the
+# blocks consume. Hiera (Hiera plan, "Architecture Summary"): 4-channel NHWC
+# pixels, Conv2d 4 -> 112, 7x7, stride 4 (padding 3, the one that keeps the
+# 512 -> 128 shape contract symmetric), weight stored (112, 7, 7, 4), plus a
+# learned position table of one row per token. SigLIP (SigLIP page,
+# ``embed_frame``): NCHW frames, Conv 3 -> 768, 16x16, stride 16 with bias,
+# plus a 32x32 position table looked up by bucketized coordinates. SAM3
+# (SAM3 page, trunk patch step): 3 x 1008 x 1008, Conv 3 -> 1024, 14x14,
+# stride 14 without bias, plus a 24x24 table tiled over the 72x72 grid.
+STEMS = {
+    "hiera": dict(name="hiera_stem", batch=1, in_h=512, in_w=512, in_ch=4, layout="nhwc", kernel=7, stride=4,
+                  pad=3, dim=112, weight_layout="ohwi", bias=True, pos_mode="rows", pos_side=0, dtype="bf16"),
+    "siglip": dict(name="siglip_stem", batch=8, in_h=512, in_w=512, in_ch=3, layout="nchw", kernel=16, stride=16,
+                   pad=0, dim=768, weight_layout="oihw", bias=True, pos_mode="bucket", pos_side=32, dtype="bf16"),
+    "sam3": dict(name="sam3_stem", batch=1, in_h=1008, in_w=1008, in_ch=3, layout="nchw", kernel=14, stride=14,
+                 pad=0, dim=1024, weight_layout="oihw", bias=False, pos_mode="tile", pos_side=24, dtype="bf16"),
+}
+
+_STEM_IDS = {"pixels": 40, "weight": 41, "bias": 42, "pos": 43}
+
+
+def stem_out_grid(spec):
+    """(out_h, out_w) of the convolution: floor((in + 2 pad - kernel) / stride) + 1."""
+    k, s, p = spec["kernel"], spec["stride"], spec["pad"]
+    return (spec["in_h"] + 2 * p - k) // s + 1, (spec["in_w"] + 2 * p - k) // s + 1
+
+
+def stem_shapes(spec):
+    B, C, k, D = spec["batch"], spec["in_ch"], spec["kernel"], spec["dim"]
+    oh, ow = stem_out_grid(spec)
+    pix = (B, C, spec["in_h"], spec["in_w"]) if spec["layout"] == "nchw" else (B, spec["in_h"], spec["in_w"], C)
+    w = (D, C, k, k) if spec["weight_layout"] == "oihw" else (D, k, k, C)
+    rows = oh * ow if spec["pos_mode"] == "rows" else spec["pos_side"] ** 2
+    shapes = {"pixels": pix, "weight": w, "pos": (rows, D)}
+    if spec["bias"]:
+        shapes["bias"] = (D,)
+    if spec["pos_mode"] == "none":
+        del shapes["pos"]
+    return shapes
+
+
+def make_stem_inputs(spec, seed=0):
+    """Pixels U(-1, 1) (the normalised range the towers feed), weight
+    N(0, 0.02), bias N(0, 0.01), position table N(0, 0.02); float32, with
+    pixels and weight rounded to bf16 for the bf16 stems."""
+    out = {}
+    for name, shape in stem_shapes(spec).items():
+        rng = np.random.default_rng([seed, _STEM_IDS[name]])
+        if name == "pixels":
+            a = rng.uniform(-1.0, 1.0, shape)
+        elif name == "weight":
+            a = rng.normal(0.0, 0.02, shape)
+        elif name == "bias":
+            a = rng.normal(0.0, 0.01, shape)
+        else:
+            a = rng.normal(0.0, 0.02, shape)
+        a = a.astype(np.float32)
+        if spec["dtype"] == "bf16" and name in ("pixels", "weight"):
+            a = bf16_round(a)
+        out[name] = a
+    return out
