@@ -295,6 +295,65 @@ vit_status vit_pool4(const void* x, int64_t x_row_stride, void* y,
                      int64_t y_row_stride, int32_t batch, int32_t tokens,
                      int32_t channels, int32_t dtype, void* stream);
 
+/* ---- patch-embedding stems (the step that makes the token grid) ----
+ *
+ *   tokens[b, y*out_w + x, o] = bias[o] + pos[row(y, x), o]
+ *       + sum_{c,ky,kx} w[o, c, ky, kx] * P[b, c, y*stride + ky - pad, x*stride + kx - pad]
+ *
+ * with P zero outside the image and out_h = (in_h + 2 pad - kernel) / stride
+ * + 1 (likewise out_w). Sources: the Hiera plan ("Architecture Summary":
+ * PatchEmbed Conv2d 4->112, 7x7, stride 4, then the learned pos_embed, one
+ * row per token); the SigLIP page (`embed_frame`: Conv 3->768, 16x16, stride
+ * 16, with bias, then position rows from bucketized patch coordinates); the
+ * SAM3 page (trunk: Conv 3->1024, 14x14, stride 14, no bias, then a 24x24
+ * position table tiled over the 72x72 grid; its ln_pre is vit_layernorm).
+ */
+enum { VIT_PIXELS_NCHW = 0, VIT_PIXELS_NHWC = 1 };
+enum { VIT_CONV_OIHW = 0, VIT_CONV_OHWI = 1 };
+/* Position-table row of output token (y, x):
+ *   ROWS    y*out_w + x   (table [out_h*out_w, dim])
+ *   BUCKET  max(y-1,0)*pos_side + max(x-1,0)   (table [pos_side^2, dim];
+ *           the SigLIP NaViT bucketize at the full-mask geometry, where
+ *           coordinates 0 and 1 share bucket 0; needs out_h = out_w = pos_side)
+ *   TILE    (y mod pos_side)*pos_side + (x mod pos_side)   (table [pos_side^2, dim]) */
+enum { VIT_POS_NONE = 0, VIT_POS_ROWS = 1, VIT_POS_BUCKET = 2, VIT_POS_TILE = 3 };
+
+typedef struct vit_patch_embed_desc {
+  int32_t batch;          /* frames >= 1                                    */
+  int32_t in_h, in_w;     /* pixel grid                                     */
+  int32_t in_ch;          /* channels C, 1..64 (3 RGB; 4 for Hiera)          */
+  int32_t pixel_layout;   /* VIT_PIXELS_NCHW [B, C, H, W] or _NHWC [B, H, W, C] */
+  int32_t kernel;         /* square kernel k, 1..32                         */
+  int32_t stride;         /* >= 1                                           */
+  int32_t pad;            /* zero padding on every side, 0 <= pad < kernel  */
+  int32_t dim;            /* output channels, a multiple of 8, <= 8192      */
+  int32_t weight_layout;  /* VIT_CONV_OIHW [dim, C, k, k] or _OHWI [dim, k, k, C] */
+  int32_t pos_mode;       /* VIT_POS_*                                      */
+  int32_t pos_side;       /* BUCKET and TILE: side of the square table      */
+  int32_t act_dtype;      /* dtype of weight and tokens: VIT_DTYPE_F32 or _BF16 */
+} vit_patch_embed_desc;
+
+/* Bytes of device workspace vit_patch_embed needs for `desc` (the gathered
+ * [B*out_h*out_w, K] pixel matrix, K = C*k*k padded to a multiple of 64, and
+ * the weight padded to the same K when C*k*k is not a multiple of 64; a
+ * multiple of 256). Validates desc as vit_patch_embed does. */
+vit_status vit_patch_embed_workspace_size(const vit_patch_embed_desc* desc, size_t* bytes);
+
+/* Run a stem. pixels: float32 in pixel_layout (bf16 stems round them to
+ * bf16 as matrix operands); weight: act_dtype in weight_layout; bias:
+ * float32 [dim] or NULL; pos: float32 table (rows as pos_mode says) or NULL
+ * when pos_mode is NONE; tokens: [B, out_h*out_w, dim] act_dtype, raster
+ * order. Accumulation in float32; bias and position are added before the one
+ * rounding to act_dtype. All pointers device, 16-byte aligned; tokens must
+ * not overlap pixels or the workspace. Errors: VIT_ERR_INVALID_ARG for a bad
+ * descriptor (also a BUCKET grid that is not pos_side x pos_side) or
+ * pointer, VIT_ERR_WORKSPACE, VIT_ERR_UNSUPPORTED when the gathered matrix
+ * reaches 2^31 entries. Asynchronous on `stream`. */
+vit_status vit_patch_embed(const vit_patch_embed_desc* desc, const float* pixels,
+                           const void* weight, const float* bias, const float* pos,
+                           void* tokens, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

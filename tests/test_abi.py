@@ -25,6 +25,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(vb.vit_block_desc) == 19 * 4
     assert ctypes.sizeof(vb.vit_block_weights) == 21 * 8
     assert ctypes.sizeof(vb.vit_block_seams) == 10 * 8
+    assert ctypes.sizeof(vb.vit_patch_embed_desc) == 13 * 4
 
 
 @pytest.mark.parametrize("name", list(synth.CONFIGS))
@@ -221,3 +222,55 @@ def test_stack_create_rejects():
     assert "does not take block 0" in str(e.value)
     with pytest.raises(vb.VitError):
         vb.Stack([], levels, [])
+
+
+@pytest.mark.parametrize("kind", sorted(synth.STEMS))
+def test_patch_embed_workspace_every_stem(kind):
+    spec = synth.STEMS[kind]
+    n = vb.vit_patch_embed_workspace_size(vb.stem_desc_from_spec(spec))
+    oh, ow = synth.stem_out_grid(spec)
+    K = spec["in_ch"] * spec["kernel"] ** 2
+    Kp = -(-K // 64) * 64
+    a = -(-(spec["batch"] * oh * ow * Kp * 2) // 256) * 256
+    w = 0 if K == Kp else -(-(spec["dim"] * Kp * 2) // 256) * 256
+    assert n == a + w and n % 256 == 0
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(batch=0), "batch"),
+    (dict(kernel=0), "kernel"),
+    (dict(pad=7), "pad"),
+    (dict(stride=0), "stride"),
+    (dict(dim=100), "dim"),
+    (dict(in_h=3, pad=0), "fit"),
+    (dict(pixel_layout=5), "layout"),
+    (dict(weight_layout=2), "layout"),
+    (dict(pos_mode=9), "pos_mode"),
+    (dict(act_dtype=7), "dtype"),
+])
+def test_patch_embed_rejects(kw, msg):
+    d = vb.stem_desc_from_spec(synth.STEMS["hiera"])
+    for k, v in kw.items():
+        setattr(d, k, v)
+    n = ctypes.c_size_t()
+    assert vb.lib.vit_patch_embed_workspace_size(ctypes.byref(d), ctypes.byref(n)) == vb.VIT_ERR_INVALID_ARG
+    assert msg in vb.last_error()
+
+
+def test_patch_embed_rejects_before_launch():
+    L = vb.lib
+    d = vb.stem_desc_from_spec(synth.STEMS["siglip"])
+    need = vb.vit_patch_embed_workspace_size(d)
+    PX, W, B, POS, T, WS = (ctypes.c_void_p(a) for a in (0x10000000, 0x20000000, 0x21000000, 0x22000000,
+                                                          0x30000000, 0x40000000))
+    call = lambda *a: L.vit_patch_embed(ctypes.byref(d), *a)
+    assert call(PX, W, B, None, T, WS, need, None) == vb.VIT_ERR_INVALID_ARG and "pos" in vb.last_error()
+    assert call(None, W, B, POS, T, WS, need, None) == vb.VIT_ERR_INVALID_ARG
+    assert call(PX, W, B, POS, T, WS, need - 256, None) == vb.VIT_ERR_WORKSPACE
+    assert call(PX, W, B, POS, T, None, need, None) == vb.VIT_ERR_WORKSPACE
+    assert call(PX, W, ctypes.c_void_p(0x21000004), POS, T, WS, need, None) == vb.VIT_ERR_INVALID_ARG
+    assert call(PX, W, B, POS, ctypes.c_void_p(0x10000000 + 4096), WS, need, None) == vb.VIT_ERR_INVALID_ARG
+    assert "overlap" in vb.last_error()
+    # the bucketized table needs the grid to be pos_side x pos_side
+    d.pos_side = 16
+    assert call(PX, W, B, POS, T, WS, need, None) == vb.VIT_ERR_INVALID_ARG and "BUCKET" in vb.last_error()

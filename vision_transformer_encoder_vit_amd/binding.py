@@ -17,6 +17,9 @@ VIT_ATTN_GLOBAL, VIT_ATTN_MASK_UNIT, VIT_ATTN_SPATIAL = 0, 1, 2
 VIT_GELU_ERF, VIT_GELU_TANH = 0, 1
 VIT_QKV_FUSED, VIT_QKV_SEPARATE = 0, 1
 VIT_ROPE_NONE, VIT_ROPE_AXIAL_TABLE = 0, 1
+VIT_PIXELS_NCHW, VIT_PIXELS_NHWC = 0, 1
+VIT_CONV_OIHW, VIT_CONV_OHWI = 0, 1
+VIT_POS_NONE, VIT_POS_ROWS, VIT_POS_BUCKET, VIT_POS_TILE = 0, 1, 2, 3
 STAGES = ["ln1", "qkv", "residual", "attn", "proj", "ln2", "fc1", "fc2", "fused"]
 VIT_NSTAGES = len(STAGES)
 
@@ -45,6 +48,11 @@ SEAM_FIELDS = ["h", "qkv", "q_pooled", "r", "ctx", "attn_branch", "x1", "h2", "u
 
 class vit_block_seams(ctypes.Structure):
     _fields_ = [(n, _vp) for n in SEAM_FIELDS]
+
+
+class vit_patch_embed_desc(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in ("batch", "in_h", "in_w", "in_ch", "pixel_layout", "kernel", "stride", "pad",
+                                     "dim", "weight_layout", "pos_mode", "pos_side", "act_dtype")]
 
 
 class VitError(RuntimeError):
@@ -82,6 +90,8 @@ def _load():
         "vit_stack_workspace_size": [_vp, P(ctypes.c_size_t)],
         "vit_stack_forward": [_vp, P(vit_block_weights), _vp, P(_vp), _vp, ctypes.c_size_t, _vp],
         "vit_stack_destroy": [_vp],
+        "vit_patch_embed_workspace_size": [P(vit_patch_embed_desc), P(ctypes.c_size_t)],
+        "vit_patch_embed": [P(vit_patch_embed_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -267,3 +277,29 @@ def vit_pool4(x, y, channels=None, stream=None):
     c = channels or x.shape[-1]
     check(lib.vit_pool4(_ptr(x), x.shape[-1], _ptr(y), y.shape[-1], x.shape[0], x.shape[1], c,
                         _dt(x), _stream(stream)))
+
+
+_POS = {"none": VIT_POS_NONE, "rows": VIT_POS_ROWS, "bucket": VIT_POS_BUCKET, "tile": VIT_POS_TILE}
+
+
+def stem_desc_from_spec(spec):
+    """vit_patch_embed_desc of a stem spec (as the input generator writes them)."""
+    return vit_patch_embed_desc(
+        batch=spec["batch"], in_h=spec["in_h"], in_w=spec["in_w"], in_ch=spec["in_ch"],
+        pixel_layout=VIT_PIXELS_NHWC if spec["layout"] == "nhwc" else VIT_PIXELS_NCHW,
+        kernel=spec["kernel"], stride=spec["stride"], pad=spec["pad"], dim=spec["dim"],
+        weight_layout=VIT_CONV_OHWI if spec["weight_layout"] == "ohwi" else VIT_CONV_OIHW,
+        pos_mode=_POS[spec["pos_mode"]], pos_side=spec["pos_side"],
+        act_dtype=VIT_DTYPE_BF16 if spec["dtype"] == "bf16" else VIT_DTYPE_F32)
+
+
+def vit_patch_embed_workspace_size(desc):
+    n = ctypes.c_size_t()
+    check(lib.vit_patch_embed_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def vit_patch_embed(desc, pixels, weight, bias, pos, tokens, workspace, stream=None):
+    check(lib.vit_patch_embed(ctypes.byref(desc), _ptr(pixels), _ptr(weight), _ptr(bias), _ptr(pos), _ptr(tokens),
+                              _ptr(workspace), workspace.numel() * workspace.element_size()
+                              if workspace is not None else 0, _stream(stream)))

@@ -761,3 +761,129 @@ VIT_API vit_status vit_pool4(const void* x, int64_t x_row_stride, void* y, int64
                      "pool4");
   return st == VIT_OK ? ok() : st;
 }
+
+// ---- patch-embedding stems ------------------------------------------------
+
+static_assert(VIT_POS_NONE == vit::POS_NONE && VIT_POS_ROWS == vit::POS_ROWS && VIT_POS_BUCKET == vit::POS_BUCKET &&
+                  VIT_POS_TILE == vit::POS_TILE,
+              "position modes of the ABI and the GEMM epilogue");
+
+namespace {
+
+struct stem_geom {
+  int out_h, out_w, K, Kp;
+  int64_t M;
+  size_t esize, a_bytes, w_bytes;  // workspace: gathered pixels, padded weight
+  bool pad_weight;
+};
+
+vit_status stem_check(const vit_patch_embed_desc* d, stem_geom* g) {
+  if (!d) return fail(VIT_ERR_INVALID_ARG, "desc is NULL");
+  vit_status st = check_dtype(d->act_dtype);
+  if (st != VIT_OK) return st;
+  if (d->batch < 1) return fail(VIT_ERR_INVALID_ARG, "batch %d < 1", d->batch);
+  if (d->in_h < 1 || d->in_w < 1 || d->in_ch < 1 || d->in_ch > 64)
+    return fail(VIT_ERR_INVALID_ARG, "bad pixel shape %dx%dx%d", d->in_h, d->in_w, d->in_ch);
+  if (d->pixel_layout != VIT_PIXELS_NCHW && d->pixel_layout != VIT_PIXELS_NHWC)
+    return fail(VIT_ERR_INVALID_ARG, "unknown pixel layout %d", d->pixel_layout);
+  if (d->weight_layout != VIT_CONV_OIHW && d->weight_layout != VIT_CONV_OHWI)
+    return fail(VIT_ERR_INVALID_ARG, "unknown weight layout %d", d->weight_layout);
+  if (d->kernel < 1 || d->kernel > 32 || d->stride < 1 || d->pad < 0 || d->pad >= d->kernel)
+    return fail(VIT_ERR_INVALID_ARG, "kernel %d, stride %d, pad %d: need 1 <= kernel <= 32, stride >= 1, 0 <= pad < kernel",
+                d->kernel, d->stride, d->pad);
+  if (d->dim < 8 || d->dim % 8 || d->dim > 8192) return fail(VIT_ERR_INVALID_ARG, "dim %d must be a multiple of 8 in [8, 8192]", d->dim);
+  g->out_h = d->in_h + 2 * d->pad >= d->kernel ? (d->in_h + 2 * d->pad - d->kernel) / d->stride + 1 : 0;
+  g->out_w = d->in_w + 2 * d->pad >= d->kernel ? (d->in_w + 2 * d->pad - d->kernel) / d->stride + 1 : 0;
+  if (g->out_h < 1 || g->out_w < 1) return fail(VIT_ERR_INVALID_ARG, "the kernel does not fit the padded image");
+  switch (d->pos_mode) {
+    case VIT_POS_NONE:
+    case VIT_POS_ROWS: break;
+    case VIT_POS_BUCKET:
+      if (d->pos_side != g->out_h || d->pos_side != g->out_w)
+        return fail(VIT_ERR_INVALID_ARG, "BUCKET positions need a square grid equal to pos_side (%d), got %dx%d",
+                    d->pos_side, g->out_h, g->out_w);
+      break;
+    case VIT_POS_TILE:
+      if (d->pos_side < 1) return fail(VIT_ERR_INVALID_ARG, "TILE positions need pos_side >= 1");
+      break;
+    default: return fail(VIT_ERR_INVALID_ARG, "unknown pos_mode %d", d->pos_mode);
+  }
+  g->K = d->in_ch * d->kernel * d->kernel;
+  g->Kp = (g->K + 63) / 64 * 64;
+  g->M = (int64_t)d->batch * g->out_h * g->out_w;
+  if (g->M * g->Kp >= (int64_t(1) << 31)) return fail(VIT_ERR_UNSUPPORTED, "gathered matrix of %lld entries is too large",
+                                                      (long long)(g->M * g->Kp));
+  g->esize = d->act_dtype == VIT_DTYPE_BF16 ? 2 : 4;
+  g->pad_weight = g->K != g->Kp;
+  g->a_bytes = round256((size_t)g->M * g->Kp * g->esize);
+  g->w_bytes = g->pad_weight ? round256((size_t)d->dim * g->Kp * g->esize) : 0;
+  return VIT_OK;
+}
+
+}  // namespace
+
+VIT_API vit_status vit_patch_embed_workspace_size(const vit_patch_embed_desc* desc, size_t* bytes) {
+  if (!bytes) return fail(VIT_ERR_INVALID_ARG, "bytes is NULL");
+  stem_geom g;
+  vit_status st = stem_check(desc, &g);
+  if (st != VIT_OK) return st;
+  *bytes = g.a_bytes + g.w_bytes;
+  return ok();
+}
+
+VIT_API vit_status vit_patch_embed(const vit_patch_embed_desc* desc, const float* pixels, const void* weight,
+                                   const float* bias, const float* pos, void* tokens, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  stem_geom g;
+  vit_status st = stem_check(desc, &g);
+  if (st != VIT_OK) return st;
+  const vit_patch_embed_desc& d = *desc;
+  if (!pixels || !weight || !tokens) return fail(VIT_ERR_INVALID_ARG, "pixels, weight and tokens must not be NULL");
+  if (d.pos_mode != VIT_POS_NONE && !pos) return fail(VIT_ERR_INVALID_ARG, "pos is NULL but pos_mode is not NONE");
+  if (!aligned16(pixels) || !aligned16(weight) || !aligned16(tokens) || (bias && !aligned16(bias)) ||
+      (pos && !aligned16(pos)))
+    return fail(VIT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (workspace_bytes < g.a_bytes + g.w_bytes)
+    return fail(VIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, g.a_bytes + g.w_bytes);
+  if (!workspace || !aligned16(workspace)) return fail(VIT_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+  const size_t pix_bytes = (size_t)d.batch * d.in_h * d.in_w * d.in_ch * 4;
+  const size_t tok_bytes = (size_t)g.M * d.dim * g.esize;
+  const size_t ws = g.a_bytes + g.w_bytes;
+  if (overlaps(tokens, tok_bytes, pixels, pix_bytes) || overlaps(tokens, tok_bytes, workspace, ws) ||
+      overlaps(workspace, ws, pixels, pix_bytes))
+    return fail(VIT_ERR_INVALID_ARG, "tokens, pixels and workspace must not overlap");
+  const vit::DType dt = d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32;
+  const hipStream_t s = (hipStream_t)stream;
+  char* base = static_cast<char*>(workspace);
+  void* A = base;
+  const void* W = weight;
+  st = device_status(vit::launch_im2col(pixels, d.pixel_layout == VIT_PIXELS_NHWC, d.batch, d.in_ch, d.in_h, d.in_w,
+                                        d.kernel, d.stride, d.pad, d.weight_layout == VIT_CONV_OHWI, A, g.Kp, dt, s),
+                     "im2col");
+  if (st != VIT_OK) return st;
+  if (g.pad_weight) {
+    void* Wp = base + g.a_bytes;
+    st = device_status(vit::launch_pad_rows(weight, d.dim, g.K, Wp, g.Kp, dt, s), "weight pad");
+    if (st != VIT_OK) return st;
+    W = Wp;
+  }
+  vit::GemmArgs a;
+  a.A = A;
+  a.lda = g.Kp;
+  a.W[0] = W;
+  a.bias[0] = bias;
+  a.seg_cols = d.dim;
+  a.C = tokens;
+  a.ldc = d.dim;
+  a.M = (int)g.M;
+  a.N = d.dim;
+  a.K = g.Kp;
+  a.epi = vit::EPI_BIAS_POS;
+  a.tokens_per_frame = g.out_h * g.out_w;
+  a.grid_w = g.out_w;
+  a.pos = d.pos_mode == VIT_POS_NONE ? nullptr : pos;
+  a.pos_mode = d.pos_mode;
+  a.pos_side = d.pos_side;
+  st = device_status(vit::launch_gemm(a, dt, s), "patch-embed GEMM");
+  return st == VIT_OK ? ok() : st;
+}

@@ -41,7 +41,19 @@ struct GemmParams {
   T* vt;  // transposed copy of columns >= vt_col0 (MFMA path only)
   int vt_col0, vt_tokens, vt_heads, vt_hd;
   bool vt_only;
+  const float* pos;  // EPI_BIAS_POS: table [rows, N]
+  int pos_mode, pos_side;
 };
+
+// Position-table row of token m (EPI_BIAS_POS), see PosMode.
+template <typename P>
+__device__ __forceinline__ int pos_row(const P& p, int64_t m) {
+  const int t = (int)(m % p.tokens_per_frame);
+  const int y = t / p.grid_w, x = t - y * p.grid_w;
+  if (p.pos_mode == POS_BUCKET) return max(y - 1, 0) * p.pos_side + max(x - 1, 0);
+  if (p.pos_mode == POS_TILE) return (y % p.pos_side) * p.pos_side + (x % p.pos_side);
+  return t;
+}
 
 __device__ __forceinline__ float gelu_erf_f(float v) { return gelu_erf_as(v); }
 __device__ __forceinline__ float gelu_tanh_f(float v) { return gelu_tanh_fast(v); }
@@ -157,9 +169,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
       if (n >= p.N) continue;
       const int seg = n / p.seg_cols;
       const float* bb = seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2);
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(bb + (n - seg * p.seg_cols));
-      f32x4 v = acc[i][j] + b4;
-      if (EPI == EPI_BIAS_ROPE) {
+      f32x4 v = acc[i][j];
+      if (EPI != EPI_BIAS_POS || bb != nullptr) v += *reinterpret_cast<const f32x4*>(bb + (n - seg * p.seg_cols));
+      if (EPI == EPI_BIAS_POS) {
+        if (p.pos_mode != POS_NONE) v += *reinterpret_cast<const f32x4*>(p.pos + (int64_t)pos_row(p, m) * p.N + n);
+      } else if (EPI == EPI_BIAS_ROPE) {
         if (n < p.rope_cols) {
           const int d = (n % (p.rope_cols / 2)) % p.head_dim;  // even, pair d/2 and d/2+1
           const f32x4 cs = *reinterpret_cast<const f32x4*>(p.rope + ((int64_t)rope_row * (p.head_dim / 2) + d / 2) * 2);
@@ -419,14 +433,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8);
       *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4);
       const int seg = n / p.seg_cols;
-      const float* bb = (seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2)) + (n - seg * p.seg_cols);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bb), b1 = *reinterpret_cast<const f32x4*>(bb + 4);
+      const float* bseg = seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2);
+      if (EPI != EPI_BIAS_POS || bseg != nullptr) {
+        const float* bb = bseg + (n - seg * p.seg_cols);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bb), b1 = *reinterpret_cast<const f32x4*>(bb + 4);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[t] += b0[t];
-        v[4 + t] += b1[t];
+        for (int t = 0; t < 4; ++t) {
+          v[t] += b0[t];
+          v[4 + t] += b1[t];
+        }
       }
-      if (EPI == EPI_BIAS_ROPE) {
+      if (EPI == EPI_BIAS_POS) {
+        if (p.pos_mode != POS_NONE) {
+          const float* pp = p.pos + (int64_t)pos_row(p, m) * p.N + n;
+          const f32x4 q0 = *reinterpret_cast<const f32x4*>(pp), q1 = *reinterpret_cast<const f32x4*>(pp + 4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v[t] += q0[t];
+            v[4 + t] += q1[t];
+          }
+        }
+      } else if (EPI == EPI_BIAS_ROPE) {
         if (n < p.rope_cols) {
           const int t = m % p.tokens_per_frame;
           int rr = t;
@@ -473,6 +500,7 @@ static hipError_t gemm32_go(const GemmParams<bf16>& p, int epi, hipStream_t s, S
     case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_ROPE>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
     case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_ERF>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
     case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_TANH>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_POS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_POS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
     default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_RES>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
   }
   return hipGetLastError();
@@ -513,6 +541,9 @@ static GemmParams<T> make_params(const GemmArgs& a) {
   p.vt_heads = a.vt_heads;
   p.vt_hd = a.vt_hd;
   p.vt_only = a.vt != nullptr && a.vt_only;
+  p.pos = a.pos;
+  p.pos_mode = a.pos ? a.pos_mode : POS_NONE;
+  p.pos_side = a.pos_side > 0 ? a.pos_side : 1;
   return p;
 }
 
@@ -527,6 +558,7 @@ static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
     case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS_ROPE>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
     case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_GELU_ERF>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
     case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_GELU_TANH>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_POS: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS_POS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
     default: hipExtLaunchKernelGGL((gemm_kernel<T, BM, BN, WTM, WTN, EPI_BIAS_RES>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
   }
   return hipGetLastError();

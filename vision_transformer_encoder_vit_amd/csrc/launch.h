@@ -21,7 +21,14 @@ enum Epilogue {
   EPI_GELU_ERF = 2,    // C = gelu_erf(acc + bias)
   EPI_GELU_TANH = 3,   // C = gelu_tanh(acc + bias)
   EPI_BIAS_RES = 4,    // C = res + (acc + bias); branch = acc + bias if set
+  EPI_BIAS_POS = 5,    // C = acc + bias + pos[row(token)] (bias and pos may be NULL)
 };
+
+// Position-table row of token t = y * grid_w + x of a frame (EPI_BIAS_POS):
+// POS_ROWS t; POS_BUCKET max(y-1,0) * pos_side + max(x-1,0); POS_TILE
+// (y mod pos_side) * pos_side + (x mod pos_side). Values match the C ABI's
+// VIT_POS_*.
+enum PosMode { POS_NONE = 0, POS_ROWS = 1, POS_BUCKET = 2, POS_TILE = 3 };
 
 // C[M, N] = epilogue(A[M, K] * W[N, K]^T + bias). W and bias may be split
 // into up to three column segments of seg_cols columns each (separate q/k/v
@@ -53,6 +60,10 @@ struct GemmArgs {
   void* vt = nullptr;
   int vt_col0 = 0, vt_tokens = 0, vt_heads = 0, vt_hd = 0;
   bool vt_only = false;
+  // EPI_BIAS_POS: float32 table [rows, N]; frames of tokens_per_frame tokens
+  // on a grid grid_w wide
+  const float* pos = nullptr;
+  int pos_mode = POS_NONE, pos_side = 0;
 };
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 
@@ -75,6 +86,16 @@ struct AttnArgs {
   int q_stride = 1;
   float scale = 1.f;
 };
+// Patch-embedding gather: A[m, kk] (m = (frame, y, x) of the output grid,
+// kk < C*k*k in the weight's flattening order, (c, ky, kx) for OIHW or
+// (ky, kx, c) for OHWI; zero outside the image and for kk >= C*k*k) for
+// float32 pixels [B, C, H, W] (nhwc false) or [B, H, W, C]; A is [M, Kp].
+hipError_t launch_im2col(const float* pixels, bool nhwc, int batch, int C, int H, int W, int k, int s, int p,
+                         bool ohwi, void* A, int Kp, DType dt, hipStream_t st, StageEvents ev = {});
+// Copy rows of `cols` elements into rows of `ld` (>= cols, a multiple of the
+// 16-byte chunk), zero-filling the tail.
+hipError_t launch_pad_rows(const void* src, int64_t rows, int cols, void* dst, int ld, DType dt, hipStream_t st);
+
 hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 
 // Large global or spatial windows go to the 32x32-MFMA attention kernel,

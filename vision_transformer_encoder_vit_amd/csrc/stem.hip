@@ -1,0 +1,131 @@
+// Patch-embedding stems: the strided convolution that turns pixels into the
+// token grid, run as a gather (im2col) into a [tokens, K] matrix followed by
+// the MFMA GEMM, whose epilogue adds the bias and the position table row of
+// each token. Sources: the Hiera plan ("Phase 4: Hiera Backbone MLX Port",
+// "Architecture Summary": PatchEmbed Conv2d 4->112, 7x7, stride 4, then the
+// learned pos_embed); the SigLIP page (``embed_frame``: k16 s16 conv with
+// bias, position rows from bucketized coordinates); the SAM3 page (trunk
+// patch step: k14 s14 conv without bias, a 24x24 table tiled over the grid,
+// then ln_pre).
+//
+// The gather writes row m = (frame, y, x) of A with its K = C*k*k pixels in
+// the weight's own flattening order -- (c, ky, kx) for OIHW weights,
+// (ky, kx, c) for OHWI -- so the weight is used as the GEMM's [N, K] operand
+// without any transpose; K is padded with zeros to a multiple of 64 (the
+// MFMA GEMM's K tile), and the weight rows are padded to match when K is not
+// already a multiple of 64.
+#include "common.h"
+#include "launch.h"
+
+#include <hip/hip_ext.h>
+
+namespace vit {
+
+struct Im2colParams {
+  int64_t M;  // frames * out_h * out_w
+  int C, H, W, k, s, p, out_h, out_w;
+  int K, Kp;  // C*k*k and its padded width
+  int nhwc, ohwi;
+};
+
+// One thread per 16-byte chunk of an A row (8 bf16 or 4 float entries):
+// consecutive threads write consecutive chunks of a row. Entries outside
+// the image (the zero padding) and past K are zero.
+template <typename T>
+__global__ __launch_bounds__(256) void im2col_kernel(const float* __restrict__ px, T* __restrict__ A,
+                                                     Im2colParams q) {
+  constexpr int VN = Vec<T>::N;
+  const int cpr = q.Kp / VN;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t m = id / cpr;
+  if (m >= q.M) return;
+  const int chunk = (int)(id - m * cpr);
+  const int T_ = q.out_h * q.out_w;
+  const int b = (int)(m / T_), t = (int)(m - (int64_t)b * T_);
+  const int y = t / q.out_w, x = t - y * q.out_w;
+  const int y0 = y * q.s - q.p, x0 = x * q.s - q.p;
+  const int kk2 = q.k * q.k, kc = q.k * q.C;
+  float v[VN];
+#pragma unroll
+  for (int e = 0; e < VN; ++e) {
+    const int kk = chunk * VN + e;
+    float val = 0.f;
+    if (kk < q.K) {
+      int c, ky, kx;
+      if (q.ohwi) {
+        ky = kk / kc;
+        const int r = kk - ky * kc;
+        kx = r / q.C;
+        c = r - kx * q.C;
+      } else {
+        c = kk / kk2;
+        const int r = kk - c * kk2;
+        ky = r / q.k;
+        kx = r - ky * q.k;
+      }
+      const int py = y0 + ky, pxx = x0 + kx;
+      if (py >= 0 && py < q.H && pxx >= 0 && pxx < q.W)
+        val = q.nhwc ? px[(((int64_t)b * q.H + py) * q.W + pxx) * q.C + c]
+                     : px[(((int64_t)b * q.C + c) * q.H + py) * q.W + pxx];
+    }
+    v[e] = val;
+  }
+  st16(A + m * q.Kp + chunk * VN, pack16<T>(v));
+}
+
+// dst[r, 0:cols] = src[r, 0:cols], dst[r, cols:ld] = 0: one 16-byte chunk of
+// dst per thread (ld a multiple of the chunk; cols <= ld need not be, the
+// source is read element by element).
+template <typename T>
+__global__ __launch_bounds__(256) void pad_rows_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                       int64_t rows, int cols, int ld) {
+  constexpr int VN = Vec<T>::N;
+  const int cpr = ld / VN;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = id / cpr;
+  if (r >= rows) return;
+  const int c0 = (int)(id - r * cpr) * VN;
+  float v[VN];
+#pragma unroll
+  for (int e = 0; e < VN; ++e) v[e] = c0 + e < cols ? to_f32(src[r * cols + c0 + e]) : 0.f;
+  st16(dst + r * ld + c0, pack16<T>(v));
+}
+
+hipError_t launch_im2col(const float* pixels, bool nhwc, int batch, int C, int H, int W, int k, int s, int p,
+                         bool ohwi, void* A, int Kp, DType dt, hipStream_t st, StageEvents ev) {
+  Im2colParams q;
+  q.C = C;
+  q.H = H;
+  q.W = W;
+  q.k = k;
+  q.s = s;
+  q.p = p;
+  q.out_h = (H + 2 * p - k) / s + 1;
+  q.out_w = (W + 2 * p - k) / s + 1;
+  q.M = (int64_t)batch * q.out_h * q.out_w;
+  q.K = C * k * k;
+  q.Kp = Kp;
+  q.nhwc = nhwc;
+  q.ohwi = ohwi;
+  const int vn = dt == DType::BF16 ? 8 : 4;
+  const int64_t threads = q.M * (Kp / vn);
+  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (dt == DType::BF16)
+    hipExtLaunchKernelGGL(im2col_kernel<bf16>, grid, block, 0, st, ev.start, ev.stop, 0, pixels, (bf16*)A, q);
+  else
+    hipExtLaunchKernelGGL(im2col_kernel<float>, grid, block, 0, st, ev.start, ev.stop, 0, pixels, (float*)A, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(const void* src, int64_t rows, int cols, void* dst, int ld, DType dt, hipStream_t st) {
+  const int vn = dt == DType::BF16 ? 8 : 4;
+  const int64_t threads = rows * (ld / vn);
+  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (dt == DType::BF16)
+    hipLaunchKernelGGL(pad_rows_kernel<bf16>, grid, block, 0, st, (const bf16*)src, (bf16*)dst, rows, cols, ld);
+  else
+    hipLaunchKernelGGL(pad_rows_kernel<float>, grid, block, 0, st, (const float*)src, (float*)dst, rows, cols, ld);
+  return hipGetLastError();
+}
+
+}  // namespace vit
