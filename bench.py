@@ -243,21 +243,19 @@ def copy_calibration(steps):
 
 
 TOWERS = {
-    "hiera": "Hiera stage stack at a 512x512 input: 128x128 tokens, 24 blocks (stages of 2/3/16/3, D 112..896), "
-             "features after blocks 1, 4, 20, 23",
-    "sam3": "SAM3 trunk: ln_pre + 32 blocks on 72x72 tokens, D 1024, 24x24 windows, global layers 7/15/23/31",
-    "siglip": "SigLIP tower: 8 frames x 32x32 tokens, 12 blocks D 768 + post_layernorm",
+    "hiera": "Hiera backbone from pixels: 1 x 512x512x4 -> 7x7/4 patch embed + positions -> 128x128 tokens, "
+             "24 blocks (stages of 2/3/16/3, D 112..896), features after blocks 1, 4, 20, 23",
+    "sam3": "SAM3 trunk from pixels: 3x1008x1008 -> 14x14 patch embed + tiled positions -> ln_pre -> 32 blocks on "
+            "72x72 tokens, D 1024, 24x24 windows, global layers 7/15/23/31",
+    "siglip": "SigLIP tower from pixels: 8 frames 3x512x512 -> 16x16 patch embed + bucketized positions -> "
+              "12 blocks D 768 on 32x32 tokens -> post_layernorm",
 }
 
 
-def run_tower(kind, steps, warmup, with_cpu):
-    """A chain of blocks through vit_stack_forward (plus the LayerNorm before
-    (SAM3 ln_pre) or after (SigLIP post_layernorm) it through vit_layernorm):
-    K event-free forwards timed like the block workload."""
-    import numpy as np
-    import torch
-    from vision_transformer_encoder_vit_amd import binding as vb
-    from vision_transformer_encoder_vit_amd import synth, work
+def tower_parts(kind):
+    """Stem spec, block specs, unroll levels, taps and the LayerNorms before
+    (SAM3 ln_pre) and after (SigLIP post_layernorm) the blocks."""
+    from vision_transformer_encoder_vit_amd import synth
     pre = post = None
     if kind == "hiera":
         specs, levels, taps = synth.hiera_stack()
@@ -266,15 +264,35 @@ def run_tower(kind, steps, warmup, with_cpu):
         levels, taps = 0, [len(specs) - 1]
         ln = synth.make_layernorm_params(specs[0]["dim_in"], 0)
         pre, post = (ln, None) if kind == "sam3" else (None, ln)
-    x, blocks = synth.make_stack_inputs(specs, seed=0)
+    return synth.STEMS[kind], specs, levels, taps, pre, post
+
+
+def run_tower(kind, steps, warmup, with_cpu):
+    """A whole vision tower from pixels: vit_patch_embed, then (SAM3) ln_pre
+    through vit_layernorm, the blocks through vit_stack_forward, then
+    (SigLIP) post_layernorm. K event-free forwards timed like the block
+    workload; a second pass times the stem alone with events."""
+    import numpy as np
+    import torch
+    from vision_transformer_encoder_vit_amd import binding as vb
+    from vision_transformer_encoder_vit_amd import synth, work
+    stem, specs, levels, taps, pre, post = tower_parts(kind)
+    sin = synth.make_stem_inputs(stem, seed=0)
+    _, blocks = synth.make_stack_inputs(specs, seed=0)
     dt = torch.bfloat16
     dev_w = []
     for w in blocks:
         dev_w.append({k: (torch.from_numpy(np.ascontiguousarray(a)).to(dt) if k.endswith("_w")
                           else torch.from_numpy(np.ascontiguousarray(a))).cuda() for k, a in w.items()})
     weights = [vb.weights_struct(w) for w in dev_w]
-    xd = torch.from_numpy(x).to(dt).cuda()
-    xin = torch.empty_like(xd)
+    px = torch.from_numpy(sin["pixels"]).cuda()
+    sw = torch.from_numpy(sin["weight"]).to(dt).cuda()
+    sb = torch.from_numpy(sin["bias"]).cuda() if "bias" in sin else None
+    spos = torch.from_numpy(sin["pos"]).cuda()
+    sdesc = vb.stem_desc_from_spec(stem)
+    sws = torch.empty(vb.vit_patch_embed_workspace_size(sdesc), dtype=torch.uint8, device="cuda")
+    B, N0, D0 = specs[0]["batch"], specs[0]["grid_h"] * specs[0]["grid_w"], specs[0]["dim_in"]
+    tok = torch.empty((B, N0, D0), dtype=dt, device="cuda")
     st = vb.Stack([vb.desc_from_spec(s) for s in specs], levels, taps)
     feats = [torch.empty((specs[t]["batch"], synth.out_tokens(specs[t]), specs[t]["dim_out"]), dtype=dt,
                          device="cuda") for t in taps]
@@ -282,12 +300,14 @@ def run_tower(kind, steps, warmup, with_cpu):
     lnd = lambda p: tuple(torch.from_numpy(a).cuda() for a in p) if p is not None else None
     pre_d, post_d = lnd(pre), lnd(post)
 
+    def embed():
+        vb.vit_patch_embed(sdesc, px, sw, sb, spos, tok, sws)
+
     def forward():
-        src = xd
+        embed()
         if pre_d is not None:
-            vb.vit_layernorm(xd, xin, pre_d[0], pre_d[1], specs[0]["eps"])
-            src = xin
-        st.forward(weights, src, feats, ws)
+            vb.vit_layernorm(tok, tok, pre_d[0], pre_d[1], specs[0]["eps"])
+        st.forward(weights, tok, feats, ws)
         if post_d is not None:
             vb.vit_layernorm(feats[-1], feats[-1], post_d[0], post_d[1], specs[-1]["eps"])
 
@@ -299,32 +319,47 @@ def run_tower(kind, steps, warmup, with_cpu):
         forward()
     torch.cuda.synchronize()
     dt_step = (time.perf_counter() - t0) / steps
+    # the stem alone, between whole forwards (so its weights and pixels are
+    # as cold as in the timed pass)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        forward()
+        e0.record()
+        embed()
+        e1.record()
+    torch.cuda.synchronize()
+    stem_us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
     st.close()
-    flops = sum(work.block_flops(s) for s in specs)
-    tokens = specs[0]["batch"] * specs[0]["grid_h"] * specs[0]["grid_w"]
-    line = {"metric": "%s tower input tokens/sec, 1 GPU" % kind, "value": tokens / dt_step,
+    oh, ow = synth.stem_out_grid(stem)
+    K = stem["in_ch"] * stem["kernel"] ** 2
+    stem_flops = 2.0 * B * oh * ow * stem["dim"] * K
+    flops = sum(work.block_flops(s) for s in specs) + stem_flops
+    line = {"metric": "%s tower from pixels, input tokens/sec, 1 GPU" % kind, "value": B * N0 / dt_step,
             "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": 1e3 * dt_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": TOWERS[kind], "batch": specs[0]["batch"],
-                       "tokens_per_frame": specs[0]["grid_h"] * specs[0]["grid_w"], "parallelism": "none (1 GPU)"},
-            "tflops": flops / dt_step / 1e12, "pct_of_bf16_peak": 100.0 * flops / dt_step / 1e12 / PEAK_BF16_TFLOPS}
+            "config": {"workload": TOWERS[kind], "batch": B, "tokens_per_frame": N0, "parallelism": "none (1 GPU)"},
+            "tflops": flops / dt_step / 1e12, "pct_of_bf16_peak": 100.0 * flops / dt_step / 1e12 / PEAK_BF16_TFLOPS,
+            "stem_us": round(stem_us, 2), "stem_tflops": round(stem_flops / stem_us / 1e6, 1)}
     if with_cpu and kind in ("hiera", "siglip"):
         # the float64 oracle on one frame (SigLIP: frame 0 of the 8; the
         # SAM3 trunk's 32 full-size layers would take minutes and is skipped)
         from oracle import stack as ost
+        from oracle import stem as ostem
         from threadpoolctl import threadpool_info
         one = [synth.derive(s, batch=1) for s in specs]
+        stem1 = dict(stem, batch=1)
+        sin1 = dict(sin, pixels=sin["pixels"][:1])
         t1 = time.perf_counter()
+        x1 = ostem.patch_embed(sin1, stem1)
         if kind == "hiera":
-            ost.stack_forward(x[:1], blocks, one, levels, taps)
+            ost.stack_forward(x1, blocks, one, levels, taps)
         else:
-            ost.tower_forward(x[:1], blocks, one, post_ln=post)
+            ost.tower_forward(x1, blocks, one, post_ln=post)
         tc = time.perf_counter() - t1
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-        n1 = one[0]["grid_h"] * one[0]["grid_w"]
-        line["cpu_baseline"] = {"value": n1 / tc, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-                                "sample": "float64 numpy oracle, the whole chain on one frame (%d tokens), %.1f s"
-                                          % (n1, tc)}
+        line["cpu_baseline"] = {"value": N0 / tc, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                                "sample": "float64 numpy oracle, stem and blocks on one frame (%d tokens), %.1f s"
+                                          % (N0, tc)}
     return line
 
 
@@ -387,8 +422,9 @@ def main():
     ap.add_argument("--config", default=DEFAULT_CONFIG, help="workload name, or 'all'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tower", choices=sorted(TOWERS),
-                    help="time a chain of blocks (hiera: the 24-block stage stack at 512x512; sam3: the 32-layer "
-                         "trunk; siglip: the 12-layer tower) instead of one block")
+                    help="time a whole tower from pixels (patch embed, then hiera: the 24-block stage stack at "
+                         "512x512; sam3: ln_pre and the 32-layer trunk; siglip: the 12-layer tower and "
+                         "post_layernorm) instead of one block")
     ap.add_argument("--rowops", action="store_true",
                     help="only time LayerNorm, unroll, reroll and pool4 on HBM-resident working sets")
     ap.add_argument("--copy-calibration", action="store_true",

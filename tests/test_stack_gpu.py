@@ -132,3 +132,58 @@ def test_siglip_tower_full_frame_vs_oracle():
     ln = synth.make_layernorm_params(768, 3)
     got = _tower_gpu(specs, x, blocks, post_ln=ln)
     _tower_gate("siglip tower 12 layers", got, ost.tower_forward(x, blocks, specs, post_ln=ln))
+
+
+def _embed_gpu(stem, sin):
+    dt = gu.torch_dtype(stem)
+    oh, ow = synth.stem_out_grid(stem)
+    desc = vb.stem_desc_from_spec(stem)
+    tok = torch.empty((stem["batch"], oh * ow, stem["dim"]), dtype=dt, device="cuda")
+    ws = torch.empty(vb.vit_patch_embed_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    vb.vit_patch_embed(desc, torch.from_numpy(sin["pixels"]).cuda(), torch.from_numpy(sin["weight"]).to(dt).cuda(),
+                       torch.from_numpy(sin["bias"]).cuda() if "bias" in sin else None,
+                       torch.from_numpy(sin["pos"]).cuda(), tok, ws)
+    return tok
+
+
+@pytest.mark.parametrize("kind", ["siglip", "sam3", "hiera"])
+def test_tower_from_pixels(kind):
+    # stem -> (ln_pre) -> blocks -> (post_layernorm), all on the GPU, against
+    # the stem oracle feeding the tower / stack oracle. SigLIP: one full
+    # frame and all 12 layers; SAM3: a 336x336 image (24x24 tokens, 12x12
+    # windows) into a narrowed 8-layer trunk; Hiera: the 512x512 backbone.
+    from oracle import stem as ostem
+    print("case tower from pixels", kind, flush=True)
+    if kind == "siglip":
+        stem = dict(synth.STEMS["siglip"], batch=1)
+        specs, levels, taps = synth.siglip_tower(batch=1), 0, [11]
+        pre, post = None, synth.make_layernorm_params(768, 4)
+    elif kind == "sam3":
+        stem = dict(synth.STEMS["sam3"], in_h=336, in_w=336, dim=256, pos_side=12)
+        specs = synth.sam3_trunk(grid=24, win=12, layers=8, global_layers=(3, 7), dim=256, heads=4, mlp=1024)
+        levels, taps = 0, [7]
+        pre, post = synth.make_layernorm_params(256, 4), None
+    else:
+        stem = synth.STEMS["hiera"]
+        specs, levels, taps = synth.hiera_stack()
+        pre = post = None
+    sin = synth.make_stem_inputs(stem, seed=4)
+    _, blocks = synth.make_stack_inputs(specs, seed=4)
+    tok = _embed_gpu(stem, sin)
+    x_ref = ostem.patch_embed(sin, stem)
+    if kind == "hiera":
+        dt = gu.torch_dtype(specs[0])
+        dev_w = [gu.to_device(w, sp) for w, sp in zip(blocks, specs)]
+        st = vb.Stack([vb.desc_from_spec(s) for s in specs], levels, taps)
+        feats = [torch.empty((1, synth.out_tokens(specs[t]), specs[t]["dim_out"]), dtype=dt, device="cuda")
+                 for t in taps]
+        ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+        st.forward([vb.weights_struct(w) for w in dev_w], tok, feats, ws)
+        torch.cuda.synchronize()
+        st.close()
+        ref = ost.stack_forward(x_ref, blocks, specs, levels, taps)
+        for k, (f, r) in enumerate(zip(feats, ref)):
+            _tower_gate("hiera from pixels, feature %d" % k, gu.to64(f), r)
+    else:
+        got = _tower_gpu(specs, gu.to64(tok), blocks, pre_ln=pre, post_ln=post)
+        _tower_gate("%s from pixels" % kind, got, ost.tower_forward(x_ref, blocks, specs, pre_ln=pre, post_ln=post))
