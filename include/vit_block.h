@@ -77,6 +77,14 @@ enum { VIT_ATTN_GLOBAL = 0, VIT_ATTN_MASK_UNIT = 1, VIT_ATTN_SPATIAL = 2 };
 enum { VIT_GELU_ERF = 0, VIT_GELU_TANH = 1 };
 enum { VIT_QKV_FUSED = 0, VIT_QKV_SEPARATE = 1 };
 enum { VIT_ROPE_NONE = 0, VIT_ROPE_AXIAL_TABLE = 1 };
+/* Weight matrix storage. Q8_ROW is the SAM3 page's `q8_row` tensor type
+ * (cortiq-engine sam3.rs, `bad_scales`: a [rows, cols] payload of one byte
+ * per element followed by one float16 scale per row): here the int8 payload
+ * and the scales are two arrays, and W[r, c] = payload[r, c] * scale[r]. The
+ * kernels multiply int8 (exact in bf16) by bf16 activations with float32
+ * accumulation and apply the scale per output column in the epilogue, so
+ * the result is that of the dequantized matrix up to float32 rounding. */
+enum { VIT_WEIGHTS_ACT = 0, VIT_WEIGHTS_Q8_ROW = 1 };
 
 /* Shape and options of one block. Validated by vit_block_create. */
 typedef struct vit_block_desc {
@@ -106,6 +114,11 @@ typedef struct vit_block_desc {
   float ln_eps;        /* LayerNorm epsilon (> 0), e.g. 1e-6                */
   float attn_scale;    /* softmax scale; 0 means head_dim^-1/2              */
   int32_t act_dtype;   /* VIT_DTYPE_F32 or VIT_DTYPE_BF16                   */
+  int32_t weight_format; /* VIT_WEIGHTS_ACT (0): matrices in act_dtype;
+                          VIT_WEIGHTS_Q8_ROW: int8 matrices with a float16
+                          scale per output row (see vit_block_weights);
+                          needs VIT_DTYPE_BF16 and dim_in, dim_out,
+                          mlp_hidden multiples of 64                        */
 } vit_block_desc;
 
 /* Device pointers to one block's parameters. Unused members may be NULL.
@@ -132,6 +145,16 @@ typedef struct vit_block_weights {
   const void* w_fc2;       /* [dim_out, mlp_hidden] */
   const float* b_fc2;      /* [dim_out] */
   const float* rope_table; /* [rope_rows, head_dim/2, 2] (cos, sin) */
+  /* VIT_WEIGHTS_Q8_ROW only: float16 scale per row of the matching int8
+   * matrix ([out_features] each); ignored otherwise */
+  const void* s_res;
+  const void* s_qkv;
+  const void* s_q;
+  const void* s_k;
+  const void* s_v;
+  const void* s_o;
+  const void* s_fc1;
+  const void* s_fc2;
 } vit_block_weights;
 
 /* Optional caller buffers for the block's intermediates (all act_dtype,

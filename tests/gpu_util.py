@@ -22,8 +22,9 @@ def to_device(inp, spec):
     dev = {}
     for k, a in inp.items():
         t = torch.from_numpy(np.ascontiguousarray(a))
-        if k == "x" or k.endswith("_w"):
+        if (k == "x" or k.endswith("_w")) and a.dtype != np.int8:
             t = t.to(dt)  # exact: the values are already representable in dt
+        # int8 payloads and float16 row scales of q8_row weights stay as they are
         dev[k] = t.to("cuda")
     return dev
 

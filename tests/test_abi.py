@@ -22,8 +22,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(vb.vit_block_desc) == 19 * 4
-    assert ctypes.sizeof(vb.vit_block_weights) == 21 * 8
+    assert ctypes.sizeof(vb.vit_block_desc) == 20 * 4
+    assert ctypes.sizeof(vb.vit_block_weights) == 29 * 8
     assert ctypes.sizeof(vb.vit_block_seams) == 10 * 8
     assert ctypes.sizeof(vb.vit_patch_embed_desc) == 13 * 4
 
@@ -61,6 +61,9 @@ BAD = [
     (dict(attn_scale=-1.0), vb.VIT_ERR_INVALID_ARG, "attn_scale"),
     (dict(act_dtype=9), vb.VIT_ERR_INVALID_ARG, "act_dtype"),
     (dict(rope=0, q_stride=4, dim_in=512), vb.VIT_ERR_UNSUPPORTED, "SPATIAL"),
+    (dict(weight_format=3), vb.VIT_ERR_INVALID_ARG, "weight_format"),
+    (dict(weight_format=vb.VIT_WEIGHTS_Q8_ROW, act_dtype=vb.VIT_DTYPE_F32), vb.VIT_ERR_UNSUPPORTED, "BF16"),
+    (dict(weight_format=vb.VIT_WEIGHTS_Q8_ROW, mlp_hidden=4712), vb.VIT_ERR_UNSUPPORTED, "multiples of 64"),
 ]
 
 
@@ -274,3 +277,20 @@ def test_patch_embed_rejects_before_launch():
     # the bucketized table needs the grid to be pos_side x pos_side
     d.pos_side = 16
     assert call(PX, W, B, POS, T, WS, need, None) == vb.VIT_ERR_INVALID_ARG and "BUCKET" in vb.last_error()
+
+
+def test_q8_forward_needs_every_scale():
+    # int8 weights: each matrix needs its float16 row scales
+    for name, drop in [("c5w_sam3_win", "s_qkv"), ("c5w_sam3_win", "s_fc2"), ("c4_siglip_b8", "s_k")]:
+        spec = dict(synth.CONFIGS[name], weights="q8_row")
+        w = _weights(spec)
+        for k, f in [("qkv_s", "s_qkv"), ("q_s", "s_q"), ("k_s", "s_k"), ("v_s", "s_v"), ("o_s", "s_o"),
+                     ("fc1_s", "s_fc1"), ("fc2_s", "s_fc2")]:
+            setattr(w, f, 0xA00000 + 0x1000 * len(k))
+        setattr(w, drop, None)
+        st, _ = _forward(spec, w, 0x10000000, 0x20000000, 0x30000000, 1 << 30)
+        assert st == vb.VIT_ERR_INVALID_ARG and drop in vb.last_error(), (name, drop, vb.last_error())
+    # and a block whose widths are not multiples of 64 cannot take them
+    spec = dict(synth.CONFIGS["c2_hiera_s0"], weights="q8_row")
+    h = ctypes.c_void_p()
+    assert vb.lib.vit_block_create(ctypes.byref(vb.desc_from_spec(spec)), ctypes.byref(h)) == vb.VIT_ERR_UNSUPPORTED

@@ -571,3 +571,34 @@ def test_sam3_pos_table_tiles_the_grid():
     np.testing.assert_array_equal(out[:24, :24], pos)
     np.testing.assert_array_equal(out[24:, :], out[:-24, :])
     np.testing.assert_array_equal(out[:, 24:], out[:, :-24])
+
+
+# ---------------------------------------------------------------- q8_row weights
+
+def test_q8_row_bytes_layout_by_hand():
+    # 2 x 3 payload, row-major, then two little-endian float16 scales
+    # (0x3800 = 0.5, 0x2000 = 2^-7)
+    from oracle import quant
+    payload = bytes([1, 0xFE, 0x7F, 0x80, 0x00, 0x05])  # 1, -2, 127 / -128, 0, 5
+    scales = bytes([0x00, 0x38, 0x00, 0x20])
+    q, s = quant.q8_row_from_bytes(payload + scales, 2, 3)
+    w = quant.dequant_q8_row(q, s)
+    np.testing.assert_array_equal(w, [[0.5, -1.0, 63.5], [-1.0, 0.0, 5.0 / 128.0]])
+    with pytest.raises(ValueError):
+        quant.q8_row_from_bytes(payload + scales[:3], 2, 3)
+
+
+def test_q8_row_dequant_within_half_step():
+    # the synthetic quantizer then the oracle's dequantization: every element
+    # within half a scale step of the float matrix (plus the float16 rounding
+    # of the scale, at most 2^-11 relative of the row maximum)
+    from oracle import quant
+    w = _rng(20).normal(0.0, 0.02, (96, 200)).astype(np.float32)
+    q, s = synth.quantize_q8_row(w)
+    assert q.dtype == np.int8 and s.dtype == np.float16 and np.abs(q.astype(int)).max() <= 127
+    d = quant.dequant_q8_row(q, s)
+    step = s.astype(np.float64)[:, None]
+    amax = np.abs(w).max(axis=1, keepdims=True)
+    assert np.all(np.abs(d - w) <= step / 2 + amax * 2.0 ** -10)
+    # and the per-row maximum is hit to within that bound
+    np.testing.assert_allclose(np.abs(d).max(axis=1), amax[:, 0], rtol=2e-3)

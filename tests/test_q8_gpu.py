@@ -1,0 +1,86 @@
+"""Blocks and a tower with q8_row weights (int8 payload, float16 row scale)
+on the GPU against the float64 oracle run on the dequantized matrices."""
+import numpy as np
+import pytest
+
+from oracle import block as ob
+from oracle import quant
+from oracle import stack as ost
+from tests import gpu_util as gu
+from vision_transformer_encoder_vit_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+d = synth.derive
+
+SMALL = {
+    # separate q/k/v (three scale segments), tanh-GELU, ragged token count
+    "c4_b2_9x13": d(C["c4_siglip_b8"], batch=2, grid_h=9, grid_w=13, dim_in=192, dim_out=192, heads=3, mlp=768),
+    # spatial windows with RoPE, fused qkv
+    "c5w_48x48": d(C["c5w_sam3_win"], grid_h=48, grid_w=48, dim_in=256, dim_out=256, heads=4, mlp=1152),
+    # global with keys split over workgroups (small grid)
+    "c5g_10x20": d(C["c5g_sam3_global"], grid_h=10, grid_w=20, dim_in=256, dim_out=256, heads=4, mlp=1024),
+    # Hiera stage 2 at full size and the stage 2 -> 3 transition (residual
+    # projection and 2x2 pool with int8 weights)
+    "c3b_hiera_s2": C["c3b_hiera_s2"],
+    "hiera_trans_448_896": d(C["c3b_hiera_s2"], grid_h=32, grid_w=32, dim_in=448, dim_out=896, heads=16,
+                             mlp=3584, q_stride=4),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_q8_block_every_seam(name):
+    spec = dict(SMALL[name], weights="q8_row")
+    print("case q8", name, flush=True)
+    inp = synth.make_q8_inputs(spec, seed=0)
+    ref = ob.block_forward(inp["x"], quant.dequant_block(inp), spec)
+    y, seams = gu.run_block(spec, gu.to_device(inp, spec))
+    for k, t in seams.items():
+        gu.check(name + ":" + k, gu.to64(t), ref[k], spec)
+    mx, rel = gu.check(name + ":y", gu.to64(y), ref["y"], spec)
+    print("  y max abs %.3e rel %.3e" % (mx, rel))
+
+
+def _sample_rows(n, count, seed):
+    r = np.random.default_rng(seed)
+    return np.array(sorted(set([0, n - 1, n // 2]) | set(r.choice(n, size=min(count, n), replace=False).tolist())))
+
+
+@pytest.mark.parametrize("name", ["c4_siglip_b8", "c5w_sam3_win", "c5g_sam3_global"])
+def test_q8_block_full_size_sampled_rows(name):
+    spec = dict(C[name], weights="q8_row")
+    print("case q8 full", name, flush=True)
+    inp = synth.make_q8_inputs(spec, seed=1)
+    y, seams = gu.run_block(spec, gu.to_device(inp, spec))
+    rows = _sample_rows(synth.out_tokens(spec), 40, 2)
+    ref = ob.block_forward_rows(inp["x"], quant.dequant_block(inp), spec, rows)
+    for k in ("ctx", "x1", "u", "y"):
+        got = gu.to64(y if k == "y" else seams[k])[:, rows]
+        gu.check(name + ":" + k, got, ref[k], spec)
+
+
+def test_q8_siglip_tower_full_frame():
+    # 12 blocks with int8 weights plus post_layernorm, one full frame
+    import torch
+    from vision_transformer_encoder_vit_amd import binding as vb
+    specs = [dict(s, weights="q8_row") for s in synth.siglip_tower(batch=1)]
+    x, _ = synth.make_stack_inputs(specs, seed=5)
+    blocks = [synth.make_q8_inputs(s, seed=5 * 1000 + i) for i, s in enumerate(specs)]
+    dev_w = [gu.to_device(w, sp) for w, sp in zip(blocks, specs)]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    st = vb.Stack([vb.desc_from_spec(s) for s in specs], 0, [11])
+    y = torch.empty_like(xd)
+    ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+    st.forward([vb.weights_struct(w) for w in dev_w], xd, [y], ws)
+    ln = synth.make_layernorm_params(768, 5)
+    g, b = (torch.from_numpy(a).cuda() for a in ln)
+    vb.vit_layernorm(y, y, g, b, specs[-1]["eps"])
+    torch.cuda.synchronize()
+    st.close()
+    ref = ost.tower_forward(x, [quant.dequant_block(w) for w in blocks], specs, post_ln=ln)
+    a, r = gu.to64(y).ravel(), ref.ravel()
+    cos = float(a @ r / np.sqrt((a @ a) * (r @ r)))
+    nrel = float(np.linalg.norm(a - r) / np.linalg.norm(r))
+    print("q8 siglip tower: cos %.7f norm-rel %.2e" % (cos, nrel))
+    assert cos >= 0.9999 and nrel <= 2e-2

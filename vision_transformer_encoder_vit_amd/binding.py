@@ -17,6 +17,7 @@ VIT_ATTN_GLOBAL, VIT_ATTN_MASK_UNIT, VIT_ATTN_SPATIAL = 0, 1, 2
 VIT_GELU_ERF, VIT_GELU_TANH = 0, 1
 VIT_QKV_FUSED, VIT_QKV_SEPARATE = 0, 1
 VIT_ROPE_NONE, VIT_ROPE_AXIAL_TABLE = 0, 1
+VIT_WEIGHTS_ACT, VIT_WEIGHTS_Q8_ROW = 0, 1
 VIT_PIXELS_NCHW, VIT_PIXELS_NHWC = 0, 1
 VIT_CONV_OIHW, VIT_CONV_OHWI = 0, 1
 VIT_POS_NONE, VIT_POS_ROWS, VIT_POS_BUCKET, VIT_POS_TILE = 0, 1, 2, 3
@@ -31,12 +32,13 @@ class vit_block_desc(ctypes.Structure):
                 ("dim_out", _i32), ("heads", _i32), ("mlp_hidden", _i32), ("attn_mode", _i32),
                 ("n_windows", _i32), ("win_h", _i32), ("win_w", _i32), ("q_stride", _i32),
                 ("gelu", _i32), ("qkv_layout", _i32), ("rope", _i32), ("rope_rows", _i32),
-                ("ln_eps", _f32), ("attn_scale", _f32), ("act_dtype", _i32)]
+                ("ln_eps", _f32), ("attn_scale", _f32), ("act_dtype", _i32), ("weight_format", _i32)]
 
 
 WEIGHT_FIELDS = ["ln1_gamma", "ln1_beta", "w_res", "b_res", "w_qkv", "b_qkv", "w_q", "b_q",
                  "w_k", "b_k", "w_v", "b_v", "w_o", "b_o", "ln2_gamma", "ln2_beta", "w_fc1",
-                 "b_fc1", "w_fc2", "b_fc2", "rope_table"]
+                 "b_fc1", "w_fc2", "b_fc2", "rope_table", "s_res", "s_qkv", "s_q", "s_k", "s_v", "s_o",
+                 "s_fc1", "s_fc2"]
 
 
 class vit_block_weights(ctypes.Structure):
@@ -141,7 +143,8 @@ def desc_from_spec(spec):
         qkv_layout=VIT_QKV_SEPARATE if spec.get("qkv") == "separate" else VIT_QKV_FUSED,
         rope=VIT_ROPE_AXIAL_TABLE if spec.get("rope") else VIT_ROPE_NONE, rope_rows=rope_rows,
         ln_eps=spec["eps"], attn_scale=spec.get("scale") or 0.0,
-        act_dtype=VIT_DTYPE_BF16 if spec["dtype"] == "bf16" else VIT_DTYPE_F32)
+        act_dtype=VIT_DTYPE_BF16 if spec["dtype"] == "bf16" else VIT_DTYPE_F32,
+        weight_format=VIT_WEIGHTS_Q8_ROW if spec.get("weights") == "q8_row" else VIT_WEIGHTS_ACT)
 
 
 # names of the synthetic input dict -> vit_block_weights members
@@ -149,7 +152,8 @@ WEIGHT_NAMES = {"ln1_g": "ln1_gamma", "ln1_b": "ln1_beta", "res_w": "w_res", "re
                 "qkv_w": "w_qkv", "qkv_b": "b_qkv", "q_w": "w_q", "q_b": "b_q", "k_w": "w_k",
                 "k_b": "b_k", "v_w": "w_v", "v_b": "b_v", "o_w": "w_o", "o_b": "b_o",
                 "ln2_g": "ln2_gamma", "ln2_b": "ln2_beta", "fc1_w": "w_fc1", "fc1_b": "b_fc1",
-                "fc2_w": "w_fc2", "fc2_b": "b_fc2", "rope": "rope_table"}
+                "fc2_w": "w_fc2", "fc2_b": "b_fc2", "rope": "rope_table", "res_s": "s_res", "qkv_s": "s_qkv",
+                "q_s": "s_q", "k_s": "s_k", "v_s": "s_v", "o_s": "s_o", "fc1_s": "s_fc1", "fc2_s": "s_fc2"}
 
 
 def weights_struct(tensors):

@@ -112,6 +112,14 @@ static vit_status validate_desc(const vit_block_desc* d) {
   }
   if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps)) return fail(VIT_ERR_INVALID_ARG, "ln_eps must be positive and finite");
   if (!(d->attn_scale >= 0.f) || !std::isfinite(d->attn_scale)) return fail(VIT_ERR_INVALID_ARG, "attn_scale must be >= 0 and finite");
+  if (d->weight_format != VIT_WEIGHTS_ACT && d->weight_format != VIT_WEIGHTS_Q8_ROW)
+    return fail(VIT_ERR_INVALID_ARG, "weight_format %d is not a VIT_WEIGHTS_* value", d->weight_format);
+  if (d->weight_format == VIT_WEIGHTS_Q8_ROW) {
+    if (d->act_dtype != VIT_DTYPE_BF16) return fail(VIT_ERR_UNSUPPORTED, "Q8_ROW weights need VIT_DTYPE_BF16 activations");
+    if (d->dim_in % 64 || d->dim_out % 64 || d->mlp_hidden % 64)
+      return fail(VIT_ERR_UNSUPPORTED, "Q8_ROW weights need dim_in %d, dim_out %d, mlp_hidden %d multiples of 64",
+                  d->dim_in, d->dim_out, d->mlp_hidden);
+  }
   const int64_t widest = std::max<int64_t>(std::max<int64_t>(3LL * d->dim_out, d->mlp_hidden), d->dim_in);
   if ((int64_t)d->batch * n_in * widest >= (1LL << 40) || (int64_t)d->batch * n_in >= (1LL << 31))
     return fail(VIT_ERR_UNSUPPORTED, "problem too large");
@@ -164,7 +172,8 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   p->off_po = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, d.dim_out * fp32_cols) : 0;
   p->off_pml = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, 2LL * d.heads * fp32_cols) : 0;
   p->ws_bytes = o;
-  p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 && d.attn_mode == VIT_ATTN_MASK_UNIT && d.q_stride == 1 &&
+  p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 && d.weight_format == VIT_WEIGHTS_ACT &&
+                       d.attn_mode == VIT_ATTN_MASK_UNIT && d.q_stride == 1 &&
                        d.rope == VIT_ROPE_NONE &&
                        vit::fused_mask_unit_supported(d.dim_out, d.heads, p->head_dim, d.mlp_hidden, p->n_in / d.n_windows) &&
                        vit::fused_mask_unit_lds_bytes(d.dim_out, d.mlp_hidden) <= 160 * 1024;
@@ -198,6 +207,7 @@ VIT_API const char* vit_last_error(void) { return g_err.c_str(); }
 static vit_status check_weights(const vit_block_plan* p, const vit_block_weights* w) {
   if (!w) return fail(VIT_ERR_INVALID_ARG, "weights struct is NULL");
   const vit_block_desc& d = p->d;
+  const bool q8 = d.weight_format == VIT_WEIGHTS_Q8_ROW;
   struct Need {
     const void* ptr;
     const char* name;
@@ -224,6 +234,14 @@ static vit_status check_weights(const vit_block_plan* p, const vit_block_weights
       {w->w_fc2, "w_fc2", true},
       {w->b_fc2, "b_fc2", true},
       {w->rope_table, "rope_table", d.rope == VIT_ROPE_AXIAL_TABLE},
+      {w->s_res, "s_res", q8 && d.q_stride == 4},
+      {w->s_qkv, "s_qkv", q8 && d.qkv_layout == VIT_QKV_FUSED},
+      {w->s_q, "s_q", q8 && d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->s_k, "s_k", q8 && d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->s_v, "s_v", q8 && d.qkv_layout == VIT_QKV_SEPARATE},
+      {w->s_o, "s_o", q8},
+      {w->s_fc1, "s_fc1", q8},
+      {w->s_fc2, "s_fc2", q8},
   };
   for (const Need& n : need) {
     if (!n.needed) continue;
@@ -239,6 +257,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   if (!plan) return fail(VIT_ERR_INVALID_ARG, "plan is NULL");
   const vit_block_plan& P = *plan;
   const vit_block_desc& d = P.d;
+  const bool q8 = d.weight_format == VIT_WEIGHTS_Q8_ROW;
   vit_status st = check_weights(&P, w);
   if (st != VIT_OK) return st;
   if (!x || !y) return fail(VIT_ERR_INVALID_ARG, "x or y is NULL");
@@ -356,9 +375,11 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g.K = Di;
   g.C = qkv;
   g.ldc = 3 * Do;
+  g.q8 = q8;
   if (d.qkv_layout == VIT_QKV_FUSED) {
     g.W[0] = w->w_qkv;
     g.bias[0] = w->b_qkv;
+    g.wscale[0] = w->s_qkv;
     g.seg_cols = 3 * Do;
   } else {
     g.W[0] = w->w_q;
@@ -367,6 +388,9 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     g.bias[0] = w->b_q;
     g.bias[1] = w->b_k;
     g.bias[2] = w->b_v;
+    g.wscale[0] = w->s_q;
+    g.wscale[1] = w->s_k;
+    g.wscale[2] = w->s_v;
     g.seg_cols = Do;
   }
   if (d.rope == VIT_ROPE_AXIAL_TABLE) {
@@ -412,6 +436,8 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     gr.K = Di;
     gr.W[0] = w->w_res;
     gr.bias[0] = w->b_res;
+    gr.q8 = q8;
+    gr.wscale[0] = w->s_res;
     gr.seg_cols = Do;
     gr.C = base + P.off_rp;
     gr.ldc = Do;
@@ -473,6 +499,8 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   go.K = Do;
   go.W[0] = w->w_o;
   go.bias[0] = w->b_o;
+  go.q8 = q8;
+  go.wscale[0] = w->s_o;
   go.seg_cols = Do;
   go.C = x1;
   go.ldc = Do;
@@ -498,6 +526,8 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g1.K = Do;
   g1.W[0] = w->w_fc1;
   g1.bias[0] = w->b_fc1;
+  g1.q8 = q8;
+  g1.wscale[0] = w->s_fc1;
   g1.seg_cols = F;
   g1.C = u;
   g1.ldc = F;
@@ -514,6 +544,8 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g2.K = F;
   g2.W[0] = w->w_fc2;
   g2.bias[0] = w->b_fc2;
+  g2.q8 = q8;
+  g2.wscale[0] = w->s_fc2;
   g2.seg_cols = Do;
   g2.C = y;
   g2.ldc = Do;

@@ -64,6 +64,11 @@ struct GemmArgs {
   // on a grid grid_w wide
   const float* pos = nullptr;
   int pos_mode = POS_NONE, pos_side = 0;
+  // int8 weights (q8_row): W[s] are int8 [rows, K], wscale[s] float16 bits
+  // [rows], W[n, k] = int8 * scale[n]; bf16 activations with K % 64 == 0
+  // (the MFMA kernel), not with EPI_BIAS_POS
+  bool q8 = false;
+  const void* wscale[3] = {nullptr, nullptr, nullptr};
 };
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 

@@ -315,3 +315,24 @@ def make_stem_inputs(spec, seed=0):
             a = bf16_round(a)
         out[name] = a
     return out
+
+
+# q8_row weights (the SAM3 page's quantized tensor type: one int8 per element
+# and a float16 scale per row). Synthetic checkpoints are made the way a
+# converter would: per row, scale = max|w| / 127 rounded to float16, payload
+# = w / scale rounded to the nearest integer and clipped to [-127, 127].
+def quantize_q8_row(w):
+    w = np.asarray(w, dtype=np.float64)
+    amax = np.abs(w).max(axis=1)
+    scale = np.where(amax > 0, amax / 127.0, 1.0).astype(np.float16)
+    q = np.clip(np.rint(w / scale.astype(np.float64)[:, None]), -127, 127).astype(np.int8)
+    return q, scale
+
+
+def make_q8_inputs(spec, seed=0, qk_gain=1.0):
+    """make_inputs with every weight matrix "<name>_w" replaced by its int8
+    payload and a float16 row scale under "<name>_s"."""
+    out = make_inputs(spec, seed, qk_gain)
+    for name in [k for k in out if k.endswith("_w")]:
+        out[name], out[name[:-2] + "_s"] = quantize_q8_row(out[name])
+    return out
