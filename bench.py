@@ -47,6 +47,8 @@ def describe(spec):
         extra.append("axial RoPE")
     if spec["qkv"] == "separate":
         extra.append("separate q/k/v")
+    if spec.get("weights") == "q8_row":
+        extra.append("q8_row int8 weights")
     return "%s: %d x %dx%d tokens (%d), D %d, %d heads x %d, %s, MLP %d %s-GELU%s" % (
         spec["name"], spec["batch"], spec["grid_h"], spec["grid_w"], n, spec["dim_out"], spec["heads"],
         spec["dim_out"] // spec["heads"], mode, spec["mlp"], spec["gelu"],
@@ -136,11 +138,12 @@ def run(spec, steps, warmup, with_cpu):
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
-    inp = synth.make_inputs(spec, seed=0)
+    q8 = spec.get("weights") == "q8_row"
+    inp = synth.make_q8_inputs(spec, seed=0) if q8 else synth.make_inputs(spec, seed=0)
     dev = {}
     for k, a in inp.items():
         t = torch.from_numpy(np.ascontiguousarray(a))
-        dev[k] = (t.to(dt) if (k == "x" or k.endswith("_w")) else t).cuda()
+        dev[k] = (t.to(dt) if (k == "x" or k.endswith("_w")) and a.dtype != np.int8 else t).cuda()
     plan = vb.Plan(vb.desc_from_spec(spec))
     active = [n for i, n in enumerate(vb.STAGES) if plan.stage_mask() >> i & 1]
     w = vb.weights_struct(dev)
@@ -267,7 +270,7 @@ def tower_parts(kind):
     return synth.STEMS[kind], specs, levels, taps, pre, post
 
 
-def run_tower(kind, steps, warmup, with_cpu):
+def run_tower(kind, steps, warmup, with_cpu, q8=False):
     """A whole vision tower from pixels: vit_patch_embed, then (SAM3) ln_pre
     through vit_layernorm, the blocks through vit_stack_forward, then
     (SigLIP) post_layernorm. K event-free forwards timed like the block
@@ -277,12 +280,17 @@ def run_tower(kind, steps, warmup, with_cpu):
     from vision_transformer_encoder_vit_amd import binding as vb
     from vision_transformer_encoder_vit_amd import synth, work
     stem, specs, levels, taps, pre, post = tower_parts(kind)
+    if q8:
+        specs = [dict(s, weights="q8_row") for s in specs]
     sin = synth.make_stem_inputs(stem, seed=0)
-    _, blocks = synth.make_stack_inputs(specs, seed=0)
+    blocks = [(synth.make_q8_inputs if s.get("weights") == "q8_row" else synth.make_inputs)(s, seed=i)
+              for i, s in enumerate(specs)]
+    for b in blocks:
+        del b["x"]
     dt = torch.bfloat16
     dev_w = []
     for w in blocks:
-        dev_w.append({k: (torch.from_numpy(np.ascontiguousarray(a)).to(dt) if k.endswith("_w")
+        dev_w.append({k: (torch.from_numpy(np.ascontiguousarray(a)).to(dt) if k.endswith("_w") and a.dtype != np.int8
                           else torch.from_numpy(np.ascontiguousarray(a))).cuda() for k, a in w.items()})
     weights = [vb.weights_struct(w) for w in dev_w]
     px = torch.from_numpy(sin["pixels"]).cuda()
@@ -334,13 +342,15 @@ def run_tower(kind, steps, warmup, with_cpu):
     K = stem["in_ch"] * stem["kernel"] ** 2
     stem_flops = 2.0 * B * oh * ow * stem["dim"] * K
     flops = sum(work.block_flops(s) for s in specs) + stem_flops
+    n_q8 = sum(s.get("weights") == "q8_row" for s in specs)
     line = {"metric": "%s tower from pixels, input tokens/sec, 1 GPU" % kind, "value": B * N0 / dt_step,
             "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": 1e3 * dt_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": TOWERS[kind], "batch": B, "tokens_per_frame": N0, "parallelism": "none (1 GPU)"},
+            "config": {"workload": TOWERS[kind], "batch": B, "tokens_per_frame": N0, "parallelism": "none (1 GPU)",
+                       "weights": "q8_row in %d of %d blocks" % (n_q8, len(specs)) if n_q8 else "bf16"},
             "tflops": flops / dt_step / 1e12, "pct_of_bf16_peak": 100.0 * flops / dt_step / 1e12 / PEAK_BF16_TFLOPS,
             "stem_us": round(stem_us, 2), "stem_tflops": round(stem_flops / stem_us / 1e6, 1)}
-    if with_cpu and kind in ("hiera", "siglip"):
+    if with_cpu and kind in ("hiera", "siglip") and not n_q8:
         # the float64 oracle on one frame (SigLIP: frame 0 of the 8; the
         # SAM3 trunk's 32 full-size layers would take minutes and is skipped)
         from oracle import stack as ost
@@ -425,6 +435,8 @@ def main():
                     help="time a whole tower from pixels (patch embed, then hiera: the 24-block stage stack at "
                          "512x512; sam3: ln_pre and the 32-layer trunk; siglip: the 12-layer tower and "
                          "post_layernorm) instead of one block")
+    ap.add_argument("--weights", choices=["bf16", "q8_row"], default="bf16",
+                    help="weight matrices in bf16, or as q8_row int8 payloads with float16 row scales")
     ap.add_argument("--rowops", action="store_true",
                     help="only time LayerNorm, unroll, reroll and pool4 on HBM-resident working sets")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -432,7 +444,7 @@ def main():
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported (use --gpus 1)" % args.gpus,
+        print("bench.py runs on one GPU only; --gpus %d is not supported (use --gpus 1)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
@@ -441,7 +453,8 @@ def main():
         rowops_cold(args.steps)
         return
     if args.tower:
-        print(json.dumps(run_tower(args.tower, args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
+        print(json.dumps(run_tower(args.tower, args.steps, args.warmup, not args.no_cpu_baseline,
+                                   q8=args.weights == "q8_row")), flush=True)
         return
     if args.copy_calibration:
         copy_calibration(args.steps)
@@ -452,8 +465,11 @@ def main():
         if n not in synth.CONFIGS:
             ap.error("unknown workload %s (choose from %s)" % (n, ", ".join(synth.CONFIGS)))
     for n in names:
-        with_cpu = not args.no_cpu_baseline and n == names[0]
-        print(json.dumps(run(synth.CONFIGS[n], args.steps, args.warmup, with_cpu)), flush=True)
+        spec = synth.CONFIGS[n]
+        if args.weights == "q8_row":
+            spec = dict(spec, weights="q8_row")
+        with_cpu = not args.no_cpu_baseline and n == names[0] and args.weights == "bf16"
+        print(json.dumps(run(spec, args.steps, args.warmup, with_cpu)), flush=True)
 
 
 if __name__ == "__main__":

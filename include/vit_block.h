@@ -80,10 +80,13 @@ enum { VIT_ROPE_NONE = 0, VIT_ROPE_AXIAL_TABLE = 1 };
 /* Weight matrix storage. Q8_ROW is the SAM3 page's `q8_row` tensor type
  * (cortiq-engine sam3.rs, `bad_scales`: a [rows, cols] payload of one byte
  * per element followed by one float16 scale per row): here the int8 payload
- * and the scales are two arrays, and W[r, c] = payload[r, c] * scale[r]. The
- * kernels multiply int8 (exact in bf16) by bf16 activations with float32
- * accumulation and apply the scale per output column in the epilogue, so
- * the result is that of the dequantized matrix up to float32 rounding. */
+ * and the scales are two arrays, and W[r, c] = payload[r, c] * scale[r].
+ * Each forward first copies the payloads into the workspace as act_dtype
+ * (exact: |q| <= 128 has at most 8 significant bits), the GEMMs multiply
+ * them with float32 accumulation and apply the scale per output column
+ * before the bias, so the result is that of the dequantized matrix up to
+ * float32 rounding. Any act_dtype; the single-kernel mask-unit path is not
+ * used with Q8_ROW. */
 enum { VIT_WEIGHTS_ACT = 0, VIT_WEIGHTS_Q8_ROW = 1 };
 
 /* Shape and options of one block. Validated by vit_block_create. */
@@ -116,9 +119,7 @@ typedef struct vit_block_desc {
   int32_t act_dtype;   /* VIT_DTYPE_F32 or VIT_DTYPE_BF16                   */
   int32_t weight_format; /* VIT_WEIGHTS_ACT (0): matrices in act_dtype;
                           VIT_WEIGHTS_Q8_ROW: int8 matrices with a float16
-                          scale per output row (see vit_block_weights);
-                          needs VIT_DTYPE_BF16 and dim_in, dim_out,
-                          mlp_hidden multiples of 64                        */
+                          scale per output row (see vit_block_weights)     */
 } vit_block_desc;
 
 /* Device pointers to one block's parameters. Unused members may be NULL.

@@ -62,8 +62,6 @@ BAD = [
     (dict(act_dtype=9), vb.VIT_ERR_INVALID_ARG, "act_dtype"),
     (dict(rope=0, q_stride=4, dim_in=512), vb.VIT_ERR_UNSUPPORTED, "SPATIAL"),
     (dict(weight_format=3), vb.VIT_ERR_INVALID_ARG, "weight_format"),
-    (dict(weight_format=vb.VIT_WEIGHTS_Q8_ROW, act_dtype=vb.VIT_DTYPE_F32), vb.VIT_ERR_UNSUPPORTED, "BF16"),
-    (dict(weight_format=vb.VIT_WEIGHTS_Q8_ROW, mlp_hidden=4712), vb.VIT_ERR_UNSUPPORTED, "multiples of 64"),
 ]
 
 
@@ -290,7 +288,13 @@ def test_q8_forward_needs_every_scale():
         setattr(w, drop, None)
         st, _ = _forward(spec, w, 0x10000000, 0x20000000, 0x30000000, 1 << 30)
         assert st == vb.VIT_ERR_INVALID_ARG and drop in vb.last_error(), (name, drop, vb.last_error())
-    # and a block whose widths are not multiples of 64 cannot take them
-    spec = dict(synth.CONFIGS["c2_hiera_s0"], weights="q8_row")
-    h = ctypes.c_void_p()
-    assert vb.lib.vit_block_create(ctypes.byref(vb.desc_from_spec(spec)), ctypes.byref(h)) == vb.VIT_ERR_UNSUPPORTED
+    # the workspace grows by the act_dtype copies of the payloads, and the
+    # single-kernel mask-unit path is not used
+    spec = synth.CONFIGS["c2_hiera_s0"]
+    p8, pb = vb.Plan(vb.desc_from_spec(dict(spec, weights="q8_row"))), vb.Plan(vb.desc_from_spec(spec))
+    D, F = spec["dim_out"], spec["mlp"]
+    mats = [(3 * D, D), (D, D), (F, D), (D, F)]
+    assert p8.workspace_bytes - pb.workspace_bytes >= sum(2 * r * c for r, c in mats)
+    assert pb.stage_mask() == 1 << vb.STAGES.index("fused") and p8.stage_mask() & (1 << vb.STAGES.index("qkv"))
+    p8.close()
+    pb.close()

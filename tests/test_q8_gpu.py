@@ -26,6 +26,13 @@ SMALL = {
     "c3b_hiera_s2": C["c3b_hiera_s2"],
     "hiera_trans_448_896": d(C["c3b_hiera_s2"], grid_h=32, grid_w=32, dim_in=448, dim_out=896, heads=16,
                              mlp=3584, q_stride=4),
+    # widths off the 64 grid: Hiera stage 0 mask units (step kernels, not the
+    # single-kernel path) and the stage 0 -> 1 transition
+    "c2_32x32": d(C["c2_hiera_s0"], grid_h=32, grid_w=32, n_windows=16),
+    "c3a_16x16": d(C["c3a_hiera_trans"], grid_h=16, grid_w=16, n_windows=16),
+    # float32 activations with int8 weights
+    "c4_f32": d(C["c4_siglip_b8"], batch=2, grid_h=10, grid_w=10, dim_in=128, dim_out=128, heads=2, mlp=512,
+                dtype="f32"),
 }
 
 

@@ -61,6 +61,9 @@ struct vit_block_plan {
   bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
   bool attn_vt;          // the large-window attention kernel runs on V^T (workspace off_vt)
   bool vt_in_gemm;       // ... written by the qkv projection's epilogue (else a transpose kernel)
+  // Q8_ROW: workspace copies of the int8 payloads in act_dtype (exact), read
+  // by the GEMMs, whose epilogues apply the row scales
+  size_t off_cres, off_cqkv, off_cq, off_ck, off_cv, off_co, off_c1, off_c2;
 };
 
 static vit_status validate_desc(const vit_block_desc* d) {
@@ -114,12 +117,6 @@ static vit_status validate_desc(const vit_block_desc* d) {
   if (!(d->attn_scale >= 0.f) || !std::isfinite(d->attn_scale)) return fail(VIT_ERR_INVALID_ARG, "attn_scale must be >= 0 and finite");
   if (d->weight_format != VIT_WEIGHTS_ACT && d->weight_format != VIT_WEIGHTS_Q8_ROW)
     return fail(VIT_ERR_INVALID_ARG, "weight_format %d is not a VIT_WEIGHTS_* value", d->weight_format);
-  if (d->weight_format == VIT_WEIGHTS_Q8_ROW) {
-    if (d->act_dtype != VIT_DTYPE_BF16) return fail(VIT_ERR_UNSUPPORTED, "Q8_ROW weights need VIT_DTYPE_BF16 activations");
-    if (d->dim_in % 64 || d->dim_out % 64 || d->mlp_hidden % 64)
-      return fail(VIT_ERR_UNSUPPORTED, "Q8_ROW weights need dim_in %d, dim_out %d, mlp_hidden %d multiples of 64",
-                  d->dim_in, d->dim_out, d->mlp_hidden);
-  }
   const int64_t widest = std::max<int64_t>(std::max<int64_t>(3LL * d->dim_out, d->mlp_hidden), d->dim_in);
   if ((int64_t)d->batch * n_in * widest >= (1LL << 40) || (int64_t)d->batch * n_in >= (1LL << 31))
     return fail(VIT_ERR_UNSUPPORTED, "problem too large");
@@ -171,6 +168,17 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   const int64_t fp32_cols = 4 / p->esize;
   p->off_po = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, d.dim_out * fp32_cols) : 0;
   p->off_pml = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, 2LL * d.heads * fp32_cols) : 0;
+  if (d.weight_format == VIT_WEIGHTS_Q8_ROW) {
+    const int64_t Di = d.dim_in, Do = d.dim_out, F = d.mlp_hidden;
+    p->off_cres = d.q_stride == 4 ? take(Do, Di) : 0;
+    p->off_cqkv = d.qkv_layout == VIT_QKV_FUSED ? take(3 * Do, Di) : 0;
+    p->off_cq = d.qkv_layout == VIT_QKV_SEPARATE ? take(Do, Di) : 0;
+    p->off_ck = d.qkv_layout == VIT_QKV_SEPARATE ? take(Do, Di) : 0;
+    p->off_cv = d.qkv_layout == VIT_QKV_SEPARATE ? take(Do, Di) : 0;
+    p->off_co = take(Do, Do);
+    p->off_c1 = take(F, Do);
+    p->off_c2 = take(Do, F);
+  }
   p->ws_bytes = o;
   p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 && d.weight_format == VIT_WEIGHTS_ACT &&
                        d.attn_mode == VIT_ATTN_MASK_UNIT && d.q_stride == 1 &&
@@ -362,8 +370,38 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   }
   auto only_stop = [](vit::StageEvents ev) { ev.start = nullptr; return ev; };
 
+  // 0. Q8_ROW: the int8 payloads to act_dtype (exact) in the workspace, one
+  // launch for all matrices (timed with LN1's stage)
+  const void* Wres = w->w_res;
+  const void *Wqkv = w->w_qkv, *Wq = w->w_q, *Wk = w->w_k, *Wv = w->w_v;
+  const void *Wo = w->w_o, *W1 = w->w_fc1, *W2 = w->w_fc2;
+  if (q8) {
+    vit::I8Segments sg;
+    auto add = [&](const void*& wp, size_t off, int64_t n) {
+      sg.src[sg.count] = static_cast<const int8_t*>(wp);
+      sg.dst[sg.count] = base + off;
+      sg.n[sg.count] = n;
+      ++sg.count;
+      wp = base + off;
+    };
+    if (d.q_stride == 4) add(Wres, P.off_cres, (int64_t)Do * Di);
+    if (d.qkv_layout == VIT_QKV_FUSED) {
+      add(Wqkv, P.off_cqkv, 3LL * Do * Di);
+    } else {
+      add(Wq, P.off_cq, (int64_t)Do * Di);
+      add(Wk, P.off_ck, (int64_t)Do * Di);
+      add(Wv, P.off_cv, (int64_t)Do * Di);
+    }
+    add(Wo, P.off_co, (int64_t)Do * Do);
+    add(W1, P.off_c1, (int64_t)F * Do);
+    add(W2, P.off_c2, (int64_t)Do * F);
+    e = vit::launch_i8_convert(sg, dt, s, only_start(stage_ev(VIT_STAGE_LN1)));
+    if ((st = device_status(e, "q8_row payload conversion")) != VIT_OK) return st;
+  }
+
   // 1. LN1
-  e = vit::launch_layernorm(x, h, w->ln1_gamma, w->ln1_beta, P.m_in, Di, d.ln_eps, dt, s, stage_ev(VIT_STAGE_LN1));
+  e = vit::launch_layernorm(x, h, w->ln1_gamma, w->ln1_beta, P.m_in, Di, d.ln_eps, dt, s,
+                            q8 ? only_stop(stage_ev(VIT_STAGE_LN1)) : stage_ev(VIT_STAGE_LN1));
   if ((st = device_status(e, "layernorm (LN1)")) != VIT_OK) return st;
 
   // 2. qkv projection (+ bias, + RoPE)
@@ -375,22 +413,23 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g.K = Di;
   g.C = qkv;
   g.ldc = 3 * Do;
-  g.q8 = q8;
   if (d.qkv_layout == VIT_QKV_FUSED) {
-    g.W[0] = w->w_qkv;
+    g.W[0] = Wqkv;
     g.bias[0] = w->b_qkv;
-    g.wscale[0] = w->s_qkv;
+    g.wscale[0] = q8 ? w->s_qkv : nullptr;
     g.seg_cols = 3 * Do;
   } else {
-    g.W[0] = w->w_q;
-    g.W[1] = w->w_k;
-    g.W[2] = w->w_v;
+    g.W[0] = Wq;
+    g.W[1] = Wk;
+    g.W[2] = Wv;
     g.bias[0] = w->b_q;
     g.bias[1] = w->b_k;
     g.bias[2] = w->b_v;
-    g.wscale[0] = w->s_q;
-    g.wscale[1] = w->s_k;
-    g.wscale[2] = w->s_v;
+    if (q8) {
+      g.wscale[0] = w->s_q;
+      g.wscale[1] = w->s_k;
+      g.wscale[2] = w->s_v;
+    }
     g.seg_cols = Do;
   }
   if (d.rope == VIT_ROPE_AXIAL_TABLE) {
@@ -434,10 +473,9 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     gr.M = (int)P.m_in;
     gr.N = Do;
     gr.K = Di;
-    gr.W[0] = w->w_res;
+    gr.W[0] = Wres;
     gr.bias[0] = w->b_res;
-    gr.q8 = q8;
-    gr.wscale[0] = w->s_res;
+    gr.wscale[0] = q8 ? w->s_res : nullptr;
     gr.seg_cols = Do;
     gr.C = base + P.off_rp;
     gr.ldc = Do;
@@ -497,10 +535,9 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   go.M = (int)P.m_out;
   go.N = Do;
   go.K = Do;
-  go.W[0] = w->w_o;
+  go.W[0] = Wo;
   go.bias[0] = w->b_o;
-  go.q8 = q8;
-  go.wscale[0] = w->s_o;
+  go.wscale[0] = q8 ? w->s_o : nullptr;
   go.seg_cols = Do;
   go.C = x1;
   go.ldc = Do;
@@ -524,10 +561,9 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g1.M = (int)P.m_out;
   g1.N = F;
   g1.K = Do;
-  g1.W[0] = w->w_fc1;
+  g1.W[0] = W1;
   g1.bias[0] = w->b_fc1;
-  g1.q8 = q8;
-  g1.wscale[0] = w->s_fc1;
+  g1.wscale[0] = q8 ? w->s_fc1 : nullptr;
   g1.seg_cols = F;
   g1.C = u;
   g1.ldc = F;
@@ -542,10 +578,9 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   g2.M = (int)P.m_out;
   g2.N = Do;
   g2.K = F;
-  g2.W[0] = w->w_fc2;
+  g2.W[0] = W2;
   g2.bias[0] = w->b_fc2;
-  g2.q8 = q8;
-  g2.wscale[0] = w->s_fc2;
+  g2.wscale[0] = q8 ? w->s_fc2 : nullptr;
   g2.seg_cols = Do;
   g2.C = y;
   g2.ldc = Do;

@@ -43,8 +43,9 @@ struct GemmParams {
   bool vt_only;
   const float* pos;  // EPI_BIAS_POS: table [rows, N]
   int pos_mode, pos_side;
-  // int8 weights (q8_row): W0..W2 hold int8 rows of K bytes, scaled per
-  // output column by the float16 ws0..ws2 (MFMA kernel only)
+  // optional float16 scale per output column (per weight row), applied to
+  // the accumulator before the bias: weights given as integers (q8_row
+  // payloads converted exactly) times a row scale
   const _Float16* ws0;
   const _Float16* ws1;
   const _Float16* ws2;
@@ -175,6 +176,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
       const int seg = n / p.seg_cols;
       const float* bb = seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2);
       f32x4 v = acc[i][j];
+      if (p.ws0 != nullptr) {
+        const _Float16* sc = (seg == 0 ? p.ws0 : (seg == 1 ? p.ws1 : p.ws2)) + (n - seg * p.seg_cols);
+        v *= f32x4{(float)sc[0], (float)sc[1], (float)sc[2], (float)sc[3]};
+      }
       if (EPI != EPI_BIAS_POS || bb != nullptr) v += *reinterpret_cast<const f32x4*>(bb + (n - seg * p.seg_cols));
       if (EPI == EPI_BIAS_POS) {
         if (p.pos_mode != POS_NONE) v += *reinterpret_cast<const f32x4*>(p.pos + (int64_t)pos_row(p, m) * p.N + n);
@@ -252,32 +257,15 @@ struct Interleave {
   }
 };
 
-// 8 int8 (two dwords, little-endian) -> 8 bf16. Integers in [-128, 127] are
-// exact in float32 with at most 8 significant bits, so their bf16 is the
-// upper half of the float32 bits (no rounding).
-__device__ __forceinline__ uint32_t bf16_pair_of_i8(uint32_t w, int sh) {
-  const float a = (float)(int8_t)(w >> sh), b = (float)(int8_t)(w >> (sh + 8));
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-}
-__device__ __forceinline__ u32x4 bf16x8_of_i8x8(uint32_t lo, uint32_t hi) {
-  return u32x4{bf16_pair_of_i8(lo, 0), bf16_pair_of_i8(lo, 16), bf16_pair_of_i8(hi, 0), bf16_pair_of_i8(hi, 16)};
-}
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI, bool QW = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(GemmParams<bf16> p) {
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   constexpr int BK = 64;
   static_assert(ST >= 2 && ST <= 4, "2 to 4 LDS stages");
-  static_assert(!QW || ST == 2, "int8 weights use two LDS stages");
   constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;  // 32x32 tiles per wave
   constexpr int STAGE = (BM + BN) * BK;                          // bf16 elements
-  // direct-to-LDS load instructions per wave per stage: A and W rows, or
-  // only A rows when int8 weights go through registers (converted to bf16
-  // on the way into LDS)
-  constexpr int LPW = (QW ? BM : BM + BN) / (8 * NW);
-  static_assert((QW ? BM : BM + BN) % (8 * NW) == 0, "rows must split evenly over the waves");
-  constexpr int LQ = QW ? BN * 4 / NT : 0;  // 16-byte int8 loads per thread per W tile
-  static_assert(!QW || (BN * 4) % NT == 0, "int8 W tile must split evenly over the threads");
+  constexpr int LPW = (BM + BN) / (8 * NW);                      // load instructions per wave per stage
+  static_assert((BM + BN) % (8 * NW) == 0, "rows must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) bf16 sm[ST * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -292,14 +280,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   // consumed only by a store that never happens (M >= 1 always).
   uint32_t touch = 0;
   {
-    constexpr int WB = QW ? 1 : 2;  // bytes per weight
-    const int row_bytes = p.K * WB, lines_per_row = (row_bytes + 127) / 128;
+    const int lines_per_row = p.K / 64;
     const int64_t lines = (int64_t)p.N * lines_per_row;
     for (int64_t g = (int64_t)blockIdx.x * NT + tid; g < lines; g += (int64_t)gridDim.x * NT) {
       const int n = (int)(g / lines_per_row), kl = (int)(g - (int64_t)n * lines_per_row);
       const int seg = n / p.seg_cols;
-      const char* base = reinterpret_cast<const char*>(seg == 0 ? p.W0 : (seg == 1 ? p.W1 : p.W2));
-      touch ^= *reinterpret_cast<const uint32_t*>(base + (int64_t)(n - seg * p.seg_cols) * row_bytes + kl * 128);
+      const bf16* base = seg == 0 ? p.W0 : (seg == 1 ? p.W1 : p.W2);
+      touch ^= *reinterpret_cast<const uint32_t*>(base + (int64_t)(n - seg * p.seg_cols) * p.K + kl * 64);
     }
   }
 
@@ -329,33 +316,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_ptr)(sm + (kt % ST) * STAGE + (wave * LPW + j) * 512),
                                      16, 0, 0);
   };
-  // int8 weights: thread load j covers 16 bytes (k 16q..16q+15) of W row r
-  const int8_t* qsrc[LQ > 0 ? LQ : 1];
-  u32x4 qreg[LQ > 0 ? LQ : 1];
-#pragma unroll
-  for (int j = 0; j < LQ; ++j) {
-    const int id = j * NT + tid, r = id >> 2, q = id & 3;
-    const int n = min(n0 + r, p.N - 1);
-    const int seg = n / p.seg_cols;
-    const int8_t* base = reinterpret_cast<const int8_t*>(seg == 0 ? p.W0 : (seg == 1 ? p.W1 : p.W2));
-    qsrc[j] = base + (int64_t)(n - seg * p.seg_cols) * p.K + q * 16;
-  }
-  auto qload = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < LQ; ++j) qreg[j] = ld16(qsrc[j] + kt * BK);
-  };
-  // convert to bf16 and write the W rows of `stage` in the layout the
-  // direct loads use (row r, 16-byte chunk c at (c ^ swz(r)))
-  auto qstore = [&](int stage) {
-    bf16* wsm = sm + stage * STAGE + BM * BK;
-#pragma unroll
-    for (int j = 0; j < LQ; ++j) {
-      const int id = j * NT + tid, r = id >> 2, c0 = 2 * (id & 3);
-      st16(wsm + r * 64 + (c0 ^ lds_swz(r)) * 8, bf16x8_of_i8x8(qreg[j][0], qreg[j][1]));
-      st16(wsm + r * 64 + ((c0 + 1) ^ lds_swz(r)) * 8, bf16x8_of_i8x8(qreg[j][2], qreg[j][3]));
-    }
-  };
-
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int fr = lane & 31, g = lane >> 5;
   f32x16 acc[TN][TM];
@@ -384,11 +344,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   constexpr int KS = BK / 16;              // MFMA K steps per tile
   constexpr int LPK = (LPW + 1) / 2;       // tile kt+ST-1's loads per K step, over the first two steps
   // tiles 0 .. ST-2 in flight before the loop
-  if constexpr (QW) qload(0);
   for (int t = 0; t < ST - 1 && t < nk; ++t)
 #pragma unroll
     for (int j = 0; j < LPW; ++j) load(j, t);
-  if constexpr (QW) qstore(0);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of tile kt have landed (the later tiles' loads, issued
     // after them, may still be in flight); after the barrier every wave's
@@ -400,15 +358,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    if constexpr (QW) __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~(0xF << 8));  // this wave's W rows are in LDS
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const bool more = kt + ST - 1 < nk;
     const int stage = kt % ST;
-    if constexpr (QW) {
-      if (more) qload(kt + 1);
-    }
     frags(0, stage, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -430,9 +384,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
         Interleave<0, TN * TM, LPK, 0>::go();
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (QW) {
-      if (more) qstore((kt + 1) % ST);
-    }
   }
 
   // ---- epilogue: accumulators -> LDS (fp32, row-major) -> 8 columns per
@@ -446,6 +397,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   float* cs = reinterpret_cast<float*>(sm);
   constexpr int WROWS = BM / WAVES_M;
   constexpr int G8 = BN / 8;
+  // per-column weight scales of this lane's columns (4 float16 per (i, q)),
+  // loaded once per tile; columns past N take the last valid scale and are
+  // never stored
+  u32x2 scl[TN][4];
+  if (p.ws0 != nullptr) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = min(n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * g, p.N - 4);
+        const int seg = n / p.seg_cols;
+        scl[i][q] = *reinterpret_cast<const u32x2*>((seg == 0 ? p.ws0 : (seg == 1 ? p.ws1 : p.ws2)) +
+                                                    (n - seg * p.seg_cols));
+      }
+  }
 #pragma unroll
   for (int pass = 0; pass < BM / PR; ++pass) {
     __syncthreads();
@@ -459,13 +425,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
           for (int q = 0; q < 4; ++q) {
             const int col = wn * TN * 32 + i * 32 + 8 * q + 4 * g;
             f32x4 a4 = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            if constexpr (QW) {
-              // per-output-column scale of the int8 weight rows (columns
-              // past N read the last valid scale and are never stored)
-              const int n = min(n0 + col, p.N - 4);
-              const int seg = n / p.seg_cols;
-              const _Float16* sc = (seg == 0 ? p.ws0 : (seg == 1 ? p.ws1 : p.ws2)) + (n - seg * p.seg_cols);
-              const u32x2 h = *reinterpret_cast<const u32x2*>(sc);
+            if (p.ws0 != nullptr) {
+              const u32x2 h = scl[i][q];
               a4 *= f32x4{(float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] & 0xFFFF)),
                           (float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] >> 16)),
                           (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] & 0xFFFF)),
@@ -562,21 +523,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2>
-static hipError_t gemm32_go_q8(const GemmParams<bf16>& p, int epi, hipStream_t s, StageEvents ev) {
-  const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
-  switch (epi) {
-    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS, true>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_ROPE, true>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_ERF, true>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_TANH, true>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_BIAS_RES: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_RES, true>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2>
 static hipError_t gemm32_go(const GemmParams<bf16>& p, int epi, hipStream_t s, StageEvents ev) {
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
@@ -655,24 +601,6 @@ static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   const bool mfma32 = dt == DType::BF16 && a.K % 64 == 0 && a.lda % 8 == 0;
-  if (a.q8) {
-    // int8 weights: the MFMA kernel only, with the same tile choice as bf16
-    // weights (two LDS stages throughout)
-    if (!mfma32 || a.N % 8 || !a.wscale[0] || a.epi == EPI_BIAS_POS ||
-        (a.vt && (a.M % 8 || a.vt_tokens <= 0 || a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 ||
-                  (a.N - a.vt_col0) != a.vt_heads * a.vt_hd)))
-      return hipErrorInvalidValue;
-    const GemmParams<bf16> p = make_params<bf16>(a);
-    const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (t256 >= 224 && t256 <= 256) return gemm32_go_q8<256, 256, 2, 4>(p, a.epi, s, ev);
-    if (2.0 * a.M * a.N * a.K >= 2e10) {
-      if (a.N % 192 == 0) return gemm32_go_q8<128, 192, 2, 2>(p, a.epi, s, ev);
-      if (a.M % 192 == 0) return gemm32_go_q8<192, 128, 2, 2>(p, a.epi, s, ev);
-    }
-    const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (t128 < 192) return gemm32_go_q8<64, 64, 2, 2>(p, a.epi, s, ev);
-    return gemm32_go_q8<128, 128, 2, 2>(p, a.epi, s, ev);
-  }
   if (a.vt && (!mfma32 || (a.epi != EPI_BIAS && a.epi != EPI_BIAS_ROPE) || a.M % 8 || a.vt_tokens <= 0 ||
                a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 || (a.N - a.vt_col0) != a.vt_heads * a.vt_hd))
     return hipErrorInvalidValue;

@@ -64,10 +64,9 @@ struct GemmArgs {
   // on a grid grid_w wide
   const float* pos = nullptr;
   int pos_mode = POS_NONE, pos_side = 0;
-  // int8 weights (q8_row): W[s] are int8 [rows, K], wscale[s] float16 bits
-  // [rows], W[n, k] = int8 * scale[n]; bf16 activations with K % 64 == 0
-  // (the MFMA kernel), not with EPI_BIAS_POS
-  bool q8 = false;
+  // optional float16 scale per weight row (output column), segment-wise
+  // like W: acc[m, n] * wscale[n] before the bias (integer-valued W rows
+  // of q8_row weights)
   const void* wscale[3] = {nullptr, nullptr, nullptr};
 };
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
@@ -100,6 +99,17 @@ hipError_t launch_im2col(const float* pixels, bool nhwc, int batch, int C, int H
 // Copy rows of `cols` elements into rows of `ld` (>= cols, a multiple of the
 // 16-byte chunk), zero-filling the tail.
 hipError_t launch_pad_rows(const void* src, int64_t rows, int cols, void* dst, int ld, DType dt, hipStream_t st);
+
+// Exact conversion of int8 arrays to the activation type (q8_row payloads
+// before their GEMMs): up to 6 segments, each a multiple of 16 elements,
+// 16-byte aligned, in one launch.
+struct I8Segments {
+  const int8_t* src[6] = {};
+  void* dst[6] = {};
+  int64_t n[6] = {};
+  int count = 0;
+};
+hipError_t launch_i8_convert(const I8Segments& sg, DType dt, hipStream_t s, StageEvents ev = {});
 
 hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 

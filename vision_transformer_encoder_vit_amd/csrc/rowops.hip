@@ -272,4 +272,84 @@ hipError_t launch_v_transpose(const void* qkv, int64_t ld, int col0, void* vt, i
   return hipGetLastError();
 }
 
+
+// int8 -> activation type, exact (|q| <= 128 fits in bf16's 8 significant
+// bits). Work unit: the int8 values of one 16-byte output chunk (8 for bf16,
+// 4 for float), so that a wave's loads and stores are both contiguous; the
+// segments are laid end to end, and each thread takes I8U units spaced a
+// grid apart, all loads issued before the stores.
+constexpr int I8U = 4;
+
+struct I8Params {
+  const int8_t* src[6];
+  void* dst[6];
+  int64_t start[7];  // unit offsets of the segments
+  int count;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void i8_convert_kernel(I8Params q) {
+  constexpr int VN = Vec<T>::N;
+  const int64_t total = q.start[q.count], stride = (int64_t)gridDim.x * 256;
+  uint32_t raw[I8U][VN / 4];
+  T* out[I8U];
+#pragma unroll
+  for (int u = 0; u < I8U; ++u) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x + u * stride;
+    out[u] = nullptr;
+    if (c >= total) continue;
+    // segment of unit c (constant indices only: no indexed copy of the
+    // parameter arrays)
+    const int8_t* src = q.src[0];
+    void* dst = q.dst[0];
+    int64_t first = 0;
+#pragma unroll
+    for (int i = 1; i < 6; ++i)
+      if (i < q.count && c >= q.start[i]) {
+        src = q.src[i];
+        dst = q.dst[i];
+        first = q.start[i];
+      }
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + (c - first) * VN);
+    if constexpr (VN == 8) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
+      raw[u][0] = v[0];
+      raw[u][VN / 4 - 1] = v[1];
+    } else {
+      raw[u][0] = sp[0];
+    }
+    out[u] = static_cast<T*>(dst) + (c - first) * VN;
+  }
+#pragma unroll
+  for (int u = 0; u < I8U; ++u) {
+    if (out[u] == nullptr) continue;
+    float f[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) f[e] = (float)(int8_t)(raw[u][e / 4] >> (8 * (e % 4)));
+    st16(out[u], pack16<T>(f));
+  }
+}
+
+hipError_t launch_i8_convert(const I8Segments& sg, DType dt, hipStream_t s, StageEvents ev) {
+  I8Params q{};
+  q.count = sg.count;
+  q.start[0] = 0;
+  const int vn = dt == DType::BF16 ? 8 : 4;
+  for (int i = 0; i < sg.count; ++i) {
+    if (sg.n[i] % 16) return hipErrorInvalidValue;
+    q.src[i] = sg.src[i];
+    q.dst[i] = sg.dst[i];
+    q.start[i + 1] = q.start[i] + sg.n[i] / vn;
+  }
+  for (int i = sg.count; i < 6; ++i) q.start[i + 1] = q.start[sg.count];
+  const int64_t units = q.start[sg.count];
+  if (units == 0) return hipSuccess;
+  dim3 grid((unsigned)((units + 256 * I8U - 1) / (256 * I8U))), block(256);
+  if (dt == DType::BF16)
+    hipExtLaunchKernelGGL(i8_convert_kernel<bf16>, grid, block, 0, s, ev.start, ev.stop, 0, q);
+  else
+    hipExtLaunchKernelGGL(i8_convert_kernel<float>, grid, block, 0, s, ev.start, ev.stop, 0, q);
+  return hipGetLastError();
+}
+
 }  // namespace vit
