@@ -166,6 +166,36 @@ MUTATIONS += [
 ]
 
 
+from oracle import quant as oquant  # noqa: E402
+
+
+def _q8_unsigned(buf, rows, cols):
+    # payload read as unsigned bytes
+    q, sc = _orig_q8_from_bytes(buf, rows, cols)
+    return q.view(np.uint8).astype(np.int16), sc
+
+
+def _q8_scale_by_column(q, scale):
+    q = np.asarray(q, dtype=np.float64)
+    s = np.resize(np.asarray(scale, dtype=np.float64), q.shape[1])
+    return q * s[None, :]
+
+
+def _q8_scales_big_endian(buf, rows, cols):
+    b = np.frombuffer(bytes(buf), dtype=np.uint8)
+    q = b[:rows * cols].view(np.int8).reshape(rows, cols)
+    return q.copy(), b[rows * cols:rows * cols + 2 * rows].view(">f2").copy()
+
+
+_orig_q8_from_bytes = oquant.q8_row_from_bytes
+
+MUTATIONS += [
+    ("q8 payload unsigned", oquant, "q8_row_from_bytes", _q8_unsigned, pins.test_q8_row_bytes_layout_by_hand),
+    ("q8 scale per column", oquant, "dequant_q8_row", _q8_scale_by_column, pins.test_q8_row_bytes_layout_by_hand),
+    ("q8 scales big-endian", oquant, "q8_row_from_bytes", _q8_scales_big_endian, pins.test_q8_row_bytes_layout_by_hand),
+]
+
+
 @pytest.mark.parametrize("label,mod,attr,bad,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(monkeypatch, label, mod, attr, bad, pin):
     monkeypatch.setattr(mod, attr, bad)
