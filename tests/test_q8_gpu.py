@@ -91,3 +91,30 @@ def test_q8_siglip_tower_full_frame():
     nrel = float(np.linalg.norm(a - r) / np.linalg.norm(r))
     print("q8 siglip tower: cos %.7f norm-rel %.2e" % (cos, nrel))
     assert cos >= 0.9999 and nrel <= 2e-2
+
+
+def test_q8_hiera_stack_32x32():
+    # eight Hiera blocks over a 32x32 grid (mask units, transitions with the
+    # residual projection, global stages), every block with int8 weights
+    import torch
+    from vision_transformer_encoder_vit_amd import binding as vb
+    specs, levels, taps = synth.hiera_stack(side=32, stage_blocks=(2, 2, 2, 2))
+    specs = [dict(s, weights="q8_row") for s in specs]
+    x, _ = synth.make_stack_inputs(specs, seed=6)
+    blocks = [synth.make_q8_inputs(s, seed=6 * 1000 + i) for i, s in enumerate(specs)]
+    dev_w = [gu.to_device(w, sp) for w, sp in zip(blocks, specs)]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    st = vb.Stack([vb.desc_from_spec(s) for s in specs], levels, taps)
+    feats = [torch.empty((1, synth.out_tokens(specs[t]), specs[t]["dim_out"]), dtype=torch.bfloat16, device="cuda")
+             for t in taps]
+    ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+    st.forward([vb.weights_struct(w) for w in dev_w], xd, feats, ws)
+    torch.cuda.synchronize()
+    st.close()
+    ref = ost.stack_forward(x, [quant.dequant_block(w) for w in blocks], specs, levels, taps)
+    for k, (f, r) in enumerate(zip(feats, ref)):
+        a, b = gu.to64(f).ravel(), r.ravel()
+        cos = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+        nrel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        print("q8 hiera feature %d: cos %.7f norm-rel %.2e" % (k, cos, nrel))
+        assert cos >= 0.9999 and nrel <= 2e-2
