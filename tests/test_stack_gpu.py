@@ -187,3 +187,48 @@ def test_tower_from_pixels(kind):
     else:
         got = _tower_gpu(specs, gu.to64(tok), blocks, pre_ln=pre, post_ln=post)
         _tower_gate("%s from pixels" % kind, got, ost.tower_forward(x_ref, blocks, specs, pre_ln=pre, post_ln=post))
+
+
+def test_stack_batch_of_two_frames():
+    # two frames through an 8-block Hiera stack: each frame's features equal
+    # the oracle's, and frame 1 equals a one-frame run of its own input
+    specs, levels, taps = synth.hiera_stack(side=32, batch=2, stage_blocks=(2, 2, 2, 2))
+    print("case stack batch 2", flush=True)
+    x, blocks = synth.make_stack_inputs(specs, seed=7)
+    feats, _, _ = _run_stack(specs, levels, taps, x, blocks)
+    ref = ost.stack_forward(x, blocks, specs, levels, taps)
+    for k, (f, r) in enumerate(zip(feats, ref)):
+        _tower_gate("batch-2 stack feature %d" % k, gu.to64(f), r)
+    one = [synth.derive(s, batch=1) for s in specs]
+    feats1, _, _ = _run_stack(one, levels, taps, x[1:], blocks)
+    for f2, f1 in zip(feats, feats1):
+        assert torch.equal(f2[1:].view(torch.int16), f1.view(torch.int16))
+
+
+def test_stack_forward_is_graph_capturable():
+    # the stack forward allocates nothing and never synchronises: captured
+    # into a HIP graph, every replay equals the eager features bit for bit
+    specs, levels, taps = synth.hiera_stack(side=32, stage_blocks=(2, 2, 2, 2))
+    x, blocks = synth.make_stack_inputs(specs, seed=8)
+    eager, dev_w, xd = _run_stack(specs, levels, taps, x, blocks)
+    weights = [vb.weights_struct(w) for w in dev_w]
+    st = vb.Stack([vb.desc_from_spec(s) for s in specs], levels, taps)
+    feats = [torch.empty_like(f) for f in eager]
+    ws = torch.empty(st.workspace_bytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        st.forward(weights, xd, feats, ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st.forward(weights, xd, feats, ws, stream=s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for f in feats:
+            f.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for f, e in zip(feats, eager):
+            assert torch.equal(f.view(torch.int16), e.view(torch.int16)), i
+    st.close()
