@@ -30,7 +30,11 @@ struct Im2colParams {
 
 // One thread per 16-byte chunk of an A row (8 bf16 or 4 float entries):
 // consecutive threads write consecutive chunks of a row. Entries outside
-// the image (the zero padding) and past K are zero.
+// the image (the zero padding) and past K are zero. The chunk's first entry
+// is located with two divisions, the rest by stepping the (c, ky, kx) or
+// (ky, kx, c) indices; runs of 4 pixels that are contiguous in memory and
+// 16-byte aligned (4 pixels of an NCHW kernel row, or the 4 channels of one
+// NHWC pixel) are read with one 16-byte load.
 template <typename T>
 __global__ __launch_bounds__(256) void im2col_kernel(const float* __restrict__ px, T* __restrict__ A,
                                                      Im2colParams q) {
@@ -44,33 +48,63 @@ __global__ __launch_bounds__(256) void im2col_kernel(const float* __restrict__ p
   const int b = (int)(m / T_), t = (int)(m - (int64_t)b * T_);
   const int y = t / q.out_w, x = t - y * q.out_w;
   const int y0 = y * q.s - q.p, x0 = x * q.s - q.p;
-  const int kk2 = q.k * q.k, kc = q.k * q.C;
+  const int kk0 = chunk * VN;
   float v[VN];
-#pragma unroll
-  for (int e = 0; e < VN; ++e) {
-    const int kk = chunk * VN + e;
-    float val = 0.f;
-    if (kk < q.K) {
-      int c, ky, kx;
-      if (q.ohwi) {
-        ky = kk / kc;
-        const int r = kk - ky * kc;
-        kx = r / q.C;
-        c = r - kx * q.C;
-      } else {
-        c = kk / kk2;
-        const int r = kk - c * kk2;
-        ky = r / q.k;
-        kx = r - ky * q.k;
-      }
-      const int py = y0 + ky, pxx = x0 + kx;
-      if (py >= 0 && py < q.H && pxx >= 0 && pxx < q.W)
-        val = q.nhwc ? px[(((int64_t)b * q.H + py) * q.W + pxx) * q.C + c]
-                     : px[(((int64_t)b * q.C + c) * q.H + py) * q.W + pxx];
-    }
-    v[e] = val;
+  int c, ky, kx;
+  if (q.ohwi) {
+    const int kc = q.k * q.C;
+    ky = kk0 / kc;
+    const int r = kk0 - ky * kc;
+    kx = r / q.C;
+    c = r - kx * q.C;
+  } else {
+    const int kk2 = q.k * q.k;
+    c = kk0 / kk2;
+    const int r = kk0 - c * kk2;
+    ky = r / q.k;
+    kx = r - ky * q.k;
   }
-  st16(A + m * q.Kp + chunk * VN, pack16<T>(v));
+  // groups of 4 entries: one 16-byte load where the run allows it, else
+  // four single loads, stepping the indices either way
+#pragma unroll
+  for (int g = 0; g < VN / 4; ++g) {
+    const int kk = kk0 + 4 * g;
+    int py = y0 + ky, pxx = x0 + kx;
+    if (q.ohwi && q.C == 4 && c == 0) {
+      // the 4 channels of one NHWC pixel
+      f32x4 pv = {0.f, 0.f, 0.f, 0.f};
+      if (kk < q.K && py >= 0 && py < q.H && pxx >= 0 && pxx < q.W)
+        pv = *reinterpret_cast<const f32x4*>(px + (((int64_t)b * q.H + py) * q.W + pxx) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * g + j] = pv[j];
+      if (++kx == q.k) { kx = 0; ++ky; }
+      continue;
+    }
+    if (!q.ohwi && (kx & 3) == 0 && kx + 4 <= q.k && kk + 4 <= q.K && ((x0 + kx) & 3) == 0 && (q.W & 3) == 0 &&
+        py >= 0 && py < q.H && pxx >= 0 && pxx + 4 <= q.W) {
+      // four pixels of one NCHW kernel row, contiguous and aligned
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(px + (((int64_t)b * q.C + c) * q.H + py) * q.W + pxx);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * g + j] = pv[j];
+      kx += 4;
+      if (kx == q.k) { kx = 0; if (++ky == q.k) { ky = 0; ++c; } }
+      continue;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      py = y0 + ky;
+      pxx = x0 + kx;
+      const bool inside = kk + j < q.K && py >= 0 && py < q.H && pxx >= 0 && pxx < q.W;
+      if (q.ohwi) {
+        v[4 * g + j] = inside ? px[(((int64_t)b * q.H + py) * q.W + pxx) * q.C + c] : 0.f;
+        if (++c == q.C) { c = 0; if (++kx == q.k) { kx = 0; ++ky; } }
+      } else {
+        v[4 * g + j] = inside ? px[(((int64_t)b * q.C + c) * q.H + py) * q.W + pxx] : 0.f;
+        if (++kx == q.k) { kx = 0; if (++ky == q.k) { ky = 0; ++c; } }
+      }
+    }
+  }
+  st16(A + m * q.Kp + kk0, pack16<T>(v));
 }
 
 // dst[r, 0:cols] = src[r, 0:cols], dst[r, cols:ld] = 0: one 16-byte chunk of
