@@ -924,16 +924,13 @@ VIT_API vit_status vit_patch_embed(const vit_patch_embed_desc* desc, const float
   char* base = static_cast<char*>(workspace);
   void* A = base;
   const void* W = weight;
+  void* Wp = g.pad_weight ? base + g.a_bytes : nullptr;
   st = device_status(vit::launch_im2col(pixels, d.pixel_layout == VIT_PIXELS_NHWC, d.batch, d.in_ch, d.in_h, d.in_w,
-                                        d.kernel, d.stride, d.pad, d.weight_layout == VIT_CONV_OHWI, A, g.Kp, dt, s),
+                                        d.kernel, d.stride, d.pad, d.weight_layout == VIT_CONV_OHWI, A, g.Kp, dt, s,
+                                        g.pad_weight ? weight : nullptr, Wp, d.dim),
                      "im2col");
   if (st != VIT_OK) return st;
-  if (g.pad_weight) {
-    void* Wp = base + g.a_bytes;
-    st = device_status(vit::launch_pad_rows(weight, d.dim, g.K, Wp, g.Kp, dt, s), "weight pad");
-    if (st != VIT_OK) return st;
-    W = Wp;
-  }
+  if (g.pad_weight) W = Wp;
   vit::GemmArgs a;
   a.A = A;
   a.lda = g.Kp;

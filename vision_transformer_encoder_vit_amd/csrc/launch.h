@@ -94,11 +94,11 @@ struct AttnArgs {
 // kk < C*k*k in the weight's flattening order, (c, ky, kx) for OIHW or
 // (ky, kx, c) for OHWI; zero outside the image and for kk >= C*k*k) for
 // float32 pixels [B, C, H, W] (nhwc false) or [B, H, W, C]; A is [M, Kp].
+// With wsrc, the same launch also copies the weight rows wsrc [wrows, C*k*k]
+// into wdst [wrows, Kp], zero-filling the tail.
 hipError_t launch_im2col(const float* pixels, bool nhwc, int batch, int C, int H, int W, int k, int s, int p,
-                         bool ohwi, void* A, int Kp, DType dt, hipStream_t st, StageEvents ev = {});
-// Copy rows of `cols` elements into rows of `ld` (>= cols, a multiple of the
-// 16-byte chunk), zero-filling the tail.
-hipError_t launch_pad_rows(const void* src, int64_t rows, int cols, void* dst, int ld, DType dt, hipStream_t st);
+                         bool ohwi, void* A, int Kp, DType dt, hipStream_t st, const void* wsrc = nullptr,
+                         void* wdst = nullptr, int wrows = 0, StageEvents ev = {});
 
 // Exact conversion of int8 arrays to the activation type (q8_row payloads
 // before their GEMMs): up to 6 segments, each a multiple of 16 elements,

@@ -12,8 +12,8 @@
 // the weight's own flattening order -- (c, ky, kx) for OIHW weights,
 // (ky, kx, c) for OHWI -- so the weight is used as the GEMM's [N, K] operand
 // without any transpose; K is padded with zeros to a multiple of 64 (the
-// MFMA GEMM's K tile), and the weight rows are padded to match when K is not
-// already a multiple of 64.
+// MFMA GEMM's K tile), and the weight rows are padded to match, in the same
+// launch, when K is not already a multiple of 64.
 #include "common.h"
 #include "launch.h"
 
@@ -26,6 +26,12 @@ struct Im2colParams {
   int C, H, W, k, s, p, out_h, out_w;
   int K, Kp;  // C*k*k and its padded width
   int nhwc, ohwi;
+  // optional weight rows padded from K to Kp by the same launch (workgroups
+  // past the gather's): wsrc [wrows, K] -> wdst [wrows, Kp]
+  const void* wsrc;
+  void* wdst;
+  int wrows;
+  unsigned gather_blocks;
 };
 
 // One thread per 16-byte chunk of an A row (8 bf16 or 4 float entries):
@@ -40,6 +46,18 @@ __global__ __launch_bounds__(256) void im2col_kernel(const float* __restrict__ p
                                                      Im2colParams q) {
   constexpr int VN = Vec<T>::N;
   const int cpr = q.Kp / VN;
+  if (blockIdx.x >= q.gather_blocks) {  // weight padding, one chunk per thread
+    const int64_t wid = (int64_t)(blockIdx.x - q.gather_blocks) * 256 + threadIdx.x;
+    const int64_t r = wid / cpr;
+    if (r >= q.wrows) return;
+    const int c0 = (int)(wid - r * cpr) * VN;
+    const T* ws = static_cast<const T*>(q.wsrc);
+    float f[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) f[e] = c0 + e < q.K ? to_f32(ws[r * q.K + c0 + e]) : 0.f;
+    st16(static_cast<T*>(q.wdst) + r * q.Kp + c0, pack16<T>(f));
+    return;
+  }
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t m = id / cpr;
   if (m >= q.M) return;
@@ -107,26 +125,9 @@ __global__ __launch_bounds__(256) void im2col_kernel(const float* __restrict__ p
   st16(A + m * q.Kp + kk0, pack16<T>(v));
 }
 
-// dst[r, 0:cols] = src[r, 0:cols], dst[r, cols:ld] = 0: one 16-byte chunk of
-// dst per thread (ld a multiple of the chunk; cols <= ld need not be, the
-// source is read element by element).
-template <typename T>
-__global__ __launch_bounds__(256) void pad_rows_kernel(const T* __restrict__ src, T* __restrict__ dst,
-                                                       int64_t rows, int cols, int ld) {
-  constexpr int VN = Vec<T>::N;
-  const int cpr = ld / VN;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t r = id / cpr;
-  if (r >= rows) return;
-  const int c0 = (int)(id - r * cpr) * VN;
-  float v[VN];
-#pragma unroll
-  for (int e = 0; e < VN; ++e) v[e] = c0 + e < cols ? to_f32(src[r * cols + c0 + e]) : 0.f;
-  st16(dst + r * ld + c0, pack16<T>(v));
-}
-
 hipError_t launch_im2col(const float* pixels, bool nhwc, int batch, int C, int H, int W, int k, int s, int p,
-                         bool ohwi, void* A, int Kp, DType dt, hipStream_t st, StageEvents ev) {
+                         bool ohwi, void* A, int Kp, DType dt, hipStream_t st, const void* wsrc, void* wdst,
+                         int wrows, StageEvents ev) {
   Im2colParams q;
   q.C = C;
   q.H = H;
@@ -143,22 +144,16 @@ hipError_t launch_im2col(const float* pixels, bool nhwc, int batch, int C, int H
   q.ohwi = ohwi;
   const int vn = dt == DType::BF16 ? 8 : 4;
   const int64_t threads = q.M * (Kp / vn);
-  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  q.gather_blocks = (unsigned)((threads + 255) / 256);
+  q.wsrc = wsrc;
+  q.wdst = wdst;
+  q.wrows = wsrc ? wrows : 0;
+  const int64_t wthreads = (int64_t)q.wrows * (Kp / vn);
+  dim3 grid(q.gather_blocks + (unsigned)((wthreads + 255) / 256)), block(256);
   if (dt == DType::BF16)
     hipExtLaunchKernelGGL(im2col_kernel<bf16>, grid, block, 0, st, ev.start, ev.stop, 0, pixels, (bf16*)A, q);
   else
     hipExtLaunchKernelGGL(im2col_kernel<float>, grid, block, 0, st, ev.start, ev.stop, 0, pixels, (float*)A, q);
-  return hipGetLastError();
-}
-
-hipError_t launch_pad_rows(const void* src, int64_t rows, int cols, void* dst, int ld, DType dt, hipStream_t st) {
-  const int vn = dt == DType::BF16 ? 8 : 4;
-  const int64_t threads = rows * (ld / vn);
-  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-  if (dt == DType::BF16)
-    hipLaunchKernelGGL(pad_rows_kernel<bf16>, grid, block, 0, st, (const bf16*)src, (bf16*)dst, rows, cols, ld);
-  else
-    hipLaunchKernelGGL(pad_rows_kernel<float>, grid, block, 0, st, (const float*)src, (float*)dst, rows, cols, ld);
   return hipGetLastError();
 }
 
