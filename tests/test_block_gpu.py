@@ -28,11 +28,20 @@ SMALL = {
                     heads=3, mlp=768),
     "c5w_48x48": d(C["c5w_sam3_win"], grid_h=48, grid_w=48, dim_in=256, dim_out=256, heads=4, mlp=1184),
     "c5g_18x22": d(C["c5g_sam3_global"], grid_h=18, grid_w=22, dim_in=256, dim_out=256, heads=4, mlp=1184),
-    # global attention on V^T from the transpose kernel (qkv projection off
-    # the MFMA path, K = 224): with and without the 2x2 query pool
+    # K = 224 (three full K tiles and one of 32 columns) with V^T written by
+    # the qkv GEMM: with and without the 2x2 query pool
     "c3b_pool_global_32": d(C["c3b_hiera_s2"], grid_h=32, grid_w=32, dim_in=224, dim_out=448, q_stride=4),
     "c4_d224_16x16": d(C["c4_siglip_b8"], batch=2, grid_h=16, grid_w=16, dim_in=224, dim_out=224, heads=4,
                        mlp=448),
+    # K = 48 (below one K tile: the VALU GEMM) and fc2's K = 176 (two full K
+    # tiles and 48 columns); K = 80 and fc2's K = 208 (16-column tails)
+    "c4_d48_b2_9x13": d(C["c4_siglip_b8"], batch=2, grid_h=9, grid_w=13, dim_in=48, dim_out=48, heads=1,
+                        mlp=176),
+    "c3b_d80_12x12": d(C["c3b_hiera_s2"], grid_h=12, grid_w=12, dim_in=80, dim_out=80, heads=2, mlp=208),
+    # K = 200 (not a multiple of 16): the qkv projection on the VALU GEMM and
+    # V^T from the transpose kernel
+    "c4_d200_16x16": d(C["c4_siglip_b8"], batch=2, grid_h=16, grid_w=16, dim_in=200, dim_out=200, heads=5,
+                       mlp=400),
     # 200 keys: V^T path, keys split over two workgroups, ragged last tile
     "c5g_10x20_split": d(C["c5g_sam3_global"], grid_h=10, grid_w=20, dim_in=256, dim_out=256, heads=4, mlp=1024),
     "c5w_f32": d(C["c5w_sam3_win"], grid_h=24, grid_w=48, dim_in=128, dim_out=128, heads=2, mlp=256,
@@ -62,11 +71,14 @@ def _sample_rows(n, count, seed):
 
 
 # Large shapes beside the benchmark's: ragged token counts through the
-# 128x192 / 192x128 GEMM tiles (8000 rows; a 4712-wide MLP), the V^T attention
-# path with a ragged last key tile (1000 keys), and K % 64 != 0 at full size.
+# 128x192 / 192x128 GEMM tiles (8000 rows; a 4712-wide MLP, whose fc2 has
+# K % 16 != 0 and runs on the VALU GEMM), the V^T attention path with a
+# ragged last key tile (1000 keys), and a 3088-wide MLP whose fc2 (K = 3088)
+# ends in a 16-column K tile after 48 full ones.
 LARGE = {
     "c4_b8_25x40": d(C["c4_siglip_b8"], grid_h=25, grid_w=40),
     "c5w_mlp4712": d(C["c5w_sam3_win"], mlp=4712),
+    "c4_mlp3088": d(C["c4_siglip_b8"], mlp=3088),
 }
 
 

@@ -155,7 +155,9 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   p->attn_vt = vit::attention_takes_vt(d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32,
                                        d.attn_mode, n_q, p->head_dim, d.win_w, p->n_in,
                                        p->m_in * 3LL * d.dim_out);
-  p->vt_in_gemm = p->attn_vt && d.dim_in % 64 == 0;  // the qkv projection's MFMA path writes V^T
+  // the qkv projection's MFMA path writes V^T
+  p->vt_in_gemm = p->attn_vt && vit::gemm_uses_mfma(d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32,
+                                                    d.dim_in, d.dim_in);
   p->off_vt = p->attn_vt ? take(p->m_in, d.dim_out) : 0;
   p->attn_splits = 1;
   if (p->attn_vt) {

@@ -209,10 +209,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path for K % 64 == 0: 32x32x16 MFMA, operands staged global -> LDS
+// bf16 path for K % 16 == 0, K >= 64: 32x32x16 MFMA, operands staged global -> LDS
 // directly (global_load_lds, 16 bytes per lane, no register round trip) in a
-// two-stage ring, and an epilogue that goes through LDS so that every global
-// store is a full 16-byte vector of one output row.
+// ring of 2-4 stages of 64 K columns, and an epilogue that goes through LDS
+// so that every global store is a full 16-byte vector of one output row.
+// When K % 64 != 0 (K >= 64) the last K tile is loaded as the last 64
+// columns of the rows, overlapping the tile before it, and only its MFMA K
+// steps past that overlap run.
 //
 // LDS layout of a stage: [BM token rows | BN weight rows] x 64 bf16 (128 B
 // per row = 8 chunks of 16 B). One load instruction of a wave fills 8 rows
@@ -257,7 +260,7 @@ struct Interleave {
   }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI, bool KT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(GemmParams<bf16> p) {
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   constexpr int BK = 64;
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   // consumed only by a store that never happens (M >= 1 always).
   uint32_t touch = 0;
   {
-    const int lines_per_row = p.K / 64;
+    const int lines_per_row = KT ? (p.K + 63) / 64 : p.K / 64;  // kl * 64 < K since K % 16 == 0
     const int64_t lines = (int64_t)p.N * lines_per_row;
     for (int64_t g = (int64_t)blockIdx.x * NT + tid; g < lines; g += (int64_t)gridDim.x * NT) {
       const int n = (int)(g / lines_per_row), kl = (int)(g - (int64_t)n * lines_per_row);
@@ -311,10 +314,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       src[j] = base + (int64_t)(n - seg * p.seg_cols) * p.K + chunk * 8;
     }
   }
+  // KT (K % 64 != 0, K >= 64): the partial last tile is read as the last
+  // 64 columns, K-64 .. K-1; its new columns are its last kst K steps
+  const int nk = KT ? (p.K + BK - 1) / BK : p.K / BK;  // K tiles
+  const int nkf = KT ? p.K / BK : nk;  // full K tiles; tile nkf (if any) is partial
+  const int kst = (p.K - nkf * BK) / 16;
+  const int klast = p.K - BK;
   // load j of tile kt (LPW per wave per tile)
   auto load = [&](int j, int kt) {
-    __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_ptr)(sm + (kt % ST) * STAGE + (wave * LPW + j) * 512),
-                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(src[j] + (KT ? min(kt * BK, klast) : kt * BK)),
+                                     (lds_ptr)(sm + (kt % ST) * STAGE + (wave * LPW + j) * 512), 16, 0, 0);
   };
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int fr = lane & 31, g = lane >> 5;
@@ -340,14 +349,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     }
   };
 
-  const int nk = p.K / BK;
   constexpr int KS = BK / 16;              // MFMA K steps per tile
   constexpr int LPK = (LPW + 1) / 2;       // tile kt+ST-1's loads per K step, over the first two steps
   // tiles 0 .. ST-2 in flight before the loop
   for (int t = 0; t < ST - 1 && t < nk; ++t)
 #pragma unroll
     for (int j = 0; j < LPW; ++j) load(j, t);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nkf; ++kt) {
     // this wave's loads of tile kt have landed (the later tiles' loads, issued
     // after them, may still be in flight); after the barrier every wave's
     // have, and every wave is done reading the stage refilled next
@@ -383,6 +391,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       else
         Interleave<0, TN * TM, LPK, 0>::go();
       __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (KT && kst > 0) {
+    // the partial tile: its loads were the last issued; K steps KS-kst .. KS-1
+    // hold columns nkf*64 .. K-1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int stage = nkf % ST, ks0 = KS - kst;
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      if (ks >= ks0) {
+        if (ks == ks0) frags(ks & 1, stage, ks);
+        if (ks + 1 < KS) frags((ks + 1) & 1, stage, ks + 1);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ks & 1][i]),
+                                                               __builtin_bit_cast(bf16x8, bfr[ks & 1][j]), acc[i][j], 0, 0, 0);
+      }
     }
   }
 
@@ -522,17 +552,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   if (p.M <= 0 && touch == 0x5EEDu) p.C[0] = bf16(0.f);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2, bool KT = false>
 static hipError_t gemm32_go(const GemmParams<bf16>& p, int epi, hipStream_t s, StageEvents ev) {
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
   switch (epi) {
-    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_ROPE>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_ERF>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_TANH>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_BIAS_POS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_POS>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_RES>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_ROPE, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_ERF, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_TANH, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_POS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_POS, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_RES, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
   }
   return hipGetLastError();
 }
@@ -600,7 +630,7 @@ static hipError_t gemm_go(const GemmArgs& a, hipStream_t s, StageEvents ev) {
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  const bool mfma32 = dt == DType::BF16 && a.K % 64 == 0 && a.lda % 8 == 0;
+  const bool mfma32 = gemm_uses_mfma(dt, a.K, a.lda);
   if (a.vt && (!mfma32 || (a.epi != EPI_BIAS && a.epi != EPI_BIAS_ROPE) || a.M % 8 || a.vt_tokens <= 0 ||
                a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 || (a.N - a.vt_col0) != a.vt_heads * a.vt_hd))
     return hipErrorInvalidValue;
@@ -612,6 +642,15 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
     // tiles with no ragged edge; 3-8 % faster on the SigLIP and SAM3 MLP and
     // qkv shapes, slower on the small projections)
     const GemmParams<bf16> p = make_params<bf16>(a);
+    const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+    if (a.K % 64 != 0) {
+      // a partial last K tile (the Hiera widths 112 and 224): only 2-4 K
+      // tiles, so per-tile prologue and epilogue dominate and 64x64 tiles
+      // (more of them in flight) beat 128x128 (c3a qkv 16384x672x112:
+      // 7.7 us against 10.2); four stages where the grid is small
+      if (t128 < 192) return gemm32_go<64, 64, 2, 2, 4, true>(p, a.epi, s, ev);
+      return gemm32_go<64, 64, 2, 2, 2, true>(p, a.epi, s, ev);
+    }
     const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (t256 >= 224 && t256 <= 256) return gemm32_go<256, 256, 2, 4>(p, a.epi, s, ev);
     if (2.0 * a.M * a.N * a.K >= 2e10) {
@@ -633,7 +672,6 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
     // leave most CUs idle, so 64x64 tiles (one 32x32 block per wave) with
     // four LDS stages: a lone workgroup per CU has nothing else to hide its
     // load latency behind
-    const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
     if (t128 < 192) return gemm32_go<64, 64, 2, 2, 4>(p, a.epi, s, ev);
     return gemm32_go<128, 128, 2, 2>(p, a.epi, s, ev);
   }

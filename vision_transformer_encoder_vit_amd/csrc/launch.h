@@ -56,7 +56,7 @@ struct GemmArgs {
   // EPI_BIAS / EPI_BIAS_ROPE: columns >= vt_col0 (V, bias only) are also
   // written transposed to vt [M / vt_tokens, vt_heads, vt_hd, vt_tokens];
   // with vt_only they are not written to C. Needs the bf16 MFMA path
-  // (K % 64 == 0), M and vt_tokens multiples of 8, vt_col0 a multiple of 8.
+  // (gemm_uses_mfma), M and vt_tokens multiples of 8, vt_col0 a multiple of 8.
   void* vt = nullptr;
   int vt_col0 = 0, vt_tokens = 0, vt_heads = 0, vt_hd = 0;
   bool vt_only = false;
@@ -70,6 +70,12 @@ struct GemmArgs {
   const void* wscale[3] = {nullptr, nullptr, nullptr};
 };
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
+// The bf16 MFMA path takes K >= 64 with K % 16 == 0 (a last K tile of 16,
+// 32 or 48 columns runs that many MFMA K steps) and 16-byte aligned A rows;
+// other shapes and fp32 run the VALU kernel. The V^T output needs this path.
+inline bool gemm_uses_mfma(DType dt, int K, int64_t lda) {
+  return dt == DType::BF16 && K >= 64 && K % 16 == 0 && lda % 8 == 0;
+}
 
 enum AttnMode { ATTN_GLOBAL = 0, ATTN_MASK_UNIT = 1, ATTN_SPATIAL = 2 };
 
