@@ -260,16 +260,42 @@ struct Interleave {
   }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI, bool KT>
+// Wait until at most `ahead` tiles' loads (LPW per wave each) are still in
+// flight: s_waitcnt takes an immediate, so one branch per possible count.
+template <int A, int LPW>
+struct WaitAhead {
+  __device__ __forceinline__ static void go(int ahead) {
+    if constexpr (A == 0) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+      if (ahead >= A)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(A * LPW));
+      else
+        WaitAhead<A - 1, LPW>::go(ahead);
+    }
+  }
+};
+
+// KW: the waves split K instead of the tile. Each of the four waves owns
+// one of a K tile's four MFMA K steps for the whole BM x BN tile, and the
+// four partial tiles are summed in LDS before the epilogue. For grids of
+// about one workgroup per CU, where one wave per SIMD with one MFMA per K
+// step spends most of each step waiting on its LDS fragment reads.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI, bool KT, bool KW>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(GemmParams<bf16> p) {
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   constexpr int BK = 64;
-  static_assert(ST >= 2 && ST <= 4, "2 to 4 LDS stages");
-  constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;  // 32x32 tiles per wave
+  static_assert(ST >= 2, "at least two LDS stages");
+  static_assert(!KW || NW == BK / 16, "KW: one wave per MFMA K step");
+  constexpr int TM = KW ? BM / 32 : BM / WAVES_M / 32, TN = KW ? BN / 32 : BN / WAVES_N / 32;  // 32x32 tiles per wave
   constexpr int STAGE = (BM + BN) * BK;                          // bf16 elements
   constexpr int LPW = (BM + BN) / (8 * NW);                      // load instructions per wave per stage
   static_assert((BM + BN) % (8 * NW) == 0, "rows must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) bf16 sm[ST * STAGE];
+  static_assert((ST - 2) * LPW <= 63, "vmcnt counts at most 63 loads");
+  constexpr int CROW = BN + 4;  // fp32 row pitch of the epilogue staging tile
+  // KW stages NW partial tiles (fp32) in the epilogue
+  constexpr int SM = KW && NW * BM * CROW * 2 > ST * STAGE ? NW * BM * CROW * 2 : ST * STAGE;
+  __shared__ __attribute__((aligned(1024))) bf16 sm[SM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
@@ -325,7 +351,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     __builtin_amdgcn_global_load_lds((const void*)(src[j] + (KT ? min(kt * BK, klast) : kt * BK)),
                                      (lds_ptr)(sm + (kt % ST) * STAGE + (wave * LPW + j) * 512), 16, 0, 0);
   };
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wm = KW ? 0 : wave / WAVES_N, wn = KW ? 0 : wave % WAVES_N;
   const int fr = lane & 31, g = lane >> 5;
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -359,18 +385,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     // this wave's loads of tile kt have landed (the later tiles' loads, issued
     // after them, may still be in flight); after the barrier every wave's
     // have, and every wave is done reading the stage refilled next
-    const int ahead = min(ST - 2, nk - 1 - kt);
-    if (ST >= 4 && ahead >= 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
-    else if (ST >= 3 && ahead >= 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    WaitAhead<ST - 2, LPW>::go(min(ST - 2, nk - 1 - kt));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const bool more = kt + ST - 1 < nk;
     const int stage = kt % ST;
+    if constexpr (KW) {
+      frags(0, stage, wave);
+      if (more) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) load(j, kt + ST - 1);
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[0][i]),
+                                                             __builtin_bit_cast(bf16x8, bfr[0][j]), acc[i][j], 0, 0, 0);
+      continue;
+    }
     frags(0, stage, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -401,8 +435,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int stage = nkf % ST, ks0 = KS - kst;
+    if (KW && wave >= ks0) {
+      frags(0, stage, wave);
 #pragma unroll
-    for (int ks = 1; ks < KS; ++ks) {
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[0][i]),
+                                                             __builtin_bit_cast(bf16x8, bfr[0][j]), acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 1; ks < (KW ? 1 : KS); ++ks) {
       if (ks >= ks0) {
         if (ks == ks0) frags(ks & 1, stage, ks);
         if (ks + 1 < KS) frags((ks + 1) & 1, stage, ks + 1);
@@ -420,11 +463,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   // thread with bias / RoPE / GELU / residual -> one 16-byte store per row
   // chunk. Lane (fr, g) of 32x32 tile (i, j) holds row j*32+fr, columns
   // i*32 + 8q + 4g + e in register 4q + e.
-  constexpr int CROW = BN + 4;
   constexpr int PR0 = (ST * STAGE * 2) / (CROW * 4);
-  constexpr int PR = PR0 >= BM ? BM : (PR0 >= BM / 2 ? BM / 2 : BM / 4);
+  constexpr int PR = KW || PR0 >= BM ? BM : (PR0 >= BM / 2 ? BM / 2 : BM / 4);
   static_assert(PR >= BM / 4 && PR % 32 == 0, "LDS too small for the epilogue");
   float* cs = reinterpret_cast<float*>(sm);
+  float* cw = cs + (KW ? wave * BM * CROW : 0);  // this wave's staging tile
   constexpr int WROWS = BM / WAVES_M;
   constexpr int G8 = BN / 8;
   // per-column weight scales of this lane's columns (4 float16 per (i, q)),
@@ -462,11 +505,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
                           (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] & 0xFFFF)),
                           (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] >> 16))};
             }
-            *reinterpret_cast<f32x4*>(cs + (row - pass * PR) * CROW + col) = a4;
+            *reinterpret_cast<f32x4*>(cw + (row - pass * PR) * CROW + col) = a4;
           }
       }
     }
     __syncthreads();
+    if constexpr (KW) {
+      // sum the NW partial tiles into the first
+      for (int e = tid; e < BM * (BN / 4); e += NT) {
+        const int r = e / (BN / 4), c4 = (e - r * (BN / 4)) * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(cs + r * CROW + c4);
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const f32x4*>(cs + w * BM * CROW + r * CROW + c4);
+        *reinterpret_cast<f32x4*>(cs + r * CROW + c4) = v;
+      }
+      __syncthreads();
+    }
     if ((EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) && p.vt != nullptr && n0 + BN > p.vt_col0) {
       // transposed copy of the V columns: one column x 8 consecutive token
       // rows per thread (a 16-byte run of one V^T row); rows are within one
@@ -552,17 +606,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   if (p.M <= 0 && touch == 0x5EEDu) p.C[0] = bf16(0.f);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2, bool KT = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int ST = 2, bool KT = false, bool KW = false>
 static hipError_t gemm32_go(const GemmParams<bf16>& p, int epi, hipStream_t s, StageEvents ev) {
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
   switch (epi) {
-    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_ROPE, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_ERF, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_TANH, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    case EPI_BIAS_POS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_POS, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
-    default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_RES, KT>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS, KT, KW>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_ROPE: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_ROPE, KT, KW>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_ERF: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_ERF, KT, KW>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_GELU_TANH: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_GELU_TANH, KT, KW>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    case EPI_BIAS_POS: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_POS, KT, KW>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((gemm_mfma32_kernel<BM, BN, WAVES_M, WAVES_N, ST, EPI_BIAS_RES, KT, KW>), grid, block, 0, s, ev.start, ev.stop, 0, p); break;
   }
   return hipGetLastError();
 }
@@ -671,7 +725,10 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
     // small products (e.g. 1024 tokens x 448 columns): 128x128 tiles would
     // leave most CUs idle, so 64x64 tiles (one 32x32 block per wave) with
     // four LDS stages: a lone workgroup per CU has nothing else to hide its
-    // load latency behind
+    // load latency behind. With a long K (the Hiera fc2, K = 1792 / 3584)
+    // the waves split K instead (13.2 -> 12.3 us on the 1024x448x1792 fc2);
+    // for short K the partial-tile reduction costs more than it saves
+    if (t128 < 192 && a.K >= 1024) return gemm32_go<64, 64, 2, 2, 4, false, true>(p, a.epi, s, ev);
     if (t128 < 192) return gemm32_go<64, 64, 2, 2, 4>(p, a.epi, s, ev);
     return gemm32_go<128, 128, 2, 2>(p, a.epi, s, ev);
   }
