@@ -135,23 +135,38 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams<T> p) {
     }
   }
 
-  // ---- K / V tile staging: thread -> (key row, head, chunk), chunk fastest
+  // ---- K / V tile staging. K: thread -> (key row, head, chunk), chunk
+  // fastest (a row's chunks are contiguous in memory). V: key fastest, so
+  // that each of the transposing 2-byte LDS writes of a wave covers 64
+  // consecutive keys of one V^T row (chunk fastest put 8 chunks x 4 heads
+  // of a write on two banks: 16-way conflicts)
+  static_assert(256 % KT == 0, "a wave's V loads share one (head, chunk)");
   u32x4 kreg[LOADS], vreg[LOADS];
   auto fetch = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int v = tid + 256 * it;
-      const int c = v % CH, rest = v / CH;
-      const int h = rest % HPW, j = rest / HPW;
-      const int kv = kt * KT + j;
-      if (kv < p.n_kv && c * VN < hd) {
-        const int tk = window_token(p.mode, win, kv, p.n_windows, p.grid_w, p.win_h, p.win_w);
-        const T* rowp = p.qkv + (frame_in + tk) * p.ld_qkv + (hg * HPW + h) * hd + c * VN;
-        kreg[it] = ld16(rowp + D);
-        vreg[it] = ld16(rowp + 2 * D);
-      } else {
-        kreg[it] = u32x4{0, 0, 0, 0};
-        vreg[it] = u32x4{0, 0, 0, 0};
+      {
+        const int c = v % CH, rest = v / CH;
+        const int h = rest % HPW, j = rest / HPW;
+        const int kv = kt * KT + j;
+        if (kv < p.n_kv && c * VN < hd) {
+          const int tk = window_token(p.mode, win, kv, p.n_windows, p.grid_w, p.win_h, p.win_w);
+          kreg[it] = ld16(p.qkv + (frame_in + tk) * p.ld_qkv + D + (hg * HPW + h) * hd + c * VN);
+        } else {
+          kreg[it] = u32x4{0, 0, 0, 0};
+        }
+      }
+      {
+        const int j = v % KT, rest = v / KT;
+        const int c = rest % CH, h = rest / CH;
+        const int kv = kt * KT + j;
+        if (kv < p.n_kv && c * VN < hd) {
+          const int tk = window_token(p.mode, win, kv, p.n_windows, p.grid_w, p.win_h, p.win_w);
+          vreg[it] = ld16(p.qkv + (frame_in + tk) * p.ld_qkv + 2 * D + (hg * HPW + h) * hd + c * VN);
+        } else {
+          vreg[it] = u32x4{0, 0, 0, 0};
+        }
       }
     }
   };
@@ -159,13 +174,19 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams<T> p) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int v = tid + 256 * it;
-      const int c = v % CH, rest = v / CH;
-      const int h = rest % HPW, j = rest / HPW;
-      st16(&Ks[h][j][c * VN], kreg[it]);
-      T e[VN];
-      *reinterpret_cast<u32x4*>(e) = vreg[it];
+      {
+        const int c = v % CH, rest = v / CH;
+        const int h = rest % HPW, j = rest / HPW;
+        st16(&Ks[h][j][c * VN], kreg[it]);
+      }
+      {
+        const int j = v % KT, rest = v / KT;
+        const int c = rest % CH, h = rest / CH;
+        T e[VN];
+        *reinterpret_cast<u32x4*>(e) = vreg[it];
 #pragma unroll
-      for (int k = 0; k < VN; ++k) Vt[h][c * VN + k][j] = e[k];
+        for (int k = 0; k < VN; ++k) Vt[h][c * VN + k][j] = e[k];
+      }
     }
   };
 
@@ -710,7 +731,13 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
                   : attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, false>(p, a.batch, s, ev);
     }
   }
-  // small query sets: several heads per workgroup, one wave each
+  // small query sets: several heads per workgroup, one wave each -- unless
+  // that leaves fewer workgroups than CUs (the 64 mask units of a 4096-token
+  // Hiera transition): then one head per workgroup (three of its four waves
+  // idle, but four times the workgroups; 8.3 -> 6.5 us there)
+  if (p.n_q <= 16 && a.heads % 4 == 0 && (int64_t)a.batch * p.windows * (a.heads / 4) < 256) {
+    return pool ? attn_go<T, 1, 1, true>(a, p, s, ev) : attn_go<T, 1, 1, false>(a, p, s, ev);
+  }
   if (p.n_q <= 16 && a.heads % 4 == 0) {
     return pool ? attn_go<T, 1, 4, true>(a, p, s, ev) : attn_go<T, 1, 4, false>(a, p, s, ev);
   }
