@@ -55,7 +55,7 @@ def describe(spec):
         (", " + ", ".join(extra)) if extra else "")
 
 
-def stage_work(spec):
+def stage_work(spec, residual_in_qkv=False):
     """Algorithmic FLOPs and minimum HBM bytes of each stage."""
     from vision_transformer_encoder_vit_amd import work
     e = work.DTYPE_BYTES[spec["dtype"]]
@@ -68,10 +68,16 @@ def stage_work(spec):
          "ln2": (0.0, work.layernorm_bytes(m_out, Do, spec["dtype"]))}
     w["qkv"] = (work.gemm_flops(*g["qkv"]), work.gemm_bytes(*g["qkv"], spec["dtype"]))
     if "res" in g:
-        # projection of every input row, then a 4x pool (read 4 rows, write 1)
-        w["residual"] = (work.gemm_flops(*g["res"]),
-                         work.gemm_bytes(*g["res"], spec["dtype"]) + e * (m_in + m_out) * Do)
+        # projection of every input row, 4x max-pooled: h and W_res read
+        # once, the pooled rows written once
+        w["residual"] = (work.gemm_flops(*g["res"]), e * (m_in * Di + Do * Di + m_out * Do))
     else:
+        w["residual"] = (0.0, 0.0)
+    if residual_in_qkv and "res" in g:
+        # the qkv GEMM also computes the pooled residual projection: its
+        # stage carries that work (h is read once for both)
+        f, by = w["qkv"]
+        w["qkv"] = (f + w["residual"][0], by + e * (Do * Di + m_out * Do))
         w["residual"] = (0.0, 0.0)
     w["attn"] = (work.attention_flops(spec), work.attention_bytes(spec))
     w["proj"] = (work.gemm_flops(*g["proj"]), work.gemm_bytes(*g["proj"], spec["dtype"], extra_rows_in=m_out))
@@ -193,7 +199,7 @@ def run(spec, steps, warmup, with_cpu):
 
     ms_step = 1e3 * elapsed / steps
     tokens = spec["batch"] * spec["grid_h"] * spec["grid_w"]
-    wk = stage_work(spec)
+    wk = stage_work(spec, residual_in_qkv=spec["q_stride"] == 4 and "residual" not in active and "fused" not in active)
     mfma_stages = [st for st in ("qkv", "residual", "attn", "proj", "fc1", "fc2", "fused") if st in active]
     flops = sum(wk[s][0] for s in mfma_stages)
     t_mfma = sum(stage_us[s] for s in mfma_stages) * 1e-6

@@ -214,7 +214,10 @@ vit_status vit_block_forward_seams(vit_block_t plan, const vit_block_weights* w,
 /* Stages of one forward, in launch order (for vit_block_forward_timed). */
 enum {
   VIT_STAGE_LN1 = 0,      /* LayerNorm of x                              */
-  VIT_STAGE_QKV = 1,      /* qkv projection (+ bias, + RoPE)              */
+  VIT_STAGE_QKV = 1,      /* qkv projection (+ bias, + RoPE); at a bf16
+                             transition without RoPE or V^T output it also
+                             computes the pooled residual projection, and
+                             VIT_STAGE_RESIDUAL is then empty           */
   VIT_STAGE_RESIDUAL = 2, /* transition: residual projection + 4x pool    */
   VIT_STAGE_ATTN = 3,     /* windowed / global attention                  */
   VIT_STAGE_PROJ = 4,     /* out projection + bias + residual             */

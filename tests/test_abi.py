@@ -185,7 +185,15 @@ def test_stage_mask():
     m = vb.Plan(vb.desc_from_spec(synth.CONFIGS["c5w_sam3_win"])).stage_mask()
     assert not m >> names.index("residual") & 1 and m >> names.index("attn") & 1
     assert not m >> names.index("fused") & 1
+    # a bf16 transition: the qkv GEMM also computes the pooled residual
     m = vb.Plan(vb.desc_from_spec(synth.CONFIGS["c3a_hiera_trans"])).stage_mask()
+    assert not m >> names.index("residual") & 1 and m >> names.index("qkv") & 1
+    # fp32 (VALU GEMM), or a qkv epilogue that writes V^T for global
+    # attention: a residual stage of its own
+    m = vb.Plan(vb.desc_from_spec(synth.derive(synth.CONFIGS["c3a_hiera_trans"], dtype="f32"))).stage_mask()
+    assert m >> names.index("residual") & 1
+    m = vb.Plan(vb.desc_from_spec(synth.derive(synth.CONFIGS["c3b_hiera_s2"], grid_h=32, grid_w=32, dim_in=224,
+                                                dim_out=448, q_stride=4))).stage_mask()
     assert m >> names.index("residual") & 1
 
 

@@ -61,6 +61,8 @@ struct vit_block_plan {
   bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
   bool attn_vt;          // the large-window attention kernel runs on V^T (workspace off_vt)
   bool vt_in_gemm;       // ... written by the qkv projection's epilogue (else a transpose kernel)
+  bool pool_gemm;        // transition: the residual projection pooled in its GEMM epilogue
+  bool residual_in_qkv;  // ... and computed by the qkv GEMM (a fourth weight segment)
   // Q8_ROW: workspace copies of the int8 payloads in act_dtype (exact), read
   // by the GEMMs, whose epilogues apply the row scales
   size_t off_cres, off_cqkv, off_cq, off_ck, off_cv, off_co, off_c1, off_c2;
@@ -159,6 +161,13 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   p->vt_in_gemm = p->attn_vt && vit::gemm_uses_mfma(d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32,
                                                     d.dim_in, d.dim_in);
   p->off_vt = p->attn_vt ? take(p->m_in, d.dim_out) : 0;
+  // At a transition the residual projection reads the same h as the qkv
+  // projection. On the MFMA path it is pooled in its GEMM's epilogue, and
+  // it joins the qkv GEMM as a fourth weight segment unless that GEMM's
+  // epilogue is taken (RoPE, the V^T output).
+  const vit::DType dtp = d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32;
+  p->pool_gemm = d.q_stride == 4 && vit::gemm_uses_mfma(dtp, d.dim_in, d.dim_in);
+  p->residual_in_qkv = p->pool_gemm && d.rope == VIT_ROPE_NONE && !p->vt_in_gemm;
   p->attn_splits = 1;
   if (p->attn_vt) {
     const int64_t windows = d.attn_mode == VIT_ATTN_SPATIAL
@@ -202,7 +211,8 @@ VIT_API vit_status vit_block_stage_mask(vit_block_t plan, uint32_t* mask) {
   if (plan->fused_mask_unit) {
     *mask = 1u << VIT_STAGE_FUSED;
   } else {
-    *mask = ((1u << VIT_STAGE_FUSED) - 1) & ~(plan->d.q_stride == 4 ? 0u : 1u << VIT_STAGE_RESIDUAL);
+    const bool residual = plan->d.q_stride == 4 && !plan->residual_in_qkv;
+    *mask = ((1u << VIT_STAGE_FUSED) - 1) & ~(residual ? 0u : 1u << VIT_STAGE_RESIDUAL);
   }
   return ok();
 }
@@ -447,6 +457,30 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   } else {
     g.epi = vit::EPI_BIAS;
   }
+  // the residual projection as a fourth weight segment whose columns the
+  // epilogue max-pools over the four quarters of each frame straight into r
+  // (Hiera's query pool; no unpooled copy, no separate launches)
+  const bool pool_gemm = P.pool_gemm, merged = P.residual_in_qkv;
+  void* r_out = S.r ? S.r : base + P.off_r;
+  if (merged) {
+    if (d.qkv_layout == VIT_QKV_FUSED) {
+      for (int k = 0; k < 3; ++k) {
+        g.W[k] = static_cast<const char*>(Wqkv) + (size_t)k * Do * Di * P.esize;
+        g.bias[k] = w->b_qkv + (size_t)k * Do;
+        g.wscale[k] = q8 ? static_cast<const void*>(static_cast<const uint16_t*>(w->s_qkv) + (size_t)k * Do) : nullptr;
+      }
+    }
+    g.W[3] = Wres;
+    g.bias[3] = w->b_res;
+    g.wscale[3] = q8 ? w->s_res : nullptr;
+    g.seg_cols = Do;
+    g.N = 4 * Do;
+    g.epi = vit::EPI_POOL;
+    g.tokens_per_frame = P.n_in;
+    g.pool_out = r_out;
+    g.ld_pool = Do;
+    g.pool_col0 = 3 * Do;
+  }
   if (P.vt_in_gemm) {
     g.vt = base + P.off_vt;
     g.vt_col0 = 2 * Do;
@@ -468,7 +502,31 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
 
   // 3. residual: x, or pool4(h W_res^T + b_res) at a transition
   const void* r = x;
-  if (d.q_stride == 4) {
+  if (d.q_stride == 4 && merged) {
+    // written by the qkv GEMM
+    if ((st = mark_empty(VIT_STAGE_RESIDUAL)) != VIT_OK) return st;
+    r = r_out;
+  } else if (d.q_stride == 4 && pool_gemm) {
+    vit::GemmArgs gr;
+    gr.A = h;
+    gr.lda = Di;
+    gr.M = (int)P.m_in;
+    gr.N = Do;
+    gr.K = Di;
+    gr.W[0] = Wres;
+    gr.bias[0] = w->b_res;
+    gr.wscale[0] = q8 ? w->s_res : nullptr;
+    gr.seg_cols = Do;
+    gr.ldc = Do;
+    gr.epi = vit::EPI_POOL;
+    gr.tokens_per_frame = P.n_in;
+    gr.pool_out = r_out;
+    gr.ld_pool = Do;
+    gr.pool_col0 = 0;
+    e = vit::launch_gemm(gr, dt, s, stage_ev(VIT_STAGE_RESIDUAL));
+    if ((st = device_status(e, "gemm (pooled residual projection)")) != VIT_OK) return st;
+    r = r_out;
+  } else if (d.q_stride == 4) {
     vit::GemmArgs gr;
     gr.A = h;
     gr.lda = Di;
@@ -489,10 +547,6 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
                           only_stop(stage_ev(VIT_STAGE_RESIDUAL)));
     if ((st = device_status(e, "pool4 (residual)")) != VIT_OK) return st;
     r = rr;
-    if (S.q_pooled) {
-      e = vit::launch_pool4(qkv, 3LL * Do, S.q_pooled, Do, d.batch, P.n_in, Do, dt, s);
-      if ((st = device_status(e, "pool4 (q seam)")) != VIT_OK) return st;
-    }
   } else {
     // no kernel in this stage: mark it empty
     if ((st = mark_empty(VIT_STAGE_RESIDUAL)) != VIT_OK) return st;
@@ -500,6 +554,10 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
       e = hipMemcpyAsync(S.r, x, x_bytes, hipMemcpyDeviceToDevice, s);
       if ((st = device_status(e, "copy (r seam)")) != VIT_OK) return st;
     }
+  }
+  if (d.q_stride == 4 && S.q_pooled) {
+    e = vit::launch_pool4(qkv, 3LL * Do, S.q_pooled, Do, d.batch, P.n_in, Do, dt, s);
+    if ((st = device_status(e, "pool4 (q seam)")) != VIT_OK) return st;
   }
 
 

@@ -51,6 +51,27 @@ struct GemmParams {
   const _Float16* ws2;
 };
 
+// EPI_POOL's arguments: a fourth weight segment, the pooled output and its
+// first column. A type of its own, so that the other kernels' argument
+// block (and code) stays as it is.
+template <typename T>
+struct GemmPoolParams : GemmParams<T> {
+  const T* W3;
+  const float* b3;
+  const _Float16* ws3;
+  T* pool_out;
+  int64_t ld_pool;
+  int pool_col0;
+};
+
+// Pointer of segment seg; S4 (EPI_POOL) adds a fourth. By value: taking
+// the kernel argument block by reference changes how the compiler loads it.
+template <bool S4, typename X>
+__device__ __forceinline__ X seg_pick(X a0, X a1, X a2, X a3, int seg) {
+  if constexpr (S4) return seg == 0 ? a0 : (seg == 1 ? a1 : (seg == 3 ? a3 : a2));
+  else return seg == 0 ? a0 : (seg == 1 ? a1 : a2);
+}
+
 // Position-table row of token m (EPI_BIAS_POS), see PosMode.
 template <typename P>
 __device__ __forceinline__ int pos_row(const P& p, int64_t m) {
@@ -282,7 +303,8 @@ struct WaitAhead {
 // about one workgroup per CU, where one wave per SIMD with one MFMA per K
 // step spends most of each step waiting on its LDS fragment reads.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI, bool KT, bool KW>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(GemmParams<bf16> p) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
+    typename std::conditional<EPI == EPI_POOL, GemmPoolParams<bf16>, GemmParams<bf16>>::type p) {
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   constexpr int BK = 64;
   static_assert(ST >= 2, "at least two LDS stages");
@@ -297,8 +319,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   constexpr int SM = KW && NW * BM * CROW * 2 > ST * STAGE ? NW * BM * CROW * 2 : ST * STAGE;
   __shared__ __attribute__((aligned(1024))) bf16 sm[SM];
 
+  // EPI_POOL: a tile is PB pooled rows; its BM A rows are the four quarter
+  // rows of each (local row r: quarter r / PB, pooled row m0 + r % PB)
+  constexpr bool POOL = EPI == EPI_POOL;
+  constexpr int PB = BM / 4;
+  const bf16* W3 = nullptr;
+  const float* b3 = nullptr;
+  const _Float16* ws3 = nullptr;
+  if constexpr (POOL) {
+    W3 = p.W3;
+    b3 = p.b3;
+    ws3 = p.ws3;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.N + BN - 1) / BN, tiles_m = POOL ? (p.M / 4 + PB - 1) / PB : (p.M + BM - 1) / BM;
 
   // Warm the memory-side cache with the whole weight matrix before the first
   // tile: one 4-byte read per 128-byte line, dealt to the threads of the
@@ -314,14 +348,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     for (int64_t g = (int64_t)blockIdx.x * NT + tid; g < lines; g += (int64_t)gridDim.x * NT) {
       const int n = (int)(g / lines_per_row), kl = (int)(g - (int64_t)n * lines_per_row);
       const int seg = n / p.seg_cols;
-      const bf16* base = seg == 0 ? p.W0 : (seg == 1 ? p.W1 : p.W2);
+      const bf16* base = seg_pick<POOL>(p.W0, p.W1, p.W2, W3, seg);
       touch ^= *reinterpret_cast<const uint32_t*>(base + (int64_t)(n - seg * p.seg_cols) * p.K + kl * 64);
     }
   }
 
   int tmi, tni;
   xcd_tile<8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tmi, tni);
-  const int m0 = tmi * BM, n0 = tni * BN;
+  const int m0 = tmi * (POOL ? PB : BM), n0 = tni * BN;
 
   // per-lane source rows (clamped into the matrix: rows past M or N are
   // loaded but never stored)
@@ -331,12 +365,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
     const int row = (wave * LPW + j) * 8 + lane / 8;
     const int chunk = (lane & 7) ^ lds_swz(row);
     if (row < BM) {
-      const int m = min(m0 + row, p.M - 1);
+      int m;
+      if constexpr (POOL) {
+        const int q4 = p.tokens_per_frame / 4, pr = min(m0 + row % PB, p.M / 4 - 1);
+        m = (pr / q4) * p.tokens_per_frame + (row / PB) * q4 + pr % q4;
+      } else {
+        m = min(m0 + row, p.M - 1);
+      }
       src[j] = p.A + (int64_t)m * p.lda + chunk * 8;
     } else {
       const int n = min(n0 + row - BM, p.N - 1);
       const int seg = n / p.seg_cols;
-      const bf16* base = seg == 0 ? p.W0 : (seg == 1 ? p.W1 : p.W2);
+      const bf16* base = seg_pick<POOL>(p.W0, p.W1, p.W2, W3, seg);
       src[j] = base + (int64_t)(n - seg * p.seg_cols) * p.K + chunk * 8;
     }
   }
@@ -465,6 +505,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
   // i*32 + 8q + 4g + e in register 4q + e.
   constexpr int PR0 = (ST * STAGE * 2) / (CROW * 4);
   constexpr int PR = KW || PR0 >= BM ? BM : (PR0 >= BM / 2 ? BM / 2 : BM / 4);
+  static_assert(!POOL || PR == BM, "EPI_POOL stages the whole tile at once");
   static_assert(PR >= BM / 4 && PR % 32 == 0, "LDS too small for the epilogue");
   float* cs = reinterpret_cast<float*>(sm);
   float* cw = cs + (KW ? wave * BM * CROW : 0);  // this wave's staging tile
@@ -481,8 +522,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
       for (int q = 0; q < 4; ++q) {
         const int n = min(n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * g, p.N - 4);
         const int seg = n / p.seg_cols;
-        scl[i][q] = *reinterpret_cast<const u32x2*>((seg == 0 ? p.ws0 : (seg == 1 ? p.ws1 : p.ws2)) +
-                                                    (n - seg * p.seg_cols));
+        scl[i][q] = *reinterpret_cast<const u32x2*>(seg_pick<POOL>(p.ws0, p.ws1, p.ws2, ws3, seg) + (n - seg * p.seg_cols));
       }
   }
 #pragma unroll
@@ -538,6 +578,52 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(Gem
         const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
         st16(p.vt + (((int64_t)fb * p.vt_heads + hh) * p.vt_hd + d) * p.vt_tokens + t, pack16<bf16>(v));
       }
+    }
+    if constexpr (POOL) {
+      const int q4 = p.tokens_per_frame / 4, mp = p.M / 4;
+      // columns < pool_col0: every row, back at its own token
+      for (int e = tid; e < BM * G8; e += NT) {
+        const int r = e / G8, c8 = (e - r * G8) * 8;
+        const int n = n0 + c8, pr = m0 + r % PB;
+        if (n >= p.pool_col0 || n >= p.N || pr >= mp) continue;
+        const int64_t m = (int64_t)(pr / q4) * p.tokens_per_frame + (r / PB) * q4 + pr % q4;
+        float v[8];
+        *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8);
+        *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4);
+        const int seg = n / p.seg_cols;
+        const float* bb = seg_pick<true>(p.b0, p.b1, p.b2, b3, seg) + (n - seg * p.seg_cols);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] += bb[t];
+        st16(p.C + m * p.ldc + n, pack16<bf16>(v));
+      }
+      // columns >= pool_col0: the max over the four quarter rows, then the bias
+      for (int e = tid; e < PB * G8; e += NT) {
+        const int i = e / G8, c8 = (e - i * G8) * 8;
+        const int n = n0 + c8, pr = m0 + i;
+        if (n < p.pool_col0 || n >= p.N || pr >= mp) continue;
+        f32x4 lo = *reinterpret_cast<const f32x4*>(cs + i * CROW + c8);
+        f32x4 hi = *reinterpret_cast<const f32x4*>(cs + i * CROW + c8 + 4);
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(cs + (q * PB + i) * CROW + c8);
+          const f32x4 h2 = *reinterpret_cast<const f32x4*>(cs + (q * PB + i) * CROW + c8 + 4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            lo[t] = fmaxf(lo[t], l2[t]);
+            hi[t] = fmaxf(hi[t], h2[t]);
+          }
+        }
+        const int seg = n / p.seg_cols;
+        const float* bb = seg_pick<true>(p.b0, p.b1, p.b2, b3, seg) + (n - seg * p.seg_cols);
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[t] = lo[t] + bb[t];
+          v[4 + t] = hi[t] + bb[4 + t];
+        }
+        st16(p.pool_out + (int64_t)pr * p.ld_pool + (n - p.pool_col0), pack16<bf16>(v));
+      }
+      continue;
     }
     for (int e = tid; e < PR * G8; e += NT) {
       const int r = e / G8, c8 = (e - r * G8) * 8;
@@ -621,6 +707,15 @@ static hipError_t gemm32_go(const GemmParams<bf16>& p, int epi, hipStream_t s, S
   return hipGetLastError();
 }
 
+// EPI_POOL: 64x64 tiles of 16 pooled rows (64 A rows)
+template <int ST, bool KT>
+static hipError_t gemm32_pool_go(const GemmPoolParams<bf16>& p, hipStream_t s, StageEvents ev) {
+  const int64_t tiles = (int64_t)((p.M / 4 + 15) / 16) * ((p.N + 63) / 64);
+  hipExtLaunchKernelGGL((gemm_mfma32_kernel<64, 64, 2, 2, ST, EPI_POOL, KT, false>), dim3((unsigned)tiles), dim3(256),
+                        0, s, ev.start, ev.stop, 0, p);
+  return hipGetLastError();
+}
+
 template <typename T>
 static GemmParams<T> make_params(const GemmArgs& a) {
   GemmParams<T> p;
@@ -688,6 +783,22 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
   if (a.vt && (!mfma32 || (a.epi != EPI_BIAS && a.epi != EPI_BIAS_ROPE) || a.M % 8 || a.vt_tokens <= 0 ||
                a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 || (a.N - a.vt_col0) != a.vt_heads * a.vt_hd))
     return hipErrorInvalidValue;
+  if (a.epi == EPI_POOL) {
+    const int T = a.tokens_per_frame;
+    if (!mfma32 || a.vt || T <= 0 || T % 4 || a.M % T || a.pool_col0 % 8 || a.pool_col0 > a.N || !a.pool_out)
+      return hipErrorInvalidValue;
+    GemmPoolParams<bf16> p;
+    static_cast<GemmParams<bf16>&>(p) = make_params<bf16>(a);
+    p.W3 = (const bf16*)(a.W[3] ? a.W[3] : a.W[0]);
+    p.b3 = a.bias[3] ? a.bias[3] : a.bias[0];
+    p.ws3 = (const _Float16*)(a.wscale[3] ? a.wscale[3] : a.wscale[0]);
+    p.pool_out = (bf16*)a.pool_out;
+    p.ld_pool = a.ld_pool;
+    p.pool_col0 = a.pool_col0;
+    const int64_t tiles = (int64_t)((a.M / 4 + 15) / 16) * ((a.N + 63) / 64);
+    if (a.K % 64) return tiles < 512 ? gemm32_pool_go<4, true>(p, s, ev) : gemm32_pool_go<2, true>(p, s, ev);
+    return tiles < 512 ? gemm32_pool_go<4, false>(p, s, ev) : gemm32_pool_go<2, false>(p, s, ev);
+  }
   if (dt == DType::F32) return gemm_go<float, 64, 64, 2, 2>(a, s, ev);
   if (mfma32) {
     // One full wave of 256x256 tiles fills the 256 CUs. Otherwise two

@@ -22,6 +22,8 @@ enum Epilogue {
   EPI_GELU_TANH = 3,   // C = gelu_tanh(acc + bias)
   EPI_BIAS_RES = 4,    // C = res + (acc + bias); branch = acc + bias if set
   EPI_BIAS_POS = 5,    // C = acc + bias + pos[row(token)] (bias and pos may be NULL)
+  EPI_POOL = 6,        // columns < pool_col0: C = acc + bias; the rest 2x2-max-pooled
+                       // into pool_out (see GemmArgs)
 };
 
 // Position-table row of token t = y * grid_w + x of a frame (EPI_BIAS_POS):
@@ -32,12 +34,12 @@ enum PosMode { POS_NONE = 0, POS_ROWS = 1, POS_BUCKET = 2, POS_TILE = 3 };
 
 // C[M, N] = epilogue(A[M, K] * W[N, K]^T + bias). W and bias may be split
 // into up to three column segments of seg_cols columns each (separate q/k/v
-// weights); with one segment seg_cols = N.
+// weights), four with EPI_POOL; with one segment seg_cols = N.
 struct GemmArgs {
   const void* A = nullptr;
   int64_t lda = 0;
-  const void* W[3] = {nullptr, nullptr, nullptr};
-  const float* bias[3] = {nullptr, nullptr, nullptr};
+  const void* W[4] = {nullptr, nullptr, nullptr, nullptr};
+  const float* bias[4] = {nullptr, nullptr, nullptr, nullptr};
   int seg_cols = 0;
   void* C = nullptr;
   int64_t ldc = 0;
@@ -67,7 +69,15 @@ struct GemmArgs {
   // optional float16 scale per weight row (output column), segment-wise
   // like W: acc[m, n] * wscale[n] before the bias (integer-valued W rows
   // of q8_row weights)
-  const void* wscale[3] = {nullptr, nullptr, nullptr};
+  const void* wscale[4] = {nullptr, nullptr, nullptr, nullptr};
+  // EPI_POOL (bf16 MFMA path only): A rows are frames of tokens_per_frame
+  // tokens (a multiple of 4; M a multiple of it). Columns >= pool_col0 (a
+  // multiple of 8) are not written to C: pool_out[f * T/4 + t, n - pool_col0]
+  // = max over s < 4 of (acc + bias)[f * T + s * T/4 + t, n] (the Hiera
+  // query pool over the four unrolled quarters of a frame), ld_pool apart.
+  void* pool_out = nullptr;
+  int64_t ld_pool = 0;
+  int pool_col0 = 0;
 };
 hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents ev = {});
 // The bf16 MFMA path takes K >= 64 with K % 16 == 0 (a last K tile of 16,
