@@ -22,6 +22,9 @@ SMALL = {
     "c2_32x32": d(C["c2_hiera_s0"], grid_h=32, grid_w=32, n_windows=16),
     "c3a_16x16": d(C["c3a_hiera_trans"], grid_h=16, grid_w=16, n_windows=16),
     "c3a_32x32_w8": d(C["c3a_hiera_trans"], grid_h=32, grid_w=32, n_windows=8),
+    # pooled epilogue with 36 pooled rows per frame: tiles of 16 pooled rows
+    # straddle the two frames and the last one is ragged
+    "c3a_b2_12x12_w9": d(C["c3a_hiera_trans"], batch=2, grid_h=12, grid_w=12, n_windows=9),
     "c3b_12x12": d(C["c3b_hiera_s2"], grid_h=12, grid_w=12),
     "c3b_pool_global": d(C["c3b_hiera_s2"], grid_h=16, grid_w=16, dim_in=224, dim_out=448, q_stride=4),
     "c4_b3_9x13": d(C["c4_siglip_b8"], batch=3, grid_h=9, grid_w=13, dim_in=192, dim_out=192,
