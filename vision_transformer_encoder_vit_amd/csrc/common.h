@@ -97,21 +97,22 @@ template <> struct Mma<float> {
   }
 };
 
-// erf-form GELU, 0.5 v (1 + erf(v / sqrt 2)). erf(z), z >= 0, by the
+// erf-form GELU, 0.5 v (1 + erf(v / sqrt 2)). With z = |v| / sqrt 2, the
 // rational approximation of Abramowitz & Stegun, Handbook of Mathematical
-// Functions, formula 7.1.26 (|error| <= 1.5e-7): with t = 1 / (1 + p z),
-// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2); erf is odd.
-// Two hardware transcendentals (reciprocal, exp2) and six FMAs.
+// Functions, formula 7.1.26 (|error| <= 1.5e-7) gives erfc(z) =
+// t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z).
+// With q = erfc(z) / 2 (the a_i halved), GELU(v) = v (1 - q) for v >= 0 and
+// v q for v < 0: the negative tail comes straight from erfc, without the
+// cancellation in 1 - erf. Two hardware transcendentals (reciprocal, exp2).
 __device__ __forceinline__ float gelu_erf_as(float v) {
-  const float z = fabsf(v) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
-  float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
-  poly = __builtin_fmaf(t, poly, 1.421413741f);
-  poly = __builtin_fmaf(t, poly, -0.284496736f);
-  poly = __builtin_fmaf(t, poly, 0.254829592f);
-  poly *= t;
-  const float erf_z = __builtin_fmaf(-poly, __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f), 1.0f);
-  return 0.5f * v * (1.0f + copysignf(erf_z, v));
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f * 0.70710678118654752f, fabsf(v), 1.0f));
+  float poly = __builtin_fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+  poly = __builtin_fmaf(t, poly, 0.5f * 1.421413741f);
+  poly = __builtin_fmaf(t, poly, 0.5f * -0.284496736f);
+  poly = __builtin_fmaf(t, poly, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(v * v * (-0.5f * 1.4426950408889634f));  // exp(-z^2)
+  const float r = v * (poly * t) * e;  // v q
+  return v >= 0.f ? v - r : r;
 }
 
 // tanh-approximated GELU, 0.5 v (1 + tanh(u)) with u = sqrt(2/pi)(v + 0.044715 v^3),
