@@ -67,6 +67,22 @@ def test_q8_block_full_size_sampled_rows(name):
         gu.check(name + ":" + k, got, ref[k], spec)
 
 
+@pytest.mark.parametrize("name", ["c2_32x32", "c2_hiera_s0"])
+def test_q8_single_kernel_mask_units(name):
+    # the whole-block-per-mask-unit kernel reading the int8 payloads itself
+    # (vit_block_forward; the seams entry point runs the step kernels)
+    from vision_transformer_encoder_vit_amd import binding as vb
+    spec = dict(SMALL[name] if name in SMALL else C[name], weights="q8_row")
+    print("case q8 fused", name, flush=True)
+    assert vb.Plan(vb.desc_from_spec(spec)).stage_mask() == 1 << vb.STAGES.index("fused")
+    inp = synth.make_q8_inputs(spec, seed=3)
+    y, _ = gu.run_block(spec, gu.to_device(inp, spec), seams=False)
+    rows = _sample_rows(synth.out_tokens(spec), 64, 4)
+    ref = ob.block_forward_rows(inp["x"], quant.dequant_block(inp), spec, rows)
+    mx, rel = gu.check(name + ":y", gu.to64(y)[:, rows], ref["y"], spec)
+    print("  y max abs %.3e rel %.3e" % (mx, rel))
+
+
 def test_q8_siglip_tower_full_frame():
     # 12 blocks with int8 weights plus post_layernorm, one full frame
     import torch

@@ -191,7 +191,7 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
     p->off_c2 = take(Do, F);
   }
   p->ws_bytes = o;
-  p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 && d.weight_format == VIT_WEIGHTS_ACT &&
+  p->fused_mask_unit = d.act_dtype == VIT_DTYPE_BF16 &&
                        d.attn_mode == VIT_ATTN_MASK_UNIT && d.q_stride == 1 &&
                        d.rope == VIT_ROPE_NONE &&
                        vit::fused_mask_unit_supported(d.dim_out, d.heads, p->head_dim, d.mlp_hidden, p->n_in / d.n_windows) &&
@@ -342,14 +342,21 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     f.ln1_b = w->ln1_beta;
     f.ln2_g = w->ln2_gamma;
     f.ln2_b = w->ln2_beta;
+    // q8_row: the kernel reads the int8 payloads itself (1-byte elements)
+    const bool q8w = d.weight_format == VIT_WEIGHTS_Q8_ROW;
     if (d.qkv_layout == VIT_QKV_FUSED) {
-      const size_t wseg = (size_t)Do * Di * P.esize;
+      const size_t wseg = (size_t)Do * Di * (q8w ? 1 : P.esize);
       f.wq = w->w_qkv;
       f.wk = (const char*)w->w_qkv + wseg;
       f.wv = (const char*)w->w_qkv + 2 * wseg;
       f.bq = w->b_qkv;
       f.bk = w->b_qkv + Do;
       f.bv = w->b_qkv + 2 * Do;
+      if (q8w) {
+        f.sq = w->s_qkv;
+        f.sk = static_cast<const uint16_t*>(w->s_qkv) + Do;
+        f.sv = static_cast<const uint16_t*>(w->s_qkv) + 2 * Do;
+      }
     } else {
       f.wq = w->w_q;
       f.wk = w->w_k;
@@ -357,6 +364,17 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
       f.bq = w->b_q;
       f.bk = w->b_k;
       f.bv = w->b_v;
+      if (q8w) {
+        f.sq = w->s_q;
+        f.sk = w->s_k;
+        f.sv = w->s_v;
+      }
+    }
+    f.q8 = q8w;
+    if (q8w) {
+      f.so = w->s_o;
+      f.s1 = w->s_fc1;
+      f.s2 = w->s_fc2;
     }
     f.wo = w->w_o;
     f.bo = w->b_o;

@@ -35,7 +35,8 @@ constexpr int QS_MAX = 3 * DP + 8;  // q|k|v row stride for the widest supported
 constexpr int US_MAX = 512 + 8;     // u row stride for the widest supported MLP
 constexpr int A_MAX = (TW * QS_MAX + HPR * 64 * VTS) > (TW * US_MAX) ? (TW * QS_MAX + HPR * 64 * VTS) : (TW * US_MAX);
 constexpr int BIAS_MAX = 3 * DP + DP + 512 + DP;  // b_q|b_k|b_v, b_o, b_1, b_2 (fp32)
-constexpr int LDS_ELEMS = 3 * TW * XS + A_MAX + 2 * 4 * DP + 2 * BIAS_MAX;  // bf16 elements; fp32 LN params and biases last
+// bf16 elements; fp32 LN params, biases and (q8_row weights) the row scales last
+constexpr int LDS_ELEMS = 3 * TW * XS + A_MAX + 2 * 4 * DP + 2 * BIAS_MAX + 2 * BIAS_MAX;
 
 struct FusedParams {
   const bf16* x;
@@ -51,6 +52,9 @@ struct FusedParams {
   const float* b2;
   int tokens, n_windows, dim, heads, head_dim, mlp, qs, us;  // qs/us: LDS row strides of q|k|v and u
   float eps, scale_log2;
+  // q8_row weights: the matrices above are int8 payloads (row stride = K
+  // bytes) and these their float16 row scales
+  const _Float16 *sq, *sk, *sv, *so, *s1, *s2;
 };
 
 __device__ __forceinline__ float gelu_erf_d(float v) { return gelu_erf_as(v); }
@@ -110,7 +114,9 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
 template <int NTM, int KSM>
 struct WFrags {
   u32x4 f[NTM][KSM];
-  template <typename Wsel>
+  // wrow(n): start of weight row n (bf16, or int8 payload when Q8: its 8
+  // values are widened to bf16, exactly since |q| <= 127)
+  template <bool Q8, typename Wsel>
   __device__ __forceinline__ void load(Wsel wrow, int N, int kreal) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 15, g = lane >> 4;
@@ -118,11 +124,21 @@ struct WFrags {
     for (int i = 0; i < NTM; ++i) {
       const int nt = wave + i * NWF;
       const bool nok = nt * 16 < N;
-      const bf16* wr = wrow(nok ? nt * 16 + fr : 0);
+      const void* wr = wrow(nok ? nt * 16 + fr : 0);
 #pragma unroll
       for (int kk = 0; kk < KSM; ++kk) {
         const int k = kk * 32 + g * 8;
-        f[i][kk] = (nok && k < kreal) ? ld16(wr + k) : u32x4{0, 0, 0, 0};
+        if (!(nok && k < kreal)) {
+          f[i][kk] = u32x4{0, 0, 0, 0};
+        } else if constexpr (Q8) {
+          const u32x2 q = *reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(wr) + k);
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (float)(int8_t)((q[e / 4] >> (8 * (e % 4))) & 0xFF);
+          f[i][kk] = pack16<bf16>(v);
+        } else {
+          f[i][kk] = ld16(static_cast<const bf16*>(wr) + k);
+        }
       }
     }
   }
@@ -159,7 +175,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <bool TANH>
+template <bool TANH, bool Q8>
 __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p) {
   // one static allocation sized for the largest supported block (static LDS
   // can use the CU's full 160 KB)
@@ -175,6 +191,10 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   float* bo_s = bqkv + 3 * DP;         // [D]
   float* b1_s = bo_s + DP;             // [mlp]
   float* b2_s = b1_s + 512;            // [D]
+  float* sqkv = b2_s + DP;             // Q8: row scales, laid out like the biases
+  float* so_s = sqkv + 3 * DP;
+  float* s1_s = so_s + DP;
+  float* s2_s = s1_s + 512;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = p.dim, hd = p.head_dim;
@@ -196,14 +216,28 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   for (int e = tid; e < 5 * D + p.mlp; e += 64 * NWF) {
     if (e < 3 * D) {
       bqkv[e] = e < D ? p.bq[e] : (e < 2 * D ? p.bk[e - D] : p.bv[e - 2 * D]);
+      if (Q8) sqkv[e] = (float)(e < D ? p.sq[e] : (e < 2 * D ? p.sk[e - D] : p.sv[e - 2 * D]));
     } else if (e < 4 * D) {
       bo_s[e - 3 * D] = p.bo[e - 3 * D];
+      if (Q8) so_s[e - 3 * D] = (float)p.so[e - 3 * D];
     } else if (e < 5 * D) {
       b2_s[e - 4 * D] = p.b2[e - 4 * D];
+      if (Q8) s2_s[e - 4 * D] = (float)p.s2[e - 4 * D];
     } else {
       b1_s[e - 5 * D] = p.b1[e - 5 * D];
+      if (Q8) s1_s[e - 5 * D] = (float)p.s1[e - 5 * D];
     }
   }
+  // Q8: the accumulator of output column n..n+3 times its row scales
+  auto scaled = [&](f32x4 v, const float* sc, int n) {
+    if constexpr (Q8) v = v * *reinterpret_cast<const f32x4*>(sc + n);
+    return v;
+  };
+  // row start of a weight matrix with rows of K values
+  auto wrow_of = [&](const bf16* w, int64_t n, int K) -> const void* {
+    if constexpr (Q8) return reinterpret_cast<const int8_t*>(w) + n * K;
+    return w + n * K;
+  };
   // with at most HPR heads the qkv epilogue writes V transposed straight into
   // vts (one attention round); rows head_dim..63 of each head stay zero
   const bool vt_direct = p.heads <= HPR;
@@ -216,17 +250,17 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
     }
   }
   WFrags<(3 * DP / 16 + NWF - 1) / NWF, DP / 32> wqkv;
-  wqkv.load([&](int n) { return n < D ? p.wq + (int64_t)n * D : (n < 2 * D ? p.wk + (int64_t)(n - D) * D : p.wv + (int64_t)(n - 2 * D) * D); },
-            3 * D, D);
+  wqkv.load<Q8>([&](int n) { return n < D ? wrow_of(p.wq, n, D) : (n < 2 * D ? wrow_of(p.wk, n - D, D) : wrow_of(p.wv, n - 2 * D, D)); },
+                3 * D, D);
   lds_barrier();
   // ---- LN1 -> cs
   ln_rows(xs, cs, lnp, lnp + DP, D, p.eps);
   WFrags<(DP / 16 + NWF - 1) / NWF, DP / 32> wo;
-  wo.load([&](int n) { return p.wo + (int64_t)n * D; }, D, D);
+  wo.load<Q8>([&](int n) { return wrow_of(p.wo, n, D); }, D, D);
   lds_barrier();
   // ---- q|k|v = h W^T + b -> qkvs
   wqkv.gemm(cs, XS, 3 * D, D, [&](int m, int n, f32x4 v) {
-    v = v + *reinterpret_cast<const f32x4*>(bqkv + n);
+    v = scaled(v, sqkv, n) + *reinterpret_cast<const f32x4*>(bqkv + n);
     if (vt_direct && n >= 2 * D) {  // 4 consecutive d of one head (head_dim % 8 == 0)
       const int vv = n - 2 * D, head = vv / hd, d = vv - head * hd;
 #pragma unroll
@@ -236,7 +270,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
     }
   });
   WFrags<(512 / 16 + NWF - 1) / NWF, DP / 32> w1;
-  w1.load([&](int n) { return p.w1 + (int64_t)n * D; }, p.mlp, D);
+  w1.load<Q8>([&](int n) { return wrow_of(p.w1, n, D); }, p.mlp, D);
   lds_barrier();
 
   // ---- attention, HPR heads per round (waves 4j..4j+3: head h0 + j)
@@ -325,7 +359,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   // ---- x1 = x + ctx W_o^T + b_o -> x1s (cs columns D..DP-1 are still zero)
   wo.gemm(cs, XS, D, D,
       [&](int m, int n, f32x4 v) {
-        v = v + *reinterpret_cast<const f32x4*>(bo_s + n) + load4<bf16>(xs + m * XS + n);
+        v = scaled(v, so_s, n) + *reinterpret_cast<const f32x4*>(bo_s + n) + load4<bf16>(xs + m * XS + n);
         store4<bf16>(x1s + m * XS + n, v);
       });
   lds_barrier();
@@ -335,10 +369,10 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   // ---- u = GELU(h2 W_1^T + b_1) -> uss; fc2's weights are requested first
   // (after LN2's barrier, so issuing them does not hold up LN2)
   WFrags<1, 16> w2;
-  w2.load([&](int n) { return p.w2 + (int64_t)n * p.mlp; }, D, p.mlp);
+  w2.load<Q8>([&](int n) { return wrow_of(p.w2, n, p.mlp); }, D, p.mlp);
   w1.gemm(cs, XS, p.mlp, D,
       [&](int m, int n, f32x4 v) {
-        v = v + *reinterpret_cast<const f32x4*>(b1_s + n);
+        v = scaled(v, s1_s, n) + *reinterpret_cast<const f32x4*>(b1_s + n);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = TANH ? gelu_tanh_d(v[e]) : gelu_erf_d(v[e]);
         store4<bf16>(uss + m * p.us + n, v);
@@ -347,7 +381,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   // ---- y = x1 + u W_2^T + b_2 -> global
   w2.gemm(uss, p.us, D, p.mlp,
       [&](int m, int n, f32x4 v) {
-        v = v + *reinterpret_cast<const f32x4*>(b2_s + n) + load4<bf16>(x1s + m * XS + n);
+        v = scaled(v, s2_s, n) + *reinterpret_cast<const f32x4*>(b2_s + n) + load4<bf16>(x1s + m * XS + n);
         store4<bf16>(p.y + (row0 + (int64_t)m * p.n_windows) * D + n, v);
       });
 }
@@ -395,14 +429,26 @@ hipError_t launch_block_mask_unit_fused(const FusedMUArgs& a, hipStream_t s, Sta
   p.us = a.mlp + 8;
   p.eps = a.eps;
   p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.sq = (const _Float16*)a.sq;
+  p.sk = (const _Float16*)a.sk;
+  p.sv = (const _Float16*)a.sv;
+  p.so = (const _Float16*)a.so;
+  p.s1 = (const _Float16*)a.s1;
+  p.s2 = (const _Float16*)a.s2;
   const int64_t blocks = (int64_t)a.batch * a.n_windows;
   if (blocks == 0) return hipSuccess;
-  if (a.gelu_tanh)
-    hipExtLaunchKernelGGL((block_mask_unit_kernel<true>), dim3((unsigned)blocks), dim3(64 * NWF), 0, s, ev.start,
-                          ev.stop, 0, p);
-  else
-    hipExtLaunchKernelGGL((block_mask_unit_kernel<false>), dim3((unsigned)blocks), dim3(64 * NWF), 0, s, ev.start,
-                          ev.stop, 0, p);
+  const dim3 grid((unsigned)blocks), block(64 * NWF);
+  if (a.q8) {
+    if (a.gelu_tanh)
+      hipExtLaunchKernelGGL((block_mask_unit_kernel<true, true>), grid, block, 0, s, ev.start, ev.stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((block_mask_unit_kernel<false, true>), grid, block, 0, s, ev.start, ev.stop, 0, p);
+  } else {
+    if (a.gelu_tanh)
+      hipExtLaunchKernelGGL((block_mask_unit_kernel<true, false>), grid, block, 0, s, ev.start, ev.stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((block_mask_unit_kernel<false, false>), grid, block, 0, s, ev.start, ev.stop, 0, p);
+  }
   return hipGetLastError();
 }
 

@@ -170,6 +170,9 @@ struct FusedMUArgs {
   int batch = 1, tokens = 0, n_windows = 1, dim = 0, heads = 1, head_dim = 0, mlp = 0;
   float eps = 1e-6f, scale = 1.f;
   bool gelu_tanh = false;
+  // q8_row weights: the w* are int8 payloads, these their float16 row scales
+  bool q8 = false;
+  const void *sq = nullptr, *sk = nullptr, *sv = nullptr, *so = nullptr, *s1 = nullptr, *s2 = nullptr;
 };
 bool fused_mask_unit_supported(int dim, int heads, int head_dim, int mlp, int window_tokens);
 size_t fused_mask_unit_lds_bytes(int dim, int mlp);
