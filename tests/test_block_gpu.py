@@ -47,6 +47,9 @@ SMALL = {
                        mlp=400),
     # 200 keys: V^T path, keys split over two workgroups, ragged last tile
     "c5g_10x20_split": d(C["c5g_sam3_global"], grid_h=10, grid_w=20, dim_in=256, dim_out=256, heads=4, mlp=1024),
+    # 576 keys = 9 tiles over 4 splits of 3: the last split holds no tile
+    "c5g_24x24_empty_split": d(C["c5g_sam3_global"], grid_h=24, grid_w=24, dim_in=256, dim_out=256, heads=4,
+                               mlp=1024),
     "c5w_f32": d(C["c5w_sam3_win"], grid_h=24, grid_w=48, dim_in=128, dim_out=128, heads=2, mlp=256,
                  dtype="f32"),
     "c4_f32": d(C["c4_siglip_b8"], batch=2, grid_h=10, grid_w=10, dim_in=128, dim_out=128, heads=2,
