@@ -110,7 +110,10 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
 // Weight fragments of one product, held in registers: this wave's 16-row
 // weight tiles nt = wave + i*NWF (i < NTM) for K steps kk < KSM (16x32 each,
 // zero past N or kreal). Loading them one phase ahead hides the L2 latency
-// behind the previous phase's work.
+// behind the previous phase's work. Every load is issued unconditionally (at
+// a clamped address, its value then selected away), so that the compiler
+// can count outstanding loads exactly and the products wait only for their
+// own fragments.
 template <int NTM, int KSM>
 struct WFrags {
   u32x4 f[NTM][KSM];
@@ -128,39 +131,69 @@ struct WFrags {
 #pragma unroll
       for (int kk = 0; kk < KSM; ++kk) {
         const int k = kk * 32 + g * 8;
-        if (!(nok && k < kreal)) {
-          f[i][kk] = u32x4{0, 0, 0, 0};
-        } else if constexpr (Q8) {
-          const u32x2 q = *reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(wr) + k);
-          float v[8];
+        const bool ok = nok && k < kreal;
+        const int kc = ok ? k : 0;  // kreal >= 8
+        if constexpr (Q8) {
+          // (int8 payloads are widened as they arrive; loaded under the
+          // lane's own condition, which keeps the widening's registers short-lived)
+          if (!ok) {
+            f[i][kk] = u32x4{0, 0, 0, 0};
+          } else {
+            const u32x2 q = *reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(wr) + k);
+            float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (float)(int8_t)((q[e / 4] >> (8 * (e % 4))) & 0xFF);
-          f[i][kk] = pack16<bf16>(v);
+            for (int e = 0; e < 8; ++e) v[e] = (float)(int8_t)((q[e / 4] >> (8 * (e % 4))) & 0xFF);
+            f[i][kk] = pack16<bf16>(v);
+          }
         } else {
-          f[i][kk] = ld16(static_cast<const bf16*>(wr) + k);
+          const u32x4 w = ld16(static_cast<const bf16*>(wr) + kc);
+          f[i][kk] = ok ? w : u32x4{0, 0, 0, 0};
         }
       }
     }
   }
   // C[64, N] = LDS A[64, K] * W^T; epi(m, n, v) gets 4 consecutive columns
-  // n..n+3 of token m; each weight fragment is reused for 4 token tiles.
+  // n..n+3 of token m. Each A fragment is read once per wave and used for
+  // all of the wave's weight tiles; each weight fragment serves 4 token
+  // tiles. K steps past kreal multiply zero weights by a finite A fragment
+  // (the last real step's), so the step loop has no branches.
   template <typename Epi>
   __device__ __forceinline__ void gemm(const bf16* As, int lda, int N, int kreal, Epi epi) const {
+    const int wave = threadIdx.x >> 6;
+    int nv = 0;
+#pragma unroll
+    for (int i = 0; i < NTM; ++i) nv += (wave + i * NWF) * 16 < N ? 1 : 0;
+    gemm_nv<NTM>(nv, As, lda, kreal, epi);
+  }
+
+ private:
+  template <int NV, typename Epi>
+  __device__ __forceinline__ void gemm_nv(int nv, const bf16* As, int lda, int kreal, Epi epi) const {
+    if constexpr (NV > 1) {
+      if (nv < NV) {
+        gemm_nv<NV - 1>(nv, As, lda, kreal, epi);
+        return;
+      }
+    } else {
+      if (nv < 1) return;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 15, g = lane >> 4;
-    const int ksteps = (kreal + 31) / 32;
+    const int klast = (kreal + 31) / 32 - 1;
 #pragma unroll
-    for (int i = 0; i < NTM; ++i) {
-      const int nt = wave + i * NWF;
-      if (nt * 16 >= N) break;
+    for (int mt = 0; mt < TW / 16; ++mt) {
+      f32x4 acc[NV];
 #pragma unroll
-      for (int mt = 0; mt < TW / 16; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NV; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const bf16* arow = As + (mt * 16 + fr) * lda + g * 8;
 #pragma unroll
-        for (int kk = 0; kk < KSM; ++kk)
-          if (kk < ksteps) acc = Mma<bf16>::step(f[i][kk], ld16(As + (mt * 16 + fr) * lda + kk * 32 + g * 8), acc);
-        epi(mt * 16 + fr, nt * 16 + 4 * g, acc);
+      for (int kk = 0; kk < KSM; ++kk) {
+        const u32x4 a = ld16(arow + (kk < klast ? kk : klast) * 32);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = Mma<bf16>::step(f[i][kk], a, acc[i]);
       }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) epi(mt * 16 + fr, (wave + i * NWF) * 16 + 4 * g, acc[i]);
     }
   }
 };
@@ -201,33 +234,6 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   const int win = blockIdx.x % p.n_windows, b = blockIdx.x / p.n_windows;
   const int64_t row0 = (int64_t)b * p.tokens + win;  // global row of token t: row0 + t * n_windows
 
-  // ---- x rows of the window and the LN parameters -> LDS; q|k|v weights
-  const int nch = D / 8;
-  for (int e = tid; e < TW * nch; e += 64 * NWF) {
-    const int t = e / nch, c = e - t * nch;
-    st16(xs + t * XS + c * 8, ld16(p.x + (row0 + (int64_t)t * p.n_windows) * D + c * 8));
-  }
-  for (int e = tid; e < 4 * D; e += 64 * NWF) {
-    const int which = e / D, c = e - which * D;
-    const float* src = which == 0 ? p.ln1_g : which == 1 ? p.ln1_b : which == 2 ? p.ln2_g : p.ln2_b;
-    lnp[which * DP + c] = src[c];
-  }
-  // biases, so that no epilogue waits on a global load
-  for (int e = tid; e < 5 * D + p.mlp; e += 64 * NWF) {
-    if (e < 3 * D) {
-      bqkv[e] = e < D ? p.bq[e] : (e < 2 * D ? p.bk[e - D] : p.bv[e - 2 * D]);
-      if (Q8) sqkv[e] = (float)(e < D ? p.sq[e] : (e < 2 * D ? p.sk[e - D] : p.sv[e - 2 * D]));
-    } else if (e < 4 * D) {
-      bo_s[e - 3 * D] = p.bo[e - 3 * D];
-      if (Q8) so_s[e - 3 * D] = (float)p.so[e - 3 * D];
-    } else if (e < 5 * D) {
-      b2_s[e - 4 * D] = p.b2[e - 4 * D];
-      if (Q8) s2_s[e - 4 * D] = (float)p.s2[e - 4 * D];
-    } else {
-      b1_s[e - 5 * D] = p.b1[e - 5 * D];
-      if (Q8) s1_s[e - 5 * D] = (float)p.s1[e - 5 * D];
-    }
-  }
   // Q8: the accumulator of output column n..n+3 times its row scales
   auto scaled = [&](f32x4 v, const float* sc, int n) {
     if constexpr (Q8) v = v * *reinterpret_cast<const f32x4*>(sc + n);
@@ -238,6 +244,50 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
     if constexpr (Q8) return reinterpret_cast<const int8_t*>(w) + n * K;
     return w + n * K;
   };
+  // ---- x rows of the window, the LN parameters and the biases -> LDS;
+  // q|k|v weights -> registers. Every global read of this phase is issued
+  // before the first LDS store (addresses clamped, values selected), so they
+  // overlap in one round trip, and the weights last, so that the stores
+  // wait only for the small reads ahead of them.
+  constexpr int NT = 64 * NWF;
+  static_assert(TW * (DP / 8) <= NT && 4 * DP <= NT && BIAS_MAX <= 2 * NT, "prologue covers");
+  const int nch = D / 8;
+  const bool x_ok = tid < TW * nch;
+  const int xt = x_ok ? tid / nch : 0, xc = x_ok ? tid - (tid / nch) * nch : 0;
+  const u32x4 xv = ld16(p.x + (row0 + (int64_t)xt * p.n_windows) * D + xc * 8);
+  const bool l_ok = tid < 4 * D;
+  const int lwhich = l_ok ? tid / D : 0, lc = l_ok ? tid - (tid / D) * D : 0;
+  const float* lsrc = lwhich == 0 ? p.ln1_g : lwhich == 1 ? p.ln1_b : lwhich == 2 ? p.ln2_g : p.ln2_b;
+  const float lv = lsrc[lc];
+  // biases (and Q8 row scales) e < 5D + mlp: q|k|v, o, 2, then 1
+  const int nb = 5 * D + p.mlp;
+  float bvv[2], svv[2];
+  int boff[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e0 = tid + r * NT, e = e0 < nb ? e0 : 0;
+    int seg = e < D ? 0 : e < 2 * D ? 1 : e < 3 * D ? 2 : e < 4 * D ? 3 : e < 5 * D ? 4 : 5;
+    const int i = seg < 5 ? e - seg * D : e - 5 * D;
+    const float* bsrc = seg == 0 ? p.bq : seg == 1 ? p.bk : seg == 2 ? p.bv : seg == 3 ? p.bo : seg == 4 ? p.b2 : p.b1;
+    bvv[r] = bsrc[i];
+    if constexpr (Q8) {
+      const _Float16* ssrc = seg == 0 ? p.sq : seg == 1 ? p.sk : seg == 2 ? p.sv : seg == 3 ? p.so : seg == 4 ? p.s2 : p.s1;
+      svv[r] = (float)ssrc[i];
+    }
+    // LDS float offset from bqkv: q|k|v at 0, o at 3DP, 1 at 4DP, 2 at 4DP + 512
+    boff[r] = e0 >= nb ? -1 : seg < 3 ? e : seg == 3 ? 3 * DP + i : seg == 4 ? 4 * DP + 512 + i : 4 * DP + i;
+  }
+  WFrags<(3 * DP / 16 + NWF - 1) / NWF, DP / 32> wqkv;
+  wqkv.load<Q8>([&](int n) { return n < D ? wrow_of(p.wq, n, D) : (n < 2 * D ? wrow_of(p.wk, n - D, D) : wrow_of(p.wv, n - 2 * D, D)); },
+                3 * D, D);
+  if (x_ok) st16(xs + xt * XS + xc * 8, xv);
+  if (l_ok) lnp[lwhich * DP + lc] = lv;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (boff[r] >= 0) {
+      bqkv[boff[r]] = bvv[r];
+      if constexpr (Q8) sqkv[boff[r]] = svv[r];
+    }
   // with at most HPR heads the qkv epilogue writes V transposed straight into
   // vts (one attention round); rows head_dim..63 of each head stay zero
   const bool vt_direct = p.heads <= HPR;
@@ -249,9 +299,6 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
       st16(vts + (hl * 64 + hd + r) * VTS + c * 8, u32x4{0, 0, 0, 0});
     }
   }
-  WFrags<(3 * DP / 16 + NWF - 1) / NWF, DP / 32> wqkv;
-  wqkv.load<Q8>([&](int n) { return n < D ? wrow_of(p.wq, n, D) : (n < 2 * D ? wrow_of(p.wk, n - D, D) : wrow_of(p.wv, n - 2 * D, D)); },
-                3 * D, D);
   lds_barrier();
   // ---- LN1 -> cs
   ln_rows(xs, cs, lnp, lnp + DP, D, p.eps);
