@@ -157,21 +157,22 @@ struct WFrags {
   // all of the wave's weight tiles; each weight fragment serves 4 token
   // tiles. K steps past kreal multiply zero weights by a finite A fragment
   // (the last real step's), so the step loop has no branches.
+  // With bias0 (fp32, LDS), the accumulators start from bias0[n..n+3].
   template <typename Epi>
-  __device__ __forceinline__ void gemm(const bf16* As, int lda, int N, int kreal, Epi epi) const {
+  __device__ __forceinline__ void gemm(const bf16* As, int lda, int N, int kreal, const float* bias0, Epi epi) const {
     const int wave = threadIdx.x >> 6;
     int nv = 0;
 #pragma unroll
     for (int i = 0; i < NTM; ++i) nv += (wave + i * NWF) * 16 < N ? 1 : 0;
-    gemm_nv<NTM>(nv, As, lda, kreal, epi);
+    gemm_nv<NTM>(nv, As, lda, kreal, bias0, epi);
   }
 
  private:
   template <int NV, typename Epi>
-  __device__ __forceinline__ void gemm_nv(int nv, const bf16* As, int lda, int kreal, Epi epi) const {
+  __device__ __forceinline__ void gemm_nv(int nv, const bf16* As, int lda, int kreal, const float* bias0, Epi epi) const {
     if constexpr (NV > 1) {
       if (nv < NV) {
-        gemm_nv<NV - 1>(nv, As, lda, kreal, epi);
+        gemm_nv<NV - 1>(nv, As, lda, kreal, bias0, epi);
         return;
       }
     } else {
@@ -180,11 +181,15 @@ struct WFrags {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 15, g = lane >> 4;
     const int klast = (kreal + 31) / 32 - 1;
+    f32x4 acc0[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      acc0[i] = bias0 ? *reinterpret_cast<const f32x4*>(bias0 + (wave + i * NWF) * 16 + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < TW / 16; ++mt) {
       f32x4 acc[NV];
 #pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NV; ++i) acc[i] = acc0[i];
       const bf16* arow = As + (mt * 16 + fr) * lda + g * 8;
 #pragma unroll
       for (int kk = 0; kk < KSM; ++kk) {
@@ -235,10 +240,12 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   const int64_t row0 = (int64_t)b * p.tokens + win;  // global row of token t: row0 + t * n_windows
 
   // Q8: the accumulator of output column n..n+3 times its row scales
-  auto scaled = [&](f32x4 v, const float* sc, int n) {
-    if constexpr (Q8) v = v * *reinterpret_cast<const f32x4*>(sc + n);
+  // (bf16 weights: the products start from the bias, so v already holds it)
+  auto scaled = [&](f32x4 v, const float* sc, const float* bias, int n) {
+    if constexpr (Q8) v = v * *reinterpret_cast<const f32x4*>(sc + n) + *reinterpret_cast<const f32x4*>(bias + n);
     return v;
   };
+  auto bias0 = [&](const float* bias) -> const float* { return Q8 ? nullptr : bias; };
   // row start of a weight matrix with rows of K values
   auto wrow_of = [&](const bf16* w, int64_t n, int K) -> const void* {
     if constexpr (Q8) return reinterpret_cast<const int8_t*>(w) + n * K;
@@ -306,8 +313,8 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   wo.load<Q8>([&](int n) { return wrow_of(p.wo, n, D); }, D, D);
   lds_barrier();
   // ---- q|k|v = h W^T + b -> qkvs
-  wqkv.gemm(cs, XS, 3 * D, D, [&](int m, int n, f32x4 v) {
-    v = scaled(v, sqkv, n) + *reinterpret_cast<const f32x4*>(bqkv + n);
+  wqkv.gemm(cs, XS, 3 * D, D, bias0(bqkv), [&](int m, int n, f32x4 v) {
+    v = scaled(v, sqkv, bqkv, n);
     if (vt_direct && n >= 2 * D) {  // 4 consecutive d of one head (head_dim % 8 == 0)
       const int vv = n - 2 * D, head = vv / hd, d = vv - head * hd;
 #pragma unroll
@@ -404,9 +411,9 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   }
 
   // ---- x1 = x + ctx W_o^T + b_o -> x1s (cs columns D..DP-1 are still zero)
-  wo.gemm(cs, XS, D, D,
+  wo.gemm(cs, XS, D, D, bias0(bo_s),
       [&](int m, int n, f32x4 v) {
-        v = scaled(v, so_s, n) + *reinterpret_cast<const f32x4*>(bo_s + n) + load4<bf16>(xs + m * XS + n);
+        v = scaled(v, so_s, bo_s, n) + load4<bf16>(xs + m * XS + n);
         store4<bf16>(x1s + m * XS + n, v);
       });
   lds_barrier();
@@ -417,18 +424,18 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   // (after LN2's barrier, so issuing them does not hold up LN2)
   WFrags<1, 16> w2;
   w2.load<Q8>([&](int n) { return wrow_of(p.w2, n, p.mlp); }, D, p.mlp);
-  w1.gemm(cs, XS, p.mlp, D,
+  w1.gemm(cs, XS, p.mlp, D, bias0(b1_s),
       [&](int m, int n, f32x4 v) {
-        v = scaled(v, s1_s, n) + *reinterpret_cast<const f32x4*>(b1_s + n);
+        v = scaled(v, s1_s, b1_s, n);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = TANH ? gelu_tanh_d(v[e]) : gelu_erf_d(v[e]);
         store4<bf16>(uss + m * p.us + n, v);
       });
   lds_barrier();
   // ---- y = x1 + u W_2^T + b_2 -> global
-  w2.gemm(uss, p.us, D, p.mlp,
+  w2.gemm(uss, p.us, D, p.mlp, bias0(b2_s),
       [&](int m, int n, f32x4 v) {
-        v = scaled(v, s2_s, n) + *reinterpret_cast<const f32x4*>(b2_s + n) + load4<bf16>(x1s + m * XS + n);
+        v = scaled(v, s2_s, b2_s, n) + load4<bf16>(x1s + m * XS + n);
         store4<bf16>(p.y + (row0 + (int64_t)m * p.n_windows) * D + n, v);
       });
 }
