@@ -111,8 +111,9 @@ __device__ __forceinline__ float gelu_erf_as(float v) {
   poly = __builtin_fmaf(t, poly, 0.5f * -0.284496736f);
   poly = __builtin_fmaf(t, poly, 0.5f * 0.254829592f);
   const float e = __builtin_amdgcn_exp2f(v * v * (-0.5f * 1.4426950408889634f));  // exp(-z^2)
-  const float r = v * (poly * t) * e;  // v q
-  return v >= 0.f ? v - r : r;
+  // |v| q with q = erfc(|z|)/2 = Phi(-|v|): v - |v| q for v >= 0, -|v| q below,
+  // i.e. max(v, 0) - |v| q in one fma
+  return __builtin_fmaf(-fabsf(v), (poly * t) * e, fmaxf(v, 0.f));
 }
 
 // tanh-approximated GELU, 0.5 v (1 + tanh(u)) with u = sqrt(2/pi)(v + 0.044715 v^3),
@@ -120,8 +121,8 @@ __device__ __forceinline__ float gelu_erf_as(float v) {
 // One exp2 and one reciprocal (hardware, ~1 ulp each); saturates to v and -0
 // for large |u| without overflow trouble (2^+inf -> inf -> reciprocal 0).
 __device__ __forceinline__ float gelu_tanh_fast(float v) {
-  const float u = 0.79788456080286536f * __builtin_fmaf(0.044715f * v, v * v, v);
-  const float e = __builtin_amdgcn_exp2f(u * -2.8853900817779268f);  // 2 log2(e)
+  // -2 u log2(e), the two constants folded into one multiply
+  const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(0.044715f * v, v * v, v) * (0.79788456080286536f * -2.8853900817779268f));
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
