@@ -51,7 +51,7 @@ struct FusedParams {
   const bf16* w2;
   const float* b2;
   int tokens, n_windows, dim, heads, head_dim, mlp, qs, us;  // qs/us: LDS row strides of q|k|v and u
-  float eps, scale_log2;
+  float eps, inv_dim, scale_log2;
   // q8_row weights: the matrices above are int8 payloads (row stride = K
   // bytes) and these their float16 row scales
   const _Float16 *sq, *sk, *sv, *so, *s1, *s2;
@@ -63,7 +63,8 @@ __device__ __forceinline__ float gelu_tanh_d(float v) { return gelu_tanh_fast(v)
 // Row LayerNorm of the window's 64 rows (src -> dst, both LDS, stride XS),
 // 8 lanes per row; columns D..DP-1 of dst are written as zeros so that dst
 // can feed a K=DP product.
-__device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float* g, const float* bta, int D, float eps) {
+__device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float* g, const float* bta, int D, float inv_d,
+                                        float eps) {
   constexpr int LPR = NWF;             // lanes per row: 64 rows over 64*NWF threads
   constexpr int CPL = (DP / 8) / LPR;  // 16-byte chunks per lane
   static_assert(CPL >= 1 && LPR <= 64, "LayerNorm lane split");
@@ -83,7 +84,7 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
   }
   static_assert(LPR == 16, "row reductions are 16-lane DPP");
   s = row16_sum(s);
-  const float mean = s / (float)D;
+  const float mean = s * inv_d;
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i)
@@ -91,7 +92,7 @@ __device__ __forceinline__ void ln_rows(const bf16* src, bf16* dst, const float*
 #pragma unroll
       for (int e = 0; e < 8; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
   q = row16_sum(q);
-  const float inv = 1.0f / sqrtf(q / (float)D + eps);
+  const float inv = __builtin_amdgcn_rsqf(q * inv_d + eps);  // hardware rsq, ~1 ulp
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = l8 + LPR * i;
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
   }
   lds_barrier();
   // ---- LN1 -> cs
-  ln_rows(xs, cs, lnp, lnp + DP, D, p.eps);
+  ln_rows(xs, cs, lnp, lnp + DP, D, p.inv_dim, p.eps);
   WFrags<(DP / 16 + NWF - 1) / NWF, DP / 32> wo;
   wo.load<Q8>([&](int n) { return wrow_of(p.wo, n, D); }, D, D);
   lds_barrier();
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(64 * NWF) void block_mask_unit_kernel(FusedParams p
       });
   lds_barrier();
   // ---- LN2 -> cs
-  ln_rows(x1s, cs, lnp + 2 * DP, lnp + 3 * DP, D, p.eps);
+  ln_rows(x1s, cs, lnp + 2 * DP, lnp + 3 * DP, D, p.inv_dim, p.eps);
   lds_barrier();
   // ---- u = GELU(h2 W_1^T + b_1) -> uss; fc2's weights are requested first
   // (after LN2's barrier, so issuing them does not hold up LN2)
@@ -482,6 +483,7 @@ hipError_t launch_block_mask_unit_fused(const FusedMUArgs& a, hipStream_t s, Sta
   p.qs = 3 * a.dim + 8;
   p.us = a.mlp + 8;
   p.eps = a.eps;
+  p.inv_dim = 1.0f / (float)a.dim;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.sq = (const _Float16*)a.sq;
   p.sk = (const _Float16*)a.sk;

@@ -32,12 +32,14 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Row LayerNorm (SAM3 layer_norm_rows): mean, biased variance over the row,
 // (x - mean) / sqrt(var + eps) * gamma + beta. Statistics in float32, two
-// passes over the values held in registers.
+// passes over the values held in registers; gamma and beta are read with x,
+// so their latency hides behind the reductions (inv_dim = 1 / dim, and the
+// hardware reciprocal square root, ~1 ulp, instead of divisions).
 template <typename T, int G, int V>
 __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x, T* __restrict__ y,
                                                         const float* __restrict__ gamma,
                                                         const float* __restrict__ beta,
-                                                        int64_t rows, int dim, float eps) {
+                                                        int64_t rows, int dim, float inv_dim, float eps) {
   constexpr int VN = Vec<T>::N;
   const int lane = threadIdx.x % G;
   const int64_t row = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
@@ -45,6 +47,23 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
   const int nvec = dim / VN;
   const T* xr = x + row * dim;
   float v[V][VN];
+  // (rows of more than 2 vectors per lane read gamma and beta at use: held
+  // early they would cost 2 VN registers per vector and, on the wide rows of
+  // the bandwidth-bound launches, occupancy)
+  constexpr bool GB_EARLY = V <= 2;
+  constexpr int VG = GB_EARLY ? V : 1;
+  f32x4 g4[VG][VN / 4], b4[VG][VN / 4];
+#pragma unroll
+  for (int i = 0; i < VG; ++i) {
+    const int vi = lane + i * G;
+    if (GB_EARLY && vi < nvec) {
+#pragma unroll
+      for (int e = 0; e < VN; e += 4) {
+        g4[i][e / 4] = *reinterpret_cast<const f32x4*>(gamma + vi * VN + e);
+        b4[i][e / 4] = *reinterpret_cast<const f32x4*>(beta + vi * VN + e);
+      }
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -59,7 +78,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
     }
   }
   s = group_sum<G>(s);
-  const float mean = s / (float)dim;
+  const float mean = s * inv_dim;
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -72,7 +91,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
     }
   }
   q = group_sum<G>(q);
-  const float inv = 1.0f / sqrtf(q / (float)dim + eps);
+  const float inv = __builtin_amdgcn_rsqf(q * inv_dim + eps);
   T* yr = y + row * dim;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -81,10 +100,16 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
       float o[VN];
 #pragma unroll
       for (int e = 0; e < VN; e += 4) {
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(gamma + vi * VN + e);
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(beta + vi * VN + e);
+        f32x4 gg, bb;
+        if constexpr (GB_EARLY) {
+          gg = g4[i][e / 4];
+          bb = b4[i][e / 4];
+        } else {
+          gg = *reinterpret_cast<const f32x4*>(gamma + vi * VN + e);
+          bb = *reinterpret_cast<const f32x4*>(beta + vi * VN + e);
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[e + j] = (v[i][e + j] - mean) * inv * g4[j] + b4[j];
+        for (int j = 0; j < 4; ++j) o[e + j] = (v[i][e + j] - mean) * inv * gg[j] + bb[j];
       }
       st16(yr + vi * VN, pack16<T>(o));
     }
@@ -97,7 +122,7 @@ static hipError_t ln_launch(const void* x, void* y, const float* g, const float*
   const int rpb = 256 / G;
   const int64_t blocks = (rows + rpb - 1) / rpb;
   hipExtLaunchKernelGGL((layernorm_kernel<T, G, V>), dim3((unsigned)blocks), dim3(256), 0, s, ev.start,
-                        ev.stop, 0, (const T*)x, (T*)y, g, b, rows, dim, eps);
+                        ev.stop, 0, (const T*)x, (T*)y, g, b, rows, dim, 1.0f / (float)dim, eps);
   return hipGetLastError();
 }
 
