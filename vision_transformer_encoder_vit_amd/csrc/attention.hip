@@ -628,26 +628,46 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
 // Key-split partials -> ctx: for each (row, head), weights 2^((m_s - m) c)
 // with m the largest split max; ctx = sum_s w_s O_s / sum_s w_s l_s.
 // One thread per 4 consecutive d of one (row, head).
+constexpr int SPLITS_MAX = 8;  // attention_splits() never returns more
+template <int S>
 __global__ __launch_bounds__(256) void attention_combine_kernel(const float* __restrict__ part_o,
                                                                 const float* __restrict__ part_ml, bf16* ctx,
                                                                 int64_t ld_ctx, int64_t rows, int heads, int hd,
-                                                                int dim, int splits, float c) {
+                                                                int dim, float c) {
   const int q4 = hd / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = idx / (heads * q4);
   if (r >= rows) return;
   const int rem = (int)(idx - r * heads * q4), head = rem / q4, d = (rem - head * q4) * 4;
-  float m = -1e30f;
-  for (int sp = 0; sp < splits; ++sp) m = fmaxf(m, part_ml[((sp * rows + r) * heads + head) * 2]);
+  // every split's (m, l) and O are requested before the first is used: one
+  // memory round trip instead of two per split
+  f32x2 ml[S];
+  f32x4 po[S];
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    ml[sp] = *reinterpret_cast<const f32x2*>(part_ml + ((sp * rows + r) * heads + head) * 2);
+    po[sp] = *reinterpret_cast<const f32x4*>(part_o + (sp * rows + r) * dim + head * hd + d);
+  }
+  float m = ml[0][0];
+#pragma unroll
+  for (int sp = 1; sp < S; ++sp) m = fmaxf(m, ml[sp][0]);
   float l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < splits; ++sp) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(part_ml + ((sp * rows + r) * heads + head) * 2);
-    const float w = __builtin_amdgcn_exp2f((ml[0] - m) * c);
-    l += w * ml[1];
-    o += w * *reinterpret_cast<const f32x4*>(part_o + (sp * rows + r) * dim + head * hd + d);
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = __builtin_amdgcn_exp2f((ml[sp][0] - m) * c);
+    l += w * ml[sp][1];
+    o += w * po[sp];
   }
   store4<bf16>(ctx + r * ld_ctx + head * hd + d, o * (1.0f / l));
+}
+
+template <int S>
+static void combine_go(const AttnParams<bf16>& p, hipStream_t s, hipEvent_t stop) {
+  const int64_t threads = p.batch_rows * p.heads * (p.head_dim / 4);
+  hipExtLaunchKernelGGL(attention_combine_kernel<S>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                        nullptr, stop, 0, (const float*)p.part_o, (const float*)p.part_ml, p.ctx, p.ld_ctx,
+                        p.batch_rows, p.heads, p.head_dim, p.dim, p.scale_log2);
 }
 
 template <int NW, int QB, int MODE, bool POOL>
@@ -659,11 +679,16 @@ static hipError_t attn32_go(AttnParams<bf16> p, int batch, hipStream_t s, StageE
   const hipEvent_t stop = p.splits > 1 ? nullptr : ev.stop;
   hipExtLaunchKernelGGL((attention_mfma32_kernel<NW, QB, MODE, POOL>), dim3((unsigned)(blocks * p.splits)),
                         dim3(64 * NW), 0, s, ev.start, stop, 0, p);
-  if (p.splits > 1) {
-    const int64_t threads = p.batch_rows * p.heads * (p.head_dim / 4);
-    hipExtLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                          nullptr, ev.stop, 0, (const float*)p.part_o, (const float*)p.part_ml, p.ctx, p.ld_ctx,
-                          p.batch_rows, p.heads, p.head_dim, p.dim, p.splits, p.scale_log2);
+  switch (p.splits) {
+    case 1: break;
+    case 2: combine_go<2>(p, s, ev.stop); break;
+    case 3: combine_go<3>(p, s, ev.stop); break;
+    case 4: combine_go<4>(p, s, ev.stop); break;
+    case 5: combine_go<5>(p, s, ev.stop); break;
+    case 6: combine_go<6>(p, s, ev.stop); break;
+    case 7: combine_go<7>(p, s, ev.stop); break;
+    case 8: combine_go<8>(p, s, ev.stop); break;
+    default: return hipErrorInvalidValue;  // more than SPLITS_MAX
   }
   return hipGetLastError();
 }
