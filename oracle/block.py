@@ -28,8 +28,11 @@ against Phi(u)*u from math.erf; softmax rows summing to 1 and shift
 invariance; attention against a pure-Python double loop (``brute``) on all of
 the tiny configuration, against torch's scaled_dot_product_attention, and the
 identical-keys / single-key special cases; RoPE norm preservation, identity
-at position 0, relative-position property; pool groups and window maps
-against the spatial definitions. The whole-block output is parity unpinned
+at position 0, relative-position property; the block's RoPE step against a
+pure-Python block that turns only the q and k parts (spatial and global), v
+equal to the plain projection, and a position-independent rotation dropping
+out of attention exactly; pool groups and window maps against the spatial
+definitions. The whole-block output is parity unpinned
 beyond these: no page prints a block output for a known input.
 """
 import numpy as np
@@ -103,6 +106,17 @@ def apply_rope(t, table, rows, head_dim):
             b = t[:, h0 + 2 * j + 1]
             out[:, h0 + 2 * j] = a * c - b * s
             out[:, h0 + 2 * j + 1] = b * c + a * s
+    return out
+
+
+def rope_qk(qkv, table, rows, dim, head_dim):
+    """The block's RoPE step (SAM3 ``apply_rope``, called on the fused qkv
+    rows of the trunk's attention): the q part (columns 0..dim-1) and the k
+    part (dim..2*dim-1) are each rotated per head; the v part is left as it
+    is. Returns a new array."""
+    out = qkv.copy()
+    out[:, :dim] = apply_rope(qkv[:, :dim], table, rows, head_dim)
+    out[:, dim:2 * dim] = apply_rope(qkv[:, dim:2 * dim], table, rows, head_dim)
     return out
 
 
@@ -181,10 +195,7 @@ def block_forward(x, w, spec):
         else:
             qkv = linear(h, w["qkv_w"], f64(w["qkv_b"]))
         if spec.get("rope"):
-            rows = rope_rows_for(spec)
-            tab = f64(w["rope"])
-            qkv = qkv.copy()
-            qkv[:, :2 * D] = apply_rope(qkv[:, :2 * D], tab, rows, hd)
+            qkv = rope_qk(qkv, f64(w["rope"]), rope_rows_for(spec), D, hd)
         q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
         if spec["q_stride"] == 4:
             q = pool4(q)
@@ -239,7 +250,7 @@ def block_forward_rows(x, w, spec, rows):
         else:
             qkv = linear(h, w["qkv_w"], f64(w["qkv_b"]))
         if spec.get("rope"):
-            qkv[:, :2 * D] = apply_rope(qkv[:, :2 * D], f64(w["rope"]), rope_rows_for(spec), hd)
+            qkv = rope_qk(qkv, f64(w["rope"]), rope_rows_for(spec), D, hd)
         q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
         if spec["q_stride"] == 4:
             q = pool4(q)

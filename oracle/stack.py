@@ -22,7 +22,10 @@ Pins (tests/test_oracle.py): the 512x512 shape contract of the plan
 ("Sub-phase 4d": 128x128x112, 64x64x224, 32x32x448, 16x16x896); a stack of
 global blocks without pooling equals the same blocks on raster-order tokens
 (global attention does not see the token order, so unroll and reroll must
-cancel exactly); a one-block stack equals unroll -> block -> reroll.
+cancel exactly); a one-block stack equals unroll -> block -> reroll;
+``tower_forward``'s post_layernorm against the pure-Python LayerNorm of the
+last block's output and its gamma 1 / beta 0 closed form, and its ln_pre
+against the pure-Python LayerNorm feeding the first block.
 """
 import numpy as np
 

@@ -344,6 +344,66 @@ def test_block_rope_windowed_locality():
     assert len(changed) == 16 and ys.max() < 4 and xs.max() < 4
 
 
+def _random_angle_table(rows, pairs, seed):
+    a = np.random.default_rng(seed).uniform(-np.pi, np.pi, (rows, pairs))
+    return np.stack([np.cos(a), np.sin(a)], axis=-1)
+
+
+def _sam3_tiny(mode):
+    kw = dict(grid_h=4, grid_w=6, dim_in=16, dim_out=16, heads=2, mlp=32, dtype="f32")
+    if mode == "spatial":
+        spec = synth.derive(synth.CONFIGS["c5w_sam3_win"], win_h=2, win_w=3, **kw)
+        rows = 6
+    else:
+        spec = synth.derive(synth.CONFIGS["c5g_sam3_global"], **kw)
+        rows = 24
+    inp = synth.make_inputs(spec, seed=12)
+    inp["rope"] = _random_angle_table(rows, 4, 13)
+    return spec, inp
+
+
+@pytest.mark.parametrize("mode", ["spatial", "global"])
+def test_block_rope_vs_brute(mode):
+    # the SAM3 block with RoPE against the pure-Python loop (SAM3 apply_rope:
+    # the q part and the k part of each head turn pair by pair, v does not),
+    # with a table of random angles so every pair turns
+    spec, inp = _sam3_tiny(mode)
+    s = ob.block_forward(inp["x"], inp, spec)
+    wh, ww = (spec["win_h"], spec["win_w"]) if mode == "spatial" else (0, 0)
+    qkv, ctx, y = brute.block_forward_rope(np.asarray(inp["x"][0], np.float64).tolist(), _as_lists(inp),
+                                           4, 6, wh, ww, spec["heads"], spec["eps"], inp["rope"].tolist())
+    np.testing.assert_allclose(s["qkv"][0], qkv, atol=1e-12)
+    np.testing.assert_allclose(s["ctx"][0], ctx, atol=1e-12)
+    np.testing.assert_allclose(s["y"][0], y, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["spatial", "global"])
+def test_block_rope_leaves_v_and_cancels_under_a_common_rotation(mode):
+    # v is the plain projection of h; q and k keep their pair lengths; and a
+    # rotation that is the same at every position (a table whose rows are all
+    # equal) must drop out of attention, because R q . R k = q . k for an
+    # orthogonal R applied to both -- so ctx and y equal the block without
+    # RoPE. Rotating v as well, or only one of q and k, breaks that.
+    spec, inp = _sam3_tiny(mode)
+    D = spec["dim_out"]
+    s = ob.block_forward(inp["x"], inp, spec)
+    h = brute.layer_norm(np.asarray(inp["x"][0], np.float64).tolist(), inp["ln1_g"].tolist(),
+                         inp["ln1_b"].tolist(), spec["eps"])
+    plain = np.array(brute.linear(h, inp["qkv_w"].tolist(), inp["qkv_b"].tolist()))
+    np.testing.assert_allclose(s["qkv"][0][:, 2 * D:], plain[:, 2 * D:], atol=1e-12)
+    for part in (slice(0, D), slice(D, 2 * D)):
+        got, ref = s["qkv"][0][:, part], plain[:, part]
+        np.testing.assert_allclose(got[:, 0::2] ** 2 + got[:, 1::2] ** 2,
+                                   ref[:, 0::2] ** 2 + ref[:, 1::2] ** 2, rtol=1e-10)
+        assert np.abs(got - ref).max() > 1e-3  # the part did turn
+    common = dict(inp)
+    common["rope"] = np.repeat(_random_angle_table(1, 4, 14), inp["rope"].shape[0], axis=0)
+    with_rope = ob.block_forward(inp["x"], common, spec)
+    no_rope = ob.block_forward(inp["x"], inp, dict(spec, rope=False))
+    for k in ("ctx", "y"):
+        np.testing.assert_allclose(with_rope[k], no_rope[k], atol=1e-12, err_msg=k)
+
+
 def test_block_rows_equals_full_block():
     # the sampled-row evaluation used at full sizes is the same computation
     for name, kw in (("c3a_hiera_trans", dict(grid_h=8, grid_w=8, dim_in=8, dim_out=16, heads=2,
@@ -461,6 +521,47 @@ def test_sam3_trunk_windows_stay_local_until_a_global_layer():
     z0 = ost.tower_forward(x, blocks_g, specs_g, pre_ln=(g, b))
     z1 = ost.tower_forward(x2, blocks_g, specs_g, pre_ln=(g, b))
     assert np.all(np.abs(z1[0] - z0[0]).max(axis=-1) > 0)
+
+
+def _tiny_tower(seed):
+    specs = synth.siglip_tower(batch=2, grid=3, layers=2, dim=16, heads=2, mlp=32)
+    specs = [synth.derive(s, dtype="f32") for s in specs]
+    x, blocks = synth.make_stack_inputs(specs, seed=seed)
+    g, b = synth.make_layernorm_params(16, seed)
+    return specs, x, blocks, g, b
+
+
+def test_tower_post_layernorm_follows_the_last_block():
+    # SigLIP forward_frame: the blocks, then post_layernorm on their output.
+    # Pinned against the pure-Python LayerNorm of the blocks' output, and by
+    # the closed form: with gamma 1, beta 0 every output row has mean 0 and
+    # variance var / (var + eps) of the last block's row.
+    from oracle import stack as ost
+    specs, x, blocks, g, b = _tiny_tower(21)
+    out = ost.tower_forward(x, blocks, specs, post_ln=(g, b))
+    t = x.astype(np.float64)
+    for w, sp in zip(blocks, specs):
+        t = ob.block_forward(t, w, sp)["y"]
+    for f in range(2):
+        np.testing.assert_allclose(out[f], brute.layer_norm(t[f].tolist(), g.tolist(), b.tolist(), 1e-6),
+                                   atol=1e-12)
+    unit = ost.tower_forward(x, blocks, specs, post_ln=(np.ones(16), np.zeros(16)))
+    var = t.var(axis=-1)
+    np.testing.assert_allclose(unit.mean(axis=-1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(unit.var(axis=-1), var / (var + 1e-6), rtol=1e-10)
+
+
+def test_tower_pre_layernorm_precedes_the_first_block():
+    # SAM3 trunk: ln_pre on the embedded tokens, then the blocks. The first
+    # block must see the pure-Python LayerNorm of x.
+    from oracle import stack as ost
+    specs, x, blocks, g, b = _tiny_tower(22)
+    out = ost.tower_forward(x, blocks, specs, pre_ln=(g, b))
+    t = np.array([brute.layer_norm(x[f].astype(np.float64).tolist(), g.tolist(), b.tolist(), 1e-6)
+                  for f in range(2)])
+    for w, sp in zip(blocks, specs):
+        t = ob.block_forward(t, w, sp)["y"]
+    np.testing.assert_allclose(out, t, atol=1e-12)
 
 
 # ---------------------------------------------------------------- patch-embedding stems

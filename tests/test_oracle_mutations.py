@@ -196,6 +196,73 @@ MUTATIONS += [
 ]
 
 
+def _rope_qkv_all(qkv, table, rows, dim, hd):
+    # rotates v as well
+    out = qkv.copy()
+    for p in range(3):
+        out[:, p * dim:(p + 1) * dim] = ob.apply_rope(qkv[:, p * dim:(p + 1) * dim], table, rows, hd)
+    return out
+
+
+def _rope_q_only(qkv, table, rows, dim, hd):
+    out = qkv.copy()
+    out[:, :dim] = ob.apply_rope(qkv[:, :dim], table, rows, hd)
+    return out
+
+
+def _rope_k_only(qkv, table, rows, dim, hd):
+    out = qkv.copy()
+    out[:, dim:2 * dim] = ob.apply_rope(qkv[:, dim:2 * dim], table, rows, hd)
+    return out
+
+
+def _rope_rows_transposed_in_windows(spec):
+    # in-window row taken column-major (x * win_h + y) instead of raster
+    n = np.arange(spec["grid_h"] * spec["grid_w"])
+    y, x = n // spec["grid_w"], n % spec["grid_w"]
+    if spec["mode"] == "spatial":
+        return (x % spec["win_w"]) * spec["win_h"] + (y % spec["win_h"])
+    return n
+
+
+_orig_tower = ost.tower_forward
+
+
+def _tower_post_ln_skipped(x, blocks, specs, pre_ln=None, post_ln=None, eps=1e-6):
+    return _orig_tower(x, blocks, specs, pre_ln=pre_ln, post_ln=None, eps=eps)
+
+
+def _tower_post_ln_before_last_block(x, blocks, specs, pre_ln=None, post_ln=None, eps=1e-6):
+    t = _orig_tower(x, blocks[:-1], specs[:-1], pre_ln=pre_ln, post_ln=post_ln, eps=eps)
+    return ob.block_forward(t, blocks[-1], specs[-1])["y"]
+
+
+def _tower_pre_ln_skipped(x, blocks, specs, pre_ln=None, post_ln=None, eps=1e-6):
+    return _orig_tower(x, blocks, specs, pre_ln=None, post_ln=post_ln, eps=eps)
+
+
+MUTATIONS += [
+    ("rope on v too (spatial)", ob, "rope_qk", _rope_qkv_all,
+     lambda: pins.test_block_rope_vs_brute("spatial")),
+    ("rope on v too (global)", ob, "rope_qk", _rope_qkv_all,
+     lambda: pins.test_block_rope_leaves_v_and_cancels_under_a_common_rotation("global")),
+    ("rope on q only (brute)", ob, "rope_qk", _rope_q_only,
+     lambda: pins.test_block_rope_vs_brute("global")),
+    ("rope on q only (common rotation)", ob, "rope_qk", _rope_q_only,
+     lambda: pins.test_block_rope_leaves_v_and_cancels_under_a_common_rotation("spatial")),
+    ("rope on k only", ob, "rope_qk", _rope_k_only,
+     lambda: pins.test_block_rope_leaves_v_and_cancels_under_a_common_rotation("global")),
+    ("rope rows column-major inside windows", ob, "rope_rows_for", _rope_rows_transposed_in_windows,
+     lambda: pins.test_block_rope_vs_brute("spatial")),
+    ("tower post_ln skipped", ost, "tower_forward", _tower_post_ln_skipped,
+     pins.test_tower_post_layernorm_follows_the_last_block),
+    ("tower post_ln before the last block", ost, "tower_forward", _tower_post_ln_before_last_block,
+     pins.test_tower_post_layernorm_follows_the_last_block),
+    ("tower pre_ln skipped", ost, "tower_forward", _tower_pre_ln_skipped,
+     pins.test_tower_pre_layernorm_precedes_the_first_block),
+]
+
+
 @pytest.mark.parametrize("label,mod,attr,bad,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(monkeypatch, label, mod, attr, bad, pin):
     monkeypatch.setattr(mod, attr, bad)
