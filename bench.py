@@ -27,7 +27,7 @@ METRIC = "encoder-block tokens/sec + attention/GEMM TFLOP/s as % of bf16 MFMA pe
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
-DEFAULT_CONFIG = "c2_hiera_s0"
+DEFAULT_CONFIG = "c5g_sam3_global"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "vision_transformer_encoder_vit_amd", "csrc")
 STAGE_SOURCE = {"ln1": "rowops.hip", "ln2": "rowops.hip", "qkv": "gemm.hip", "residual": "gemm.hip",
@@ -109,27 +109,44 @@ def measured_traffic(config, stage):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(spec, budget_s=10.0):
-    """The float64 CPU oracle on frame 0 of the workload, repeated until about
-    budget_s of CPU time; returns tokens/s and the BLAS threads it used."""
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo) and the number
+    of cores this process may run on."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return name, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(spec, budget_s=20.0, max_runs=3):
+    """The float64 CPU oracle on frame 0 of the workload: whole block forwards
+    until max_runs are done or budget_s has passed (at least one); the median
+    run gives tokens/s. Reports the BLAS threads it used and the CPU model."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import block as ob
     from vision_transformer_encoder_vit_amd import synth
     one = synth.derive(spec, batch=1)
     inp = synth.make_inputs(one, seed=0)
-    reps, t0 = 0, time.perf_counter()
-    while True:
+    runs = []
+    while len(runs) < max_runs and sum(runs) < budget_s:
+        t0 = time.perf_counter()
         ob.block_forward(inp["x"], inp, one)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / reps
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     n = one["grid_h"] * one["grid_w"]
+    model, ncpu = cpu_model()
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "float64 numpy oracle, one full block forward of frame 0 (%d tokens), %d rep(s), %.2f s each"
-                      % (n, reps, dt)}
+            "cpu_model": model, "cpus_available": ncpu,
+            "sample": "float64 numpy oracle, one full block forward of frame 0 (%d tokens); median of %d run(s): "
+                      "%s s" % (n, len(runs), ", ".join("%.2f" % r for r in runs))}
 
 
 def run(spec, steps, warmup, with_cpu):

@@ -307,3 +307,26 @@ def test_q8_forward_needs_every_scale():
     assert pb.stage_mask() == p8.stage_mask() == 1 << vb.STAGES.index("fused")
     p8.close()
     pb.close()
+
+
+def test_library_binds_torchs_hip_runtime():
+    # the binding loads torch first, so the library resolves torch's runtime
+    ours = vb._runtime_file(vb.lib)
+    assert ours is not None and ours == vb._runtime_file(ctypes.CDLL(vb._torch_runtime_path()))
+
+
+def test_second_hip_runtime_fails_loudly():
+    # a process that mapped another libamdhip64 before torch (the system one
+    # from /opt/rocm) would run the library in a context without torch's
+    # memory and streams; the import must refuse instead of crashing later
+    import subprocess
+    import sys
+    import glob
+    other = sorted(glob.glob("/opt/rocm*/lib/libamdhip64.so.*"))
+    if not other:
+        pytest.skip("no system HIP runtime to map")
+    code = ("import ctypes; ctypes.CDLL(%r); import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import vision_transformer_encoder_vit_amd.binding\nexcept ImportError as e:\n"
+            "    print('REFUSED', e); raise SystemExit(0)\nraise SystemExit(3)\n") % (other[0], ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "REFUSED" in r.stdout and "HIP runtime" in r.stdout, r.stdout + r.stderr

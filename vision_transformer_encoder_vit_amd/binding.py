@@ -63,6 +63,38 @@ class VitError(RuntimeError):
         self.status = status
 
 
+def hip_runtimes_mapped():
+    """Distinct HIP runtime libraries (libamdhip64*) mapped into this
+    process, as real paths. Two of them means two HIP contexts: device memory
+    and streams of one are invalid in the other."""
+    found = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and os.path.basename(parts[5]).startswith("libamdhip64"):
+                found.add(os.path.realpath(parts[5]))
+    return sorted(found)
+
+
+def _torch_runtime_path():
+    import torch
+    p = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    return p if os.path.exists(p) else "libamdhip64.so.7"
+
+
+def _runtime_file(handle):
+    """Real path of the file that holds the hipGetDevice this library handle
+    resolves (dlsym searches the handle's own dependency scope)."""
+    addr = ctypes.cast(handle.hipGetDevice, ctypes.c_void_p).value
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            lo, hi = (int(v, 16) for v in parts[0].split("-"))
+            if lo <= addr < hi and len(parts) >= 6:
+                return os.path.realpath(parts[5])
+    return None
+
+
 def _load():
     # torch ships its own HIP runtime under the same soname as the system's
     # (libamdhip64.so.7). Importing torch first makes this library bind to
@@ -73,6 +105,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libvitblock.so is not built (run vision_transformer_encoder_vit_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
+    ours, torchs = _runtime_file(lib), _runtime_file(ctypes.CDLL(_torch_runtime_path()))
+    if ours is None or ours != torchs:
+        raise ImportError("libvitblock.so must share torch's HIP runtime, but it resolved %s while torch uses %s "
+                          "(mapped: %s); load torch before anything that links libamdhip64 (this library "
+                          "included)" % (ours, torchs, ", ".join(hip_runtimes_mapped())))
     P = ctypes.POINTER
     sig = {
         "vit_block_create": [P(vit_block_desc), P(_vp)],
