@@ -147,6 +147,23 @@ def test_peaked_softmax_bf16():
     gu.check("peaked:y", gu.to64(y), ref["y"], spec)
 
 
+@pytest.mark.parametrize("name", ["c5w_48x48", "c5g_18x22", "c5g_10x20_split"])
+def test_attention_range_fallback(name, monkeypatch):
+    # the head_dim-64 attention takes exp2 of the scaled scores without a
+    # running maximum and re-runs a window with the maximum subtracted when a
+    # row sum leaves its band; a band of width 0 sends every window through
+    # that second pass, which must match the oracle on its own
+    monkeypatch.setenv("VIT_ATTN_RANGE_LOG2", "0")
+    spec = SMALL[name]
+    print("case", name, flush=True)
+    inp = synth.make_inputs(spec, seed=4)
+    ref = ob.block_forward(inp["x"], inp, spec)
+    y, seams = gu.run_block(spec, gu.to_device(inp, spec))
+    for k in ("ctx", "attn_branch", "x1", "y"):
+        got = y if k == "y" else seams[k]
+        gu.check(name + " (max pass):" + k, gu.to64(got), ref[k], spec)
+
+
 def test_rerun_is_bitwise_identical():
     spec = C["c5w_sam3_win"]
     dev = gu.to_device(synth.make_inputs(spec, seed=0), spec)

@@ -25,6 +25,9 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
 #include <type_traits>
 
 namespace vit {
@@ -38,6 +41,7 @@ constexpr int KT = 64;   // keys per tile
 #endif
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int HDP = 64;  // padded head dim
 
 template <typename T>
@@ -693,6 +697,279 @@ static hipError_t attn32_go(AttnParams<bf16> p, int batch, hipStream_t s, StageE
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Large windows, head_dim 64, on head-major operands (written in window
+// order by the qkv projection): q [B, windows, heads, n, 64] already
+// multiplied by scale * log2 e, k likewise, V^T [B, windows, heads, 64, n].
+// One workgroup = NW waves of 32 queries of one (frame, window, head); a
+// wave computes S^T = K Q^T (keys on the MFMA rows, so a lane holds 16 keys
+// of ONE query) and O^T += V^T P^T, K and V^T tiles of 64 keys streamed
+// into LDS by buffer loads (the tile offset is a scalar: no per-lane
+// address arithmetic).
+//
+// Softmax without a running maximum: q arrives multiplied by scale * log2 e,
+// so the MFMA returns c*s and P = exp2(c*s) directly -- one exponential per
+// score, no per-tile maximum, no rescaling of O. Subtracting the row maximum
+// (the stable form) changes every P and the row sum l by the same factor,
+// which cancels in O / l; it only serves to keep exp2 in range. So the pass
+// checks the range instead: if some row ends with l outside [2^-64, 2^64]
+// (some c*s above 64, or every c*s of the row far below zero, or an
+// overflow), the workgroup runs the window again with the running maximum
+// subtracted (the classic online softmax). Within the range every P is at
+// most 2^64 and the largest P of a row at least 2^-64 / n, so nothing
+// overflows and the terms that matter stay normal floats. The row sums come
+// from the bf16 P that multiply V (dot products with (1, 1) over packed
+// pairs).
+// ---------------------------------------------------------------------------
+struct AttnHmParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* vt;
+  bf16* ctx;
+  int64_t ld_ctx;
+  int n;                 // tokens per window (queries = keys)
+  int groups, heads;     // groups = B * windows * heads
+  int windows;           // per frame
+  int spatial, grid_w, win_h, win_w, tokens_per_frame;
+  float l_lo, l_hi;      // the band a row sum must fall in (2^-64, 2^64)
+};
+
+constexpr uint32_t BUF_WORD3 = 0x00020000;  // raw buffer, 32-bit data, range-checked
+
+// (the operands are wave-uniform; readfirstlane lets the compiler keep the
+// descriptor in SGPRs instead of looping over lanes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ptr = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ptr, (short)0, __builtin_amdgcn_readfirstlane(bytes), BUF_WORD3);
+}
+
+// 16 bytes per lane from a buffer into LDS (lane l's at lds + 16 l bytes)
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (attn_lds_ptr)lds, 16, voff, 0, 0, 0);
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p) {
+  static_assert(KT == 64 && (KT / 8) % NW == 0, "64-key tiles split over the waves");
+  constexpr int LPW = KT / 8 / NW;  // 1 KB buffer loads per wave per tile, for K and for V^T each
+  // one array per stage: the compiler can then tell that a tile's buffer
+  // loads into one stage never alias the LDS reads of the other (with one
+  // array it waits for the prefetch before every read)
+  __shared__ __attribute__((aligned(1024))) bf16 Ks0[KT * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs0[64 * KT];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks1[KT * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs1[64 * KT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 31, h = lane >> 5;
+  // consecutive workgroups share (frame, window, head): with groups a
+  // multiple of 8 all query tiles of a group land on one XCD (its L2)
+  const int g = blockIdx.x % p.groups, qt = blockIdx.x / p.groups;
+  const int n = p.n;
+  const int64_t gbase = (int64_t)g * n * 64;
+  const bf16* kg = p.k + gbase;
+  const bf16* vg = p.vt + gbase;
+
+  // Q fragments (B operand): lane holds q[qi][16ks + 8h .. +7]
+  const int qi = (qt * NW + wave) * 32 + fr;
+  const bool qvalid = qi < n;
+  u32x4 qf[4];
+  {
+    const bf16* qr = p.q + gbase + (int64_t)(qvalid ? qi : 0) * 64 + h * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = qvalid ? ld16(qr + ks * 16) : u32x4{0, 0, 0, 0};
+  }
+
+  // per-lane byte offsets of the K and V^T tile loads (fixed over tiles).
+  // K: LDS row R holds key key_of_row(R), its 16-byte chunks XOR-swizzled;
+  // V^T: LDS row R = d, chunk c = keys 8c .. 8c+7 of the tile, swizzled.
+  int koff[LPW], voff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int row = (wave * LPW + j) * 8 + lane / 8;
+    const int ch = (lane & 7) ^ kswz(row);
+    koff[j] = (key_of_row(row) * 64 + ch * 8) * 2;
+    voff[j] = (row * n + ch * 8) * 2;
+  }
+  const int ntiles = (n + KT - 1) / KT;
+  // tile kt's K and V^T into one stage's LDS arrays
+  auto issue = [&](bf16* kd, bf16* vd, int kt) {
+    // bytes from the tile's start to the end of the (frame, window, head)
+    // block: loads past it return zeros
+    const __amdgpu_buffer_rsrc_t kr = buf_rsrc(kg + (int64_t)kt * KT * 64, (n - kt * KT) * 128);
+    const __amdgpu_buffer_rsrc_t vr = buf_rsrc(vg + (int64_t)kt * KT, (n * 64 - kt * KT) * 2);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) buf_load_lds16(kr, kd + (wave * LPW + j) * 512, koff[j]);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) buf_load_lds16(vr, vd + (wave * LPW + j) * 512, voff[j]);
+  };
+
+  f32x16 acc_o[2] = {f32x16{}, f32x16{}};  // O^T[d = 32db + 8(r/4) + 4h + r%4][query]
+  float l = 0.f;                            // this lane's share of the row sum
+  const bf16x2_t ones = {(bf16)1.f, (bf16)1.f};
+  f32x16 sacc[2];
+
+  // S^T (c*s) of the tile in LDS at ks, ragged keys at -1e30
+  auto scores = [&](const bf16* ks, int kt) {
+    // the two key blocks' MFMA chains interleaved
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + fr;
+        const u32x4 kfr = ld16(ks + row * 64 + ((q * 2 + h) ^ kswz(row)) * 8);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfr),
+                                                           __builtin_bit_cast(bf16x8, qf[q]),
+                                                           q == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
+      }
+    const int kv_left = n - kt * KT;
+    if (kv_left < KT) {  // uniform: only the last tile of a ragged window
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key_of_row(kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) >= kv_left) sacc[kb][r] = -1e30f;
+    }
+  };
+  // P = exp2(sacc) in bf16, its row sums, and O^T += V^T P^T for one tile
+  // whose V^T is in LDS at vs
+  auto pv_step = [&](const bf16* vs) {
+    u32x4 pf[2][2];  // [kb][s]: keys 32kb + 16s + 8h + 0..7
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = (bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * s + e]);
+        pf[kb][s] = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2_t pr = {pv[2 * e], pv[2 * e + 1]};
+          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        }
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int row = db * 32 + fr;
+          const u32x4 vf = ld16(vs + row * 64 + ((4 * kb + 2 * s + h) ^ kswz(row)) * 8);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
+                                                             __builtin_bit_cast(bf16x8, pf[kb][s]), acc_o[db], 0, 0, 0);
+        }
+  };
+  // one tile kt in LDS at (ks, vs): wait for its loads, start tile kt + 1's
+  // into the other stage (kn, vn), then S and P V. Every call site passes
+  // the stage arrays themselves, so the compiler sees which LDS each access
+  // touches.
+  auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int kt) {
+    __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kn, vn, kt + 1);
+    scores(ks, kt);
+    pv_step(vs);
+  };
+
+  // the pass: tile kt in stage kt & 1, tiles taken in pairs so that the
+  // stage of each is known at compile time
+  issue(Ks0, Vs0, 0);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(Ks0, Vs0, Ks1, Vs1, kt);
+    if (kt + 1 < ntiles) step(Ks1, Vs1, Ks0, Vs0, kt + 1);
+  }
+  l += __shfl_xor(l, 32, 64);
+
+  if (__syncthreads_or(!(l >= p.l_lo && l <= p.l_hi))) {
+    // out of range somewhere in the workgroup: the window again, with the
+    // running row maximum m subtracted and O, l rescaled as it grows
+    acc_o[0] = f32x16{};
+    acc_o[1] = f32x16{};
+    l = 0.f;
+    float m = -1e30f;
+    issue(Ks0, Vs0, 0);
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int stage = kt & 1;
+      __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
+      __syncthreads();
+      if (kt + 1 < ntiles) {
+        if (stage) issue(Ks0, Vs0, kt + 1);
+        else issue(Ks1, Vs1, kt + 1);
+      }
+      scores(stage ? Ks1 : Ks0, kt);
+      float mt = -1e30f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      const float m_new = fmaxf(m, halves_max(mt));
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) acc_o[db] *= alpha;
+      l *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] -= m;
+      pv_step(stage ? Vs1 : Vs0);
+    }
+    l += __shfl_xor(l, 32, 64);
+  }
+
+  if (!qvalid) return;
+  // output row of query qi: its token in the frame
+  const int bw = g / p.heads, head = g - bw * p.heads;
+  const int b = bw / p.windows, win = bw - b * p.windows;
+  int t = qi;
+  if (p.spatial) {
+    const int nwx = p.grid_w / p.win_w, wy = win / nwx, wx = win - wy * nwx;
+    const int iy = qi / p.win_w, ix = qi - iy * p.win_w;
+    t = (wy * p.win_h + iy) * p.grid_w + wx * p.win_w + ix;
+  }
+  const float inv = 1.0f / l;
+  bf16* out = p.ctx + ((int64_t)b * p.tokens_per_frame + t) * p.ld_ctx + head * 64;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+      store4<bf16>(out + db * 32 + 8 * gq + 4 * h,
+                   f32x4{acc_o[db][4 * gq], acc_o[db][4 * gq + 1], acc_o[db][4 * gq + 2], acc_o[db][4 * gq + 3]} * inv);
+}
+
+
+static hipError_t attn_hm_go(const AttnArgs& a, hipStream_t s, StageEvents ev) {
+  AttnHmParams p;
+  p.q = (const bf16*)a.qh;
+  p.k = (const bf16*)a.kh;
+  p.vt = (const bf16*)a.vt;
+  p.ctx = (bf16*)a.ctx;
+  p.ld_ctx = a.ld_ctx;
+  p.spatial = a.mode == ATTN_SPATIAL;
+  p.n = p.spatial ? a.win_h * a.win_w : a.tokens_in;
+  p.windows = a.tokens_in / p.n;
+  p.heads = a.heads;
+  p.groups = a.batch * p.windows * a.heads;
+  p.grid_w = a.grid_w;
+  p.win_h = a.win_h;
+  p.win_w = a.win_w;
+  p.tokens_per_frame = a.tokens_in;
+  // VIT_ATTN_RANGE_LOG2 (test hook, default 64) narrows the band; 0 sends
+  // every window through the pass with the running maximum
+  int range = 64;
+  if (const char* env = std::getenv("VIT_ATTN_RANGE_LOG2")) range = std::max(0, std::min(64, std::atoi(env)));
+  p.l_lo = std::ldexp(1.0f, -range);
+  p.l_hi = range == 0 ? 0.f : std::ldexp(1.0f, range);
+  constexpr int NW = 4;
+  const int q_tiles = (p.n + 32 * NW - 1) / (32 * NW);
+  const int64_t blocks = (int64_t)p.groups * q_tiles;
+  if (blocks == 0) return hipSuccess;
+  hipExtLaunchKernelGGL(attention_hm_kernel<NW>, dim3((unsigned)blocks), dim3(64 * NW), 0, s, ev.start, ev.stop, 0, p);
+  return hipGetLastError();
+}
+
 template <typename T, int QB, int HPW, bool POOL>
 static hipError_t attn_go(const AttnArgs& a, AttnParams<T> p, hipStream_t s, StageEvents ev) {
   constexpr int rows = (4 / HPW) * 16 * QB;
@@ -736,6 +1013,13 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
     p.n_kv = a.tokens_in;
   }
   const bool pool = a.q_stride == 4;
+  if (a.qh != nullptr) {
+    if (!std::is_same<T, bf16>::value || !a.kh || !a.vt || a.q_stride != 1 || a.head_dim != 64 ||
+        a.dim != 64 * a.heads || a.ld_ctx % 8 ||
+        (a.mode == ATTN_SPATIAL ? (a.win_w % 8 || a.tokens_in % (a.win_h * a.win_w)) : a.mode != ATTN_GLOBAL))
+      return hipErrorInvalidValue;
+    return attn_hm_go(a, s, ev);
+  }
   p.vt = (const T*)a.vt;
   p.splits = 1;
   p.batch_rows = 0;

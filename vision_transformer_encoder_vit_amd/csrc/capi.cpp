@@ -56,11 +56,13 @@ struct vit_block_plan {
   int64_t m_in, m_out;
   size_t esize;
   // workspace layout (byte offsets)
-  size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, off_vt, off_po, off_pml, ws_bytes;
+  size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, off_vt, off_po, off_pml, off_qh, off_kh,
+      ws_bytes;
   int attn_splits;       // key splits of the large-window attention (1: none)
   bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
   bool attn_vt;          // the large-window attention kernel runs on V^T (workspace off_vt)
   bool vt_in_gemm;       // ... written by the qkv projection's epilogue (else a transpose kernel)
+  bool attn_hm;          // ... with q (scaled) and k head-major too (off_qh, off_kh): the head_dim-64 kernel
   bool pool_gemm;        // transition: the residual projection pooled in its GEMM epilogue
   bool residual_in_qkv;  // ... and computed by the qkv GEMM (a fourth weight segment)
   // Q8_ROW: workspace copies of the int8 payloads in act_dtype (exact), read
@@ -168,8 +170,12 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   const vit::DType dtp = d.act_dtype == VIT_DTYPE_BF16 ? vit::DType::BF16 : vit::DType::F32;
   p->pool_gemm = d.q_stride == 4 && vit::gemm_uses_mfma(dtp, d.dim_in, d.dim_in);
   p->residual_in_qkv = p->pool_gemm && d.rope == VIT_ROPE_NONE && !p->vt_in_gemm;
+  p->attn_hm = p->vt_in_gemm && vit::attention_takes_hm(dtp, d.attn_mode, n_q, p->head_dim, d.win_w, p->n_in,
+                                                         d.q_stride);
+  p->off_qh = p->attn_hm ? take(p->m_in, d.dim_out) : 0;
+  p->off_kh = p->attn_hm ? take(p->m_in, d.dim_out) : 0;
   p->attn_splits = 1;
-  if (p->attn_vt) {
+  if (p->attn_vt && !p->attn_hm) {
     const int64_t windows = d.attn_mode == VIT_ATTN_SPATIAL
                                 ? (int64_t)(d.grid_h / d.win_h) * (d.grid_w / d.win_w) : 1;
     const int64_t n_kv = d.attn_mode == VIT_ATTN_SPATIAL ? (int64_t)d.win_h * d.win_w : p->n_in;
@@ -499,13 +505,24 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     g.ld_pool = Do;
     g.pool_col0 = 3 * Do;
   }
+  const float attn_scale = d.attn_scale > 0.f ? d.attn_scale : 1.0f / std::sqrt((float)hd);
   if (P.vt_in_gemm) {
     g.vt = base + P.off_vt;
     g.vt_col0 = 2 * Do;
     g.vt_tokens = P.n_in;
     g.vt_heads = d.heads;
     g.vt_hd = hd;
-    g.vt_only = !seams;  // the qkv seam keeps V in row layout too
+    g.vt_only = !seams;  // the qkv seam keeps q, k and v in row layout too
+  }
+  if (P.attn_hm) {
+    // q (times scale * log2 e) and k head-major in window order as well
+    g.hm_q = base + P.off_qh;
+    g.hm_k = base + P.off_kh;
+    g.hm_qscale = attn_scale * 1.4426950408889634f;
+    g.hm_spatial = d.attn_mode == VIT_ATTN_SPATIAL;
+    g.grid_w = d.grid_w;
+    g.win_h = g.hm_spatial ? d.win_h : 1;
+    g.win_w = g.hm_spatial ? d.win_w : 1;
   }
   if (P.attn_vt && !P.vt_in_gemm) {
     e = vit::launch_gemm(g, dt, s, only_start(stage_ev(VIT_STAGE_QKV)));
@@ -584,6 +601,10 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   a.qkv = qkv;
   a.ld_qkv = 3 * Do;
   a.vt = P.attn_vt ? base + P.off_vt : nullptr;
+  if (P.attn_hm) {
+    a.qh = base + P.off_qh;
+    a.kh = base + P.off_kh;
+  }
   if (P.attn_splits > 1) {
     a.part_o = reinterpret_cast<float*>(base + P.off_po);
     a.part_ml = reinterpret_cast<float*>(base + P.off_pml);
@@ -602,7 +623,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
   a.win_h = d.win_h;
   a.win_w = d.win_w;
   a.q_stride = d.q_stride;
-  a.scale = d.attn_scale > 0.f ? d.attn_scale : 1.0f / std::sqrt((float)hd);
+  a.scale = attn_scale;
   e = vit::launch_attention(a, dt, s, stage_ev(VIT_STAGE_ATTN));
   if ((st = device_status(e, "attention")) != VIT_OK) return st;
 

@@ -41,6 +41,11 @@ struct GemmParams {
   T* vt;  // transposed copy of columns >= vt_col0 (MFMA path only)
   int vt_col0, vt_tokens, vt_heads, vt_hd;
   bool vt_only;
+  // head-major attention operands (GemmArgs::hm_q), MFMA path only
+  T* hm_q;
+  T* hm_k;
+  float hm_qscale;
+  bool hm_spatial;
   const float* pos;  // EPI_BIAS_POS: table [rows, N]
   int pos_mode, pos_side;
   // optional float16 scale per output column (per weight row), applied to
@@ -80,6 +85,17 @@ __device__ __forceinline__ int pos_row(const P& p, int64_t m) {
   if (p.pos_mode == POS_BUCKET) return max(y - 1, 0) * p.pos_side + max(x - 1, 0);
   if (p.pos_mode == POS_TILE) return (y % p.pos_side) * p.pos_side + (x % p.pos_side);
   return t;
+}
+
+// Attention window of token t of a frame and its index inside the window,
+// as a flat offset (window * window_tokens + index): the frame is one window,
+// or (spatial) the win_h x win_w tiles of a grid grid_w wide, row-major, each
+// read row-major.
+__device__ __forceinline__ int window_order(int t, bool spatial, int grid_w, int win_h, int win_w) {
+  if (!spatial) return t;
+  const int y = t / grid_w, x = t - y * grid_w;
+  const int wy = y / win_h, wx = x / win_w;
+  return ((wy * (grid_w / win_w) + wx) * win_h + (y - wy * win_h)) * win_w + (x - wx * win_w);
 }
 
 __device__ __forceinline__ float gelu_erf_f(float v) { return gelu_erf_as(v); }
@@ -576,7 +592,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
         for (int k = 0; k < 8; ++k) v[k] = cs[(rg * 8 + k) * CROW + cc] + bn;
         const int vv = n - p.vt_col0, hh = vv / p.vt_hd, d = vv - hh * p.vt_hd;
         const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
-        st16(p.vt + (((int64_t)fb * p.vt_heads + hh) * p.vt_hd + d) * p.vt_tokens + t, pack16<bf16>(v));
+        if (p.hm_q != nullptr) {
+          // [frame, window, head, d, i]: the 8 rows are consecutive tokens of
+          // one window row (win_w % 8 == 0), so consecutive i
+          const int wn = p.hm_spatial ? p.win_h * p.win_w : p.vt_tokens;
+          const int wi = window_order(t, p.hm_spatial, p.grid_w, p.win_h, p.win_w);
+          const int win = wi / wn, i = wi - win * wn;
+          const int64_t blk = ((int64_t)fb * (p.vt_tokens / wn) + win) * p.vt_heads + hh;
+          st16(p.vt + (blk * p.vt_hd + d) * wn + i, pack16<bf16>(v));
+        } else {
+          st16(p.vt + (((int64_t)fb * p.vt_heads + hh) * p.vt_hd + d) * p.vt_tokens + t, pack16<bf16>(v));
+        }
       }
     }
     if constexpr (POOL) {
@@ -630,6 +656,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
       const int m = m0 + pass * PR + r, n = n0 + c8;
       if (m >= p.M || n >= p.N) continue;
       if (p.vt_only && n >= p.vt_col0) continue;
+      const bool to_hm = (EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) && p.hm_q != nullptr && n < p.vt_col0;
       float v[8];
       *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8);
       *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4);
@@ -685,6 +712,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
         unpack16<bf16>(ld16(p.res + (int64_t)m * p.ldres + n), rv);
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] += rv[t];
+      }
+      if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) {
+        if (to_hm) {
+          // q (scaled) or k, 8 consecutive d of one head, to [frame, window, head, i, 64]
+          const int dq = p.vt_col0 / 2, isk = n >= dq ? 1 : 0, nn = n - isk * dq;
+          const int hh = nn / p.vt_hd, d = nn - hh * p.vt_hd;
+          const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
+          const int wn = p.hm_spatial ? p.win_h * p.win_w : p.vt_tokens;
+          const int wi = window_order(t, p.hm_spatial, p.grid_w, p.win_h, p.win_w);
+          const int win = wi / wn, i = wi - win * wn;
+          const int64_t blk = ((int64_t)fb * (p.vt_tokens / wn) + win) * p.vt_heads + hh;
+          float hv[8];
+          const float sc = isk ? 1.f : p.hm_qscale;
+#pragma unroll
+          for (int t2 = 0; t2 < 8; ++t2) hv[t2] = v[t2] * sc;
+          st16((isk ? p.hm_k : p.hm_q) + (blk * wn + i) * p.vt_hd + d, pack16<bf16>(hv));
+          if (p.vt_only) continue;
+        }
       }
       st16(p.C + (int64_t)m * p.ldc + n, pack16<bf16>(v));
     }
@@ -751,6 +796,10 @@ static GemmParams<T> make_params(const GemmArgs& a) {
   p.vt_heads = a.vt_heads;
   p.vt_hd = a.vt_hd;
   p.vt_only = a.vt != nullptr && a.vt_only;
+  p.hm_q = (T*)a.hm_q;
+  p.hm_k = (T*)a.hm_k;
+  p.hm_qscale = a.hm_qscale;
+  p.hm_spatial = a.hm_spatial;
   p.ws0 = (const _Float16*)a.wscale[0];
   p.ws1 = (const _Float16*)(a.wscale[1] ? a.wscale[1] : a.wscale[0]);
   p.ws2 = (const _Float16*)(a.wscale[2] ? a.wscale[2] : a.wscale[0]);
@@ -782,6 +831,9 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
   const bool mfma32 = gemm_uses_mfma(dt, a.K, a.lda);
   if (a.vt && (!mfma32 || (a.epi != EPI_BIAS && a.epi != EPI_BIAS_ROPE) || a.M % 8 || a.vt_tokens <= 0 ||
                a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 || (a.N - a.vt_col0) != a.vt_heads * a.vt_hd))
+    return hipErrorInvalidValue;
+  if (a.hm_q && (!a.vt || !a.hm_k || a.vt_hd != 64 || a.vt_col0 != 2 * a.vt_heads * 64 ||
+                 (a.hm_spatial && (a.win_w % 8 || a.grid_w % a.win_w || a.vt_tokens % (a.win_h * a.win_w)))))
     return hipErrorInvalidValue;
   if (a.epi == EPI_POOL) {
     const int T = a.tokens_per_frame;

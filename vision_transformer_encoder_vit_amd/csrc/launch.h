@@ -62,6 +62,17 @@ struct GemmArgs {
   void* vt = nullptr;
   int vt_col0 = 0, vt_tokens = 0, vt_heads = 0, vt_hd = 0;
   bool vt_only = false;
+  // Head-major attention operands (with vt, head_dim vt_hd = 64): columns
+  // < vt_col0 / 2 (q, after RoPE) times hm_qscale go to hm_q, columns
+  // vt_col0 / 2 .. vt_col0 - 1 (k) to hm_k, both [frame, window, head, i, 64]
+  // with i the token's index inside its attention window; vt then takes the
+  // same window order, [frame, window, head, 64, i]. Windows are the whole
+  // frame, or (hm_spatial) the win_h x win_w tiles of a grid grid_w wide
+  // (win_w a multiple of 8). With vt_only, q and k are not written to C.
+  void* hm_q = nullptr;
+  void* hm_k = nullptr;
+  float hm_qscale = 1.f;
+  bool hm_spatial = false;
   // EPI_BIAS_POS: float32 table [rows, N]; frames of tokens_per_frame tokens
   // on a grid grid_w wide
   const float* pos = nullptr;
@@ -91,6 +102,12 @@ enum AttnMode { ATTN_GLOBAL = 0, ATTN_MASK_UNIT = 1, ATTN_SPATIAL = 2 };
 
 struct AttnArgs {
   const void* qkv = nullptr;  // [B * tokens_in, 3 * dim], rows [q | k | v]
+  // Head-major operands written by the qkv projection (GemmArgs::hm_q):
+  // when qh is set, q (pre-multiplied by scale * log2 e), k and vt are read
+  // in window order, [B, windows, heads, n, 64] and [B, windows, heads, 64,
+  // n]; needs attention_takes_hm()
+  const void* qh = nullptr;
+  const void* kh = nullptr;
   // V transposed, [B, heads, head_dim, tokens_in]: given exactly when
   // attention_takes_vt() holds, and then read in place of qkv's V columns
   const void* vt = nullptr;
@@ -145,6 +162,14 @@ inline int attention_splits(int64_t batch, int64_t windows, int64_t n_q, int64_t
   s = s < tiles / 2 ? s : tiles / 2;
   s = s < 8 ? s : 8;
   return s >= 2 ? (int)s : 1;
+}
+
+// Large windows with head_dim 64 and no query pool: the head-major kernel
+// (operands in window order from the qkv projection; no key split).
+inline bool attention_takes_hm(DType dt, int mode, int64_t n_q, int head_dim, int win_w, int64_t tokens_in,
+                               int q_stride) {
+  return dt == DType::BF16 && (mode == ATTN_GLOBAL || (mode == ATTN_SPATIAL && win_w % 8 == 0)) && n_q >= 128 &&
+         head_dim == 64 && tokens_in % 8 == 0 && q_stride == 1;
 }
 
 inline bool attention_takes_vt(DType dt, int mode, int64_t n_q, int head_dim, int win_w, int64_t tokens_in,
