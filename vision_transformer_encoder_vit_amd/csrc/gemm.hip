@@ -46,6 +46,7 @@ struct GemmParams {
   T* hm_k;
   float hm_qscale;
   bool hm_spatial;
+  float hm_rcp[4];  // 1 / (vt_tokens, grid_w, win_h, win_w)
   const float* pos;  // EPI_BIAS_POS: table [rows, N]
   int pos_mode, pos_side;
   // optional float16 scale per output column (per weight row), applied to
@@ -87,15 +88,32 @@ __device__ __forceinline__ int pos_row(const P& p, int64_t m) {
   return t;
 }
 
-// Attention window of token t of a frame and its index inside the window,
-// as a flat offset (window * window_tokens + index): the frame is one window,
-// or (spatial) the win_h x win_w tiles of a grid grid_w wide, row-major, each
-// read row-major.
-__device__ __forceinline__ int window_order(int t, bool spatial, int grid_w, int win_h, int win_w) {
-  if (!spatial) return t;
-  const int y = t / grid_w, x = t - y * grid_w;
-  const int wy = y / win_h, wx = x / win_w;
-  return ((wy * (grid_w / win_w) + wx) * win_h + (y - wy * win_h)) * win_w + (x - wx * win_w);
+// n / d for 0 <= n < 2^22 and d >= 1, from a float reciprocal (the product
+// is within one of the quotient there) and one correction.
+__device__ __forceinline__ int div_small(int n, int d, float rcp) {
+  int q = (int)((float)n * rcp);
+  const int r = n - q * d;
+  return q + (r >= d ? 1 : 0) - (r < 0 ? 1 : 0);
+}
+
+// Head-major placement of token row m (frames of vt_tokens tokens): blk0 =
+// (frame * windows + window) * heads, wn = tokens per window, i = the
+// token's index in its window. Windows are the frame, or (hm_spatial) the
+// win_h x win_w tiles of a grid grid_w wide, each read row-major.
+template <typename P>
+__device__ __forceinline__ void hm_place(const P& p, int m, int& blk0, int& wn, int& i) {
+  const int fb = div_small(m, p.vt_tokens, p.hm_rcp[0]), t = m - fb * p.vt_tokens;
+  if (!p.hm_spatial) {
+    wn = p.vt_tokens;
+    blk0 = fb * p.vt_heads;
+    i = t;
+    return;
+  }
+  const int y = div_small(t, p.grid_w, p.hm_rcp[1]), x = t - y * p.grid_w;
+  const int wy = div_small(y, p.win_h, p.hm_rcp[2]), wx = div_small(x, p.win_w, p.hm_rcp[3]);
+  wn = p.win_h * p.win_w;
+  blk0 = ((fb * (p.vt_tokens / wn) + wy * (p.grid_w / p.win_w) + wx)) * p.vt_heads;
+  i = (y - wy * p.win_h) * p.win_w + (x - wx * p.win_w);
 }
 
 __device__ __forceinline__ float gelu_erf_f(float v) { return gelu_erf_as(v); }
@@ -590,17 +608,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = cs[(rg * 8 + k) * CROW + cc] + bn;
-        const int vv = n - p.vt_col0, hh = vv / p.vt_hd, d = vv - hh * p.vt_hd;
-        const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
+        const int vv = n - p.vt_col0;
         if (p.hm_q != nullptr) {
-          // [frame, window, head, d, i]: the 8 rows are consecutive tokens of
-          // one window row (win_w % 8 == 0), so consecutive i
-          const int wn = p.hm_spatial ? p.win_h * p.win_w : p.vt_tokens;
-          const int wi = window_order(t, p.hm_spatial, p.grid_w, p.win_h, p.win_w);
-          const int win = wi / wn, i = wi - win * wn;
-          const int64_t blk = ((int64_t)fb * (p.vt_tokens / wn) + win) * p.vt_heads + hh;
-          st16(p.vt + (blk * p.vt_hd + d) * wn + i, pack16<bf16>(v));
+          // [frame, window, head, d, i] (head_dim 64): the 8 rows are
+          // consecutive tokens of one window row (win_w % 8 == 0), so
+          // consecutive i
+          int blk0, wn, i;
+          hm_place(p, m, blk0, wn, i);
+          st16(p.vt + ((blk0 + (vv >> 6)) * 64 + (vv & 63)) * wn + i, pack16<bf16>(v));
         } else {
+          const int hh = vv / p.vt_hd, d = vv - hh * p.vt_hd;
+          const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
           st16(p.vt + (((int64_t)fb * p.vt_heads + hh) * p.vt_hd + d) * p.vt_tokens + t, pack16<bf16>(v));
         }
       }
@@ -716,18 +734,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
       if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) {
         if (to_hm) {
           // q (scaled) or k, 8 consecutive d of one head, to [frame, window, head, i, 64]
+          // head_dim is 64 here
           const int dq = p.vt_col0 / 2, isk = n >= dq ? 1 : 0, nn = n - isk * dq;
-          const int hh = nn / p.vt_hd, d = nn - hh * p.vt_hd;
-          const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
-          const int wn = p.hm_spatial ? p.win_h * p.win_w : p.vt_tokens;
-          const int wi = window_order(t, p.hm_spatial, p.grid_w, p.win_h, p.win_w);
-          const int win = wi / wn, i = wi - win * wn;
-          const int64_t blk = ((int64_t)fb * (p.vt_tokens / wn) + win) * p.vt_heads + hh;
+          const int hh = nn >> 6, d = nn & 63;
+          int blk0, wn, i;
+          hm_place(p, m, blk0, wn, i);
           float hv[8];
           const float sc = isk ? 1.f : p.hm_qscale;
 #pragma unroll
           for (int t2 = 0; t2 < 8; ++t2) hv[t2] = v[t2] * sc;
-          st16((isk ? p.hm_k : p.hm_q) + (blk * wn + i) * p.vt_hd + d, pack16<bf16>(hv));
+          st16((isk ? p.hm_k : p.hm_q) + ((blk0 + hh) * wn + i) * 64 + d, pack16<bf16>(hv));
           if (p.vt_only) continue;
         }
       }
@@ -800,6 +816,10 @@ static GemmParams<T> make_params(const GemmArgs& a) {
   p.hm_k = (T*)a.hm_k;
   p.hm_qscale = a.hm_qscale;
   p.hm_spatial = a.hm_spatial;
+  p.hm_rcp[0] = 1.0f / (float)(a.vt_tokens > 0 ? a.vt_tokens : 1);
+  p.hm_rcp[1] = 1.0f / (float)(a.grid_w > 0 ? a.grid_w : 1);
+  p.hm_rcp[2] = 1.0f / (float)(a.win_h > 0 ? a.win_h : 1);
+  p.hm_rcp[3] = 1.0f / (float)(a.win_w > 0 ? a.win_w : 1);
   p.ws0 = (const _Float16*)a.wscale[0];
   p.ws1 = (const _Float16*)(a.wscale[1] ? a.wscale[1] : a.wscale[0]);
   p.ws2 = (const _Float16*)(a.wscale[2] ? a.wscale[2] : a.wscale[0]);
@@ -832,7 +852,8 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
   if (a.vt && (!mfma32 || (a.epi != EPI_BIAS && a.epi != EPI_BIAS_ROPE) || a.M % 8 || a.vt_tokens <= 0 ||
                a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 || (a.N - a.vt_col0) != a.vt_heads * a.vt_hd))
     return hipErrorInvalidValue;
-  if (a.hm_q && (!a.vt || !a.hm_k || a.vt_hd != 64 || a.vt_col0 != 2 * a.vt_heads * 64 ||
+  if (a.hm_q && (!a.vt || !a.hm_k || a.vt_hd != 64 || a.vt_col0 != 2 * a.vt_heads * 64 || a.M >= (1 << 22) ||
+                 (int64_t)a.M * a.vt_heads * 64 >= (1LL << 31) ||
                  (a.hm_spatial && (a.win_w % 8 || a.grid_w % a.win_w || a.vt_tokens % (a.win_h * a.win_w)))))
     return hipErrorInvalidValue;
   if (a.epi == EPI_POOL) {
