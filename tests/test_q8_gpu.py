@@ -67,15 +67,18 @@ def test_q8_block_full_size_sampled_rows(name):
         gu.check(name + ":" + k, got, ref[k], spec)
 
 
-@pytest.mark.parametrize("name", ["c2_32x32", "c2_hiera_s0"])
-def test_q8_single_kernel_mask_units(name):
+@pytest.mark.parametrize("name,x_scale", [("c2_32x32", 1.0), ("c2_hiera_s0", 1.0), ("c2_hiera_s0", 2.0 ** -8)],
+                         ids=["c2_32x32", "c2_hiera_s0", "c2_hiera_s0_residual_suppressed"])
+def test_q8_single_kernel_mask_units(name, x_scale):
     # the whole-block-per-mask-unit kernel reading the int8 payloads itself
-    # (vit_block_forward; the seams entry point runs the step kernels)
+    # (vit_block_forward; the seams entry point runs the step kernels); with
+    # x scaled by 2^-8 y is mostly the attention and MLP branches
     from vision_transformer_encoder_vit_amd import binding as vb
     spec = dict(SMALL[name] if name in SMALL else C[name], weights="q8_row")
-    print("case q8 fused", name, flush=True)
+    print("case q8 fused", name, x_scale, flush=True)
     assert vb.Plan(vb.desc_from_spec(spec)).stage_mask() == 1 << vb.STAGES.index("fused")
     inp = synth.make_q8_inputs(spec, seed=3)
+    inp["x"] = inp["x"] * np.float32(x_scale)
     y, _ = gu.run_block(spec, gu.to_device(inp, spec), seams=False)
     rows = _sample_rows(synth.out_tokens(spec), 64, 4)
     ref = ob.block_forward_rows(inp["x"], quant.dequant_block(inp), spec, rows)

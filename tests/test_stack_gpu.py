@@ -54,7 +54,7 @@ def test_stack_vs_oracle(side, stage_blocks):
         nrel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
         mrel = float(np.abs(a - b).max() / np.abs(b).max())
         print("feature %d (after block %d): cos %.7f norm-rel %.2e max-rel %.2e" % (k, taps[k], cos, nrel, mrel))
-        assert cos >= 0.9999 and nrel <= 2e-2, (k, cos, nrel)
+        assert cos >= 0.9999 and nrel <= 2e-2 and mrel <= STACK_MAX_REL, (k, cos, nrel, mrel)
 
 
 def test_stack_equals_chained_single_calls():
@@ -107,12 +107,20 @@ def _tower_gpu(specs, x, blocks, pre_ln=None, post_ln=None):
     return gu.to64(y)
 
 
+# Element-wise bound of a stack or tower output: max|got - ref| / max|ref|
+# (the block's rel form). A block holds it to 2e-2; through a chain of bf16
+# blocks the per-block roundings add up, so the chain takes twice that.
+STACK_MAX_REL = 4e-2
+
+
 def _tower_gate(name, got, want):
     a, b = got.ravel(), want.ravel()
     cos = float(a @ b / np.sqrt((a @ a) * (b @ b)))
     nrel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
-    print("%s: cos %.7f norm-rel %.2e max-rel %.2e" % (name, cos, nrel, np.abs(a - b).max() / np.abs(b).max()))
-    assert np.all(np.isfinite(got)) and cos >= 0.9999 and nrel <= 2e-2, (name, cos, nrel)
+    mrel = float(np.abs(a - b).max() / np.abs(b).max())
+    print("%s: cos %.7f norm-rel %.2e max-rel %.2e" % (name, cos, nrel, mrel))
+    assert np.all(np.isfinite(got)) and cos >= 0.9999 and nrel <= 2e-2 and mrel <= STACK_MAX_REL, \
+        (name, cos, nrel, mrel)
 
 
 def test_sam3_trunk_reduced_vs_oracle():
@@ -123,6 +131,33 @@ def test_sam3_trunk_reduced_vs_oracle():
     ln = synth.make_layernorm_params(256, 2)
     got = _tower_gpu(specs, x, blocks, pre_ln=ln)
     _tower_gate("sam3 trunk 8 layers", got, ost.tower_forward(x, blocks, specs, pre_ln=ln))
+
+
+def test_sam3_trunk_full_grid_vs_oracle():
+    # the SAM3 trunk at its real grid and width (72x72 tokens, D 1024, 16
+    # heads): ln_pre, two windowed layers (24x24 windows, in-window RoPE), a
+    # global layer (grid RoPE) and a windowed layer, every output element
+    # against the oracle
+    specs = synth.sam3_trunk(grid=72, layers=4, global_layers=(2,))
+    print("case sam3 trunk 72x72 4 layers", flush=True)
+    x, blocks = synth.make_stack_inputs(specs, seed=5)
+    ln = synth.make_layernorm_params(1024, 5)
+    got = _tower_gpu(specs, x, blocks, pre_ln=ln)
+    _tower_gate("sam3 trunk 72x72 x 4 layers", got, ost.tower_forward(x, blocks, specs, pre_ln=ln))
+
+
+def test_siglip_tower_batch8_vs_oracle():
+    # the SigLIP tower on a batch of 8 frames (12 blocks + post_layernorm);
+    # frames never mix, so the oracle evaluates two of them (0 and 5)
+    specs = synth.siglip_tower(batch=8)
+    print("case siglip tower batch 8", flush=True)
+    x, blocks = synth.make_stack_inputs(specs, seed=6)
+    ln = synth.make_layernorm_params(768, 6)
+    got = _tower_gpu(specs, x, blocks, post_ln=ln)
+    two = [synth.derive(s, batch=2) for s in specs]
+    want = ost.tower_forward(x[[0, 5]], blocks, two, post_ln=ln)
+    for i, f in enumerate((0, 5)):
+        _tower_gate("siglip tower batch 8, frame %d" % f, got[f], want[i])
 
 
 def test_siglip_tower_full_frame_vs_oracle():
