@@ -201,6 +201,25 @@ vit_status vit_block_forward(vit_block_t plan, const vit_block_weights* w,
                              const void* x, void* y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Maximum workspace of vit_block_forward_static: the library's own device
+ * scratch, 256 MiB on every GPU the library runs on (held from the first
+ * call on that GPU until the process ends). */
+#define VIT_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): as
+ * vit_block_forward, with the workspace taken from the library's static
+ * device scratch instead of the caller. Allocates nothing (no hipMalloc,
+ * hipFree or allocating library call); the first call on a device looks the
+ * scratch up there. Fails with VIT_ERR_WORKSPACE, before any launch, when
+ * the plan's workspace (vit_block_workspace_size) exceeds
+ * VIT_STATIC_SCRATCH_BYTES. Every call on one GPU uses that GPU's single
+ * scratch and leaves its contents behind; nothing in it needs to start at
+ * zero. Calls that overlap on one GPU (other streams, other threads) race
+ * on the scratch: the caller serialises them. */
+vit_status vit_block_forward_static(vit_block_t plan, const vit_block_weights* w,
+                                    const void* x, void* y, void* stream);
+
 /* As vit_block_forward, and also writes every non-NULL seam buffer. It
  * always runs the step-by-step kernels (one per stage), so where
  * vit_block_forward uses the single fused kernel (bf16 mask units of 64

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libvitblock.so")
 
 VIT_OK, VIT_ERR_INVALID_ARG, VIT_ERR_UNSUPPORTED, VIT_ERR_WORKSPACE, VIT_ERR_DEVICE = range(5)
+VIT_STATIC_SCRATCH_BYTES = 256 << 20  # include/vit_block.h
 VIT_DTYPE_F32, VIT_DTYPE_BF16 = 0, 1
 VIT_ATTN_GLOBAL, VIT_ATTN_MASK_UNIT, VIT_ATTN_SPATIAL = 0, 1, 2
 VIT_GELU_ERF, VIT_GELU_TANH = 0, 1
@@ -115,6 +116,7 @@ def _load():
         "vit_block_create": [P(vit_block_desc), P(_vp)],
         "vit_block_workspace_size": [_vp, P(ctypes.c_size_t)],
         "vit_block_forward": [_vp, P(vit_block_weights), _vp, _vp, _vp, ctypes.c_size_t, _vp],
+        "vit_block_forward_static": [_vp, P(vit_block_weights), _vp, _vp, _vp],
         "vit_block_forward_seams": [_vp, P(vit_block_weights), _vp, _vp, P(vit_block_seams), _vp,
                                     ctypes.c_size_t, _vp],
         "vit_block_forward_timed": [_vp, P(vit_block_weights), _vp, _vp, _vp, ctypes.c_size_t, _vp,
@@ -223,6 +225,11 @@ class Plan:
         check(lib.vit_block_forward(self.handle, ctypes.byref(weights), _ptr(x), _ptr(y),
                                     _ptr(workspace), workspace.numel() * workspace.element_size()
                                     if workspace is not None else 0, _stream(stream)))
+
+    def forward_static(self, weights, x, y, stream=None):
+        """vit_block_forward_static: the workspace is the library's own
+        device scratch (no allocation; calls on one GPU must not overlap)."""
+        check(lib.vit_block_forward_static(self.handle, ctypes.byref(weights), _ptr(x), _ptr(y), _stream(stream)))
 
     def forward_timed(self, weights, x, y, workspace, events, stream=None):
         """events: a ctypes array of 2 * VIT_NSTAGES hipEvent_t handles."""

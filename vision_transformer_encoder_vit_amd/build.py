@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvitblock.so")
-SOURCES = ["capi.cpp", "rowops.hip", "gemm.hip", "attention.hip", "fused_mu.hip", "stem.hip"]
+SOURCES = ["capi.cpp", "rowops.hip", "gemm.hip", "attention.hip", "fused_mu.hip", "stem.hip", "scratch.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

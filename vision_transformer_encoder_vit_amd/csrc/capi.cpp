@@ -699,6 +699,20 @@ VIT_API vit_status vit_block_forward(vit_block_t plan, const vit_block_weights* 
   return forward_impl(plan, w, x, y, nullptr, workspace, workspace_bytes, stream);
 }
 
+VIT_API vit_status vit_block_forward_static(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
+                                            void* stream) {
+  if (!plan) return fail(VIT_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->ws_bytes > vit::STATIC_SCRATCH_BYTES)
+    return fail(VIT_ERR_WORKSPACE,
+                "this block needs %zu bytes of workspace; the library's static scratch holds %zu "
+                "(use vit_block_forward with a caller workspace)",
+                plan->ws_bytes, vit::STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  vit_status st = device_status(vit::static_scratch(&ws), "static scratch lookup");
+  if (st != VIT_OK) return st;
+  return forward_impl(plan, w, x, y, nullptr, ws, vit::STATIC_SCRATCH_BYTES, stream);
+}
+
 VIT_API vit_status vit_block_forward_timed(vit_block_t plan, const vit_block_weights* w, const void* x, void* y,
                                            void* workspace, size_t workspace_bytes, void* stream,
                                            void* const* events, int32_t n_events) {

@@ -7,6 +7,12 @@ namespace vit {
 
 enum class DType { F32 = 0, BF16 = 1 };
 
+// The library's own device scratch (scratch.hip): STATIC_SCRATCH_BYTES on
+// every GPU, for vit_block_forward_static. static_scratch() returns its
+// address on the current device (looked up on the first call there).
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(256) << 20;
+hipError_t static_scratch(void** ptr);
+
 // Optional events for measurement: `start` takes the first kernel's begin
 // time and `stop` the last kernel's end time (hipExtLaunchKernel timestamps
 // from the dispatch packets, so no extra packets enter the stream).
