@@ -29,10 +29,6 @@ PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 DEFAULT_CONFIG = "c5g_sam3_global"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-CSRC = os.path.join(ROOT, "vision_transformer_encoder_vit_amd", "csrc")
-STAGE_SOURCE = {"ln1": "rowops.hip", "ln2": "rowops.hip", "qkv": "gemm.hip", "residual": "gemm.hip",
-                "attn": "attention.hip", "proj": "gemm.hip", "fc1": "gemm.hip", "fc2": "gemm.hip",
-                "fused": "fused_mu.hip"}
 
 
 def describe(spec):
@@ -55,47 +51,6 @@ def describe(spec):
         (", " + ", ".join(extra)) if extra else "")
 
 
-def stage_work(spec, residual_in_qkv=False):
-    """Algorithmic FLOPs and minimum HBM bytes of each stage."""
-    from vision_transformer_encoder_vit_amd import work
-    e = work.DTYPE_BYTES[spec["dtype"]]
-    B = spec["batch"]
-    n_in = spec["grid_h"] * spec["grid_w"]
-    m_in, m_out = B * n_in, B * n_in // spec["q_stride"]
-    Di, Do = spec["dim_in"], spec["dim_out"]
-    g = work.gemms(spec)
-    w = {"ln1": (0.0, work.layernorm_bytes(m_in, Di, spec["dtype"])),
-         "ln2": (0.0, work.layernorm_bytes(m_out, Do, spec["dtype"]))}
-    w["qkv"] = (work.gemm_flops(*g["qkv"]), work.gemm_bytes(*g["qkv"], spec["dtype"]))
-    if "res" in g:
-        # projection of every input row, 4x max-pooled: h and W_res read
-        # once, the pooled rows written once
-        w["residual"] = (work.gemm_flops(*g["res"]), e * (m_in * Di + Do * Di + m_out * Do))
-    else:
-        w["residual"] = (0.0, 0.0)
-    if residual_in_qkv and "res" in g:
-        # the qkv GEMM also computes the pooled residual projection: its
-        # stage carries that work (h is read once for both)
-        f, by = w["qkv"]
-        w["qkv"] = (f + w["residual"][0], by + e * (Do * Di + m_out * Do))
-        w["residual"] = (0.0, 0.0)
-    w["attn"] = (work.attention_flops(spec), work.attention_bytes(spec))
-    w["proj"] = (work.gemm_flops(*g["proj"]), work.gemm_bytes(*g["proj"], spec["dtype"], extra_rows_in=m_out))
-    w["fc1"] = (work.gemm_flops(*g["fc1"]), work.gemm_bytes(*g["fc1"], spec["dtype"]))
-    w["fc2"] = (work.gemm_flops(*g["fc2"]), work.gemm_bytes(*g["fc2"], spec["dtype"], extra_rows_in=m_out))
-    # whole block in one kernel: x in, y out, every weight once
-    w["fused"] = (work.block_flops(spec), work.block_min_bytes(spec))
-    return w
-
-
-def src_hash(stage):
-    h = hashlib.sha256()
-    for f in (STAGE_SOURCE[stage], "common.h"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(config, stage):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current source of the stage's kernel."""
@@ -103,6 +58,7 @@ def measured_traffic(config, stage):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
+    from vision_transformer_encoder_vit_amd.profsum import src_hash
     rec = t.get(config, {}).get(stage)
     if not rec or rec.get("src_sha") != src_hash(stage):
         return None
@@ -216,6 +172,7 @@ def run(spec, steps, warmup, with_cpu):
 
     ms_step = 1e3 * elapsed / steps
     tokens = spec["batch"] * spec["grid_h"] * spec["grid_w"]
+    from vision_transformer_encoder_vit_amd.work import stage_work
     wk = stage_work(spec, residual_in_qkv=spec["q_stride"] == 4 and "residual" not in active and "fused" not in active)
     mfma_stages = [st for st in ("qkv", "residual", "attn", "proj", "fc1", "fc2", "fused") if st in active]
     flops = sum(wk[s][0] for s in mfma_stages)

@@ -1,5 +1,12 @@
 """Summaries of rocprofv3 CSV output as markdown tables (measurement tooling).
 
+  python -m vision_transformer_encoder_vit_amd.profsum traffic CONFIG FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+      HBM bytes per launch of each stage of one block workload from two
+      rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of bench.py on it, each
+      scaled by what the same counter reads for the plain copy of
+      bench.py --copy-calibration; updates profiles/traffic.json (with a hash
+      of the stage kernel's source) and prints the markdown rows
+
   python -m vision_transformer_encoder_vit_amd.profsum stats DIR
       kernel statistics (calls, mean/min/max duration, share of GPU time)
       from every *kernel_stats.csv under DIR
@@ -10,21 +17,44 @@
       rates below
 
 Derived rates (MI355X: 256 CUs = 1024 SIMDs in 8 XCDs):
-  MFMA busy      sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024)
+  MFMA busy      SQ_VALU_MFMA_BUSY_CYCLES / 1024 (busy cycles per SIMD; a
+                 32x32x16 bf16 MFMA keeps its SIMD's matrix core 32 cycles),
+                 over the kernel's cycles at 2.4 GHz and at the measured clock
+  clock MHz      GRBM_GUI_ACTIVE per XCD, minus the same counter on the
+                 runtime's 2 us copy kernel of the run (a fixed collection
+                 window), over the duration difference; GRBM_GUI_ACTIVE is
+                 reported summed over the 8 XCDs
   bf16 MFMA FLOP SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
-  clock MHz      GRBM_GUI_ACTIVE per XCD / dispatch duration in us
-  VALU busy      sum SQ_ACTIVE_INST_VALU x 4 / (GRBM_GUI_ACTIVE per XCD x 256)
-                 (the SQ counts VALU issue in quad-cycles per CU)
-  LDS busy       sum SQ_LDS_IDX_ACTIVE x 4 / (GRBM_GUI_ACTIVE per XCD x 256)
-GRBM_GUI_ACTIVE is reported summed over the XCDs; it is divided by 8.
+  L2             TCC_HIT / (TCC_HIT + TCC_MISS); TCP_TCC_READ_REQ_LATENCY /
+                 TCP_TCC_READ_REQ (cycles from a vector cache miss to L2 data)
 """
 import csv
 import glob
+import hashlib
+import json
 import os
 import sys
 from collections import defaultdict
 
 N_XCD, N_CU, N_SIMD = 8, 256, 1024
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+TRAFFIC_FILE = os.path.join(os.path.dirname(HERE), "profiles", "traffic.json")
+# source file of each stage's kernel (with common.h): a change invalidates
+# the stage's measured traffic
+STAGE_SOURCE = {"ln1": "rowops.hip", "ln2": "rowops.hip", "qkv": "gemm.hip", "residual": "gemm.hip",
+                "attn": "attention.hip", "proj": "gemm.hip", "fc1": "gemm.hip", "fc2": "gemm.hip",
+                "fused": "fused_mu.hip"}
+STAGE_ORDER = ["ln1", "qkv", "residual", "attn", "proj", "ln2", "fc1", "fc2", "fused"]
+COPY_BYTES = 65536 * 512 * 2  # bench.py --copy-calibration: bytes read and written per launch
+
+
+def src_hash(stage):
+    h = hashlib.sha256()
+    for f in (STAGE_SOURCE[stage], "common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _rows(dirs, suffix):
@@ -73,26 +103,108 @@ def counters(dirs):
                                             " | ".join("%.4g" % mean(vals[k][c]) if c in vals[k] else ""
                                                        for c in cols)))
     print()
-    print("| kernel | mean us | clock MHz | MFMA busy | bf16 MFMA TFLOP/s | VALU busy | LDS busy |")
-    print("|---|---:|---:|---:|---:|---:|---:|")
+    # GRBM_GUI_ACTIVE spans a fixed collection window around each dispatch
+    # as well as the kernel; the runtime's short copy kernel in the same runs
+    # measures that window, so (GUI - GUI_copy) / (t - t_copy) is the clock
+    # during a long kernel (reported for kernels of 20 us or more)
+    copy = next((k for k in names if k.startswith("__amd_rocclr_copyBuffer")), None)
+    gui_copy = mean(vals[copy]["GRBM_GUI_ACTIVE"]) / N_XCD if copy and "GRBM_GUI_ACTIVE" in vals[copy] else None
+    t_copy = mean(dur[copy]) if copy else None
+    print("| kernel | mean us | clock MHz | MFMA busy cycles / SIMD | MFMA busy at 2.4 GHz | MFMA busy at that clock "
+          "| bf16 MFMA TFLOP/s | VALU instr / MFMA instr | of which transcendental | L2 hit rate | L2 read latency (cycles) "
+          "| LDS bank-conflict cycles |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
     for k in names:
         v = {c: mean(x) for c, x in vals[k].items()}
         us = mean(dur[k])
-        gui = v.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD
-        f = lambda x: "%.3f" % x if x == x else "-"
-        mfma = v.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (gui * N_SIMD)
+        if k == copy or "SQ_VALU_MFMA_BUSY_CYCLES" not in v:
+            continue
+        busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD
+        clock = None
+        if gui_copy is not None and us >= 20 and "GRBM_GUI_ACTIVE" in v:
+            clock = (v["GRBM_GUI_ACTIVE"] / N_XCD - gui_copy) / (us - t_copy)
+        f = lambda x, fmt="%.3f": fmt % x if x is not None and x == x else "-"
         tf = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512 / (us * 1e-6) / 1e12
-        valu = v.get("SQ_ACTIVE_INST_VALU", float("nan")) * 4 / (gui * N_CU)
-        lds = v.get("SQ_LDS_IDX_ACTIVE", float("nan")) * 4 / (gui * N_CU)
-        print("| `%s` | %.2f | %s | %s | %s | %s | %s |" % (short(k), us, "%.0f" % (gui / us) if gui == gui else "-",
-                                                         f(mfma), "%.0f" % tf if tf == tf else "-", f(valu), f(lds)))
+        mf = v.get("SQ_INSTS_MFMA", 0) or float("nan")
+        hit = v.get("TCC_HIT_sum")
+        hitr = hit / (hit + v["TCC_MISS_sum"]) if hit is not None and "TCC_MISS_sum" in v else None
+        lat = v["TCP_TCC_READ_REQ_LATENCY_sum"] / v["TCP_TCC_READ_REQ_sum"] if "TCP_TCC_READ_REQ_sum" in v else None
+        print("| `%s` | %.2f | %s | %.0f | %.3f | %s | %.0f | %s | %s | %s | %s | %s |" % (
+            short(k), us, f(clock, "%.0f"), busy, busy / (us * 2400.0), f(busy / (us * clock) if clock else None),
+            tf, f(v.get("SQ_INSTS_VALU", float("nan")) / mf, "%.1f"),
+            f(v.get("SQ_INSTS_VALU_TRANS_F32", float("nan")) / mf, "%.1f"), f(hitr), f(lat, "%.0f"),
+            f(v.get("SQ_LDS_BANK_CONFLICT"), "%.3g")))
+
+
+def _dispatches(d, counter):
+    """(kernel name, counter value) per dispatch in dispatch order, block
+    kernels only (runtime copies dropped)."""
+    per = {}
+    for r in _rows([d], "counter_collection.csv"):
+        if r["Counter_Name"] != counter or r["Kernel_Name"].startswith("__amd"):
+            continue
+        key = (int(r.get("Process_Id") or 0), int(r["Dispatch_Id"]))
+        name, v = per.get(key, (r["Kernel_Name"], 0.0))
+        per[key] = (name, v + float(r["Counter_Value"]))
+    return [per[k] for k in sorted(per)]
+
+
+def traffic(config, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    sys.path.insert(0, os.path.dirname(HERE))
+    from vision_transformer_encoder_vit_amd import synth, work
+    spec = synth.CONFIGS[config]
+    mean = lambda xs: sum(xs) / len(xs)
+    cf = mean([v for _, v in _dispatches(copy_fetch_dir, "FETCH_SIZE")])
+    cw = mean([v for _, v in _dispatches(copy_write_dir, "WRITE_SIZE")])
+    fscale, wscale = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    fetch, write = _dispatches(fetch_dir, "FETCH_SIZE"), _dispatches(write_dir, "WRITE_SIZE")
+    # the kernels of one forward: the period of the dispatch name sequence
+    names = [n for n, _ in fetch]
+    k = next(p for p in range(1, len(names) + 1)
+             if len(names) % p == 0 and all(names[i] == names[i % p] for i in range(len(names))))
+    n_gemm = sum("gemm" in n for n in names[:k])
+    gemm_names = ["qkv", "proj", "fc1", "fc2"] if n_gemm == 4 else ["qkv", "residual", "proj", "fc1", "fc2"]
+    stages, ln_i, g_i = [], 0, 0
+    for n in names[:k]:
+        if "layernorm" in n:
+            stages.append(("ln1", "ln2")[ln_i])
+            ln_i += 1
+        elif "attention" in n:
+            stages.append("attn")
+        elif "block_mask_unit" in n:
+            stages.append("fused")
+        else:
+            stages.append(gemm_names[g_i])
+            g_i += 1
+    k = len(stages)
+    if len(fetch) % k or len(write) % k:
+        raise SystemExit("dispatch counts %d / %d are not a multiple of the %d kernels of one forward"
+                         % (len(fetch), len(write), k))
+    wk = work.stage_work(spec)
+    table = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    rec = table.setdefault(config, {})
+    for i, st in enumerate(stages):
+        fv = mean([v for _, v in fetch[i::k]])
+        wv = mean([v for _, v in write[i::k]])
+        by = (fv * fscale + wv * wscale) * 1024
+        rec[st] = {"bytes_per_launch": by, "fetch_kib_per_dispatch": fv, "write_kib_per_dispatch": wv,
+                   "fetch_scale": fscale, "write_scale": wscale, "dispatches": [len(fetch[i::k]), len(write[i::k])],
+                   "src_sha": src_hash(st)}
+        alg = wk[st][1]
+        print("| %s | %s | `%s` | %.1f | %.1f | %.0f | %.0f | %.2f |" % (config, st, short(fetch[i][0], 60), fv, wv,
+                                                                       by, alg, by / alg))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1)
+    print("copy calibration: FETCH_SIZE %.1f KiB (scale %.4f), WRITE_SIZE %.1f KiB (scale %.4f)" % (cf, fscale, cw, wscale))
 
 
 if __name__ == "__main__":
-    if len(sys.argv) < 3 or sys.argv[1] not in ("stats", "counters"):
+    if len(sys.argv) < 3 or sys.argv[1] not in ("stats", "counters", "traffic"):
         print(__doc__)
         sys.exit(2)
     if sys.argv[1] == "stats":
         stats(sys.argv[2])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:7])
     else:
         counters(sys.argv[2:])

@@ -106,3 +106,35 @@ def siglip_tower_gflop():
                 mlp=3072, mode="global", q_stride=1, n_windows=1)
     embed = gemm_flops(1024, 768, 3 * 16 * 16)
     return (12 * block_flops(spec) + embed) / 1e9
+
+
+def stage_work(spec, residual_in_qkv=False):
+    """Algorithmic FLOPs and minimum HBM bytes of each stage."""
+    e = DTYPE_BYTES[spec["dtype"]]
+    B = spec["batch"]
+    n_in = spec["grid_h"] * spec["grid_w"]
+    m_in, m_out = B * n_in, B * n_in // spec["q_stride"]
+    Di, Do = spec["dim_in"], spec["dim_out"]
+    g = gemms(spec)
+    w = {"ln1": (0.0, layernorm_bytes(m_in, Di, spec["dtype"])),
+         "ln2": (0.0, layernorm_bytes(m_out, Do, spec["dtype"]))}
+    w["qkv"] = (gemm_flops(*g["qkv"]), gemm_bytes(*g["qkv"], spec["dtype"]))
+    if "res" in g:
+        # projection of every input row, 4x max-pooled: h and W_res read
+        # once, the pooled rows written once
+        w["residual"] = (gemm_flops(*g["res"]), e * (m_in * Di + Do * Di + m_out * Do))
+    else:
+        w["residual"] = (0.0, 0.0)
+    if residual_in_qkv and "res" in g:
+        # the qkv GEMM also computes the pooled residual projection: its
+        # stage carries that work (h is read once for both)
+        f, by = w["qkv"]
+        w["qkv"] = (f + w["residual"][0], by + e * (Do * Di + m_out * Do))
+        w["residual"] = (0.0, 0.0)
+    w["attn"] = (attention_flops(spec), attention_bytes(spec))
+    w["proj"] = (gemm_flops(*g["proj"]), gemm_bytes(*g["proj"], spec["dtype"], extra_rows_in=m_out))
+    w["fc1"] = (gemm_flops(*g["fc1"]), gemm_bytes(*g["fc1"], spec["dtype"]))
+    w["fc2"] = (gemm_flops(*g["fc2"]), gemm_bytes(*g["fc2"], spec["dtype"], extra_rows_in=m_out))
+    # whole block in one kernel: x in, y out, every weight once
+    w["fused"] = (block_flops(spec), block_min_bytes(spec))
+    return w
