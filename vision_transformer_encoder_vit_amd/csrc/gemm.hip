@@ -15,6 +15,7 @@
 #include "launch.h"
 
 #include <hip/hip_ext.h>
+#include <numeric>
 
 namespace vit {
 
@@ -69,6 +70,9 @@ struct GemmPoolParams : GemmParams<T> {
   int64_t ld_pool;
   int pool_col0;
 };
+
+// Eight zero floats: the bias of a GEMM without one.
+__device__ __attribute__((aligned(16))) const float kZeros8[8] = {};
 
 // Pointer of segment seg; S4 (EPI_POOL) adds a fourth. By value: taking
 // the kernel argument block by reference changes how the compiler loads it.
@@ -283,6 +287,23 @@ __host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4
 __device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Buffer descriptor of `bytes` bytes from `base` (range-checked: loads past
+// the end return zeros); the operands are wave-uniform, readfirstlane keeps
+// the descriptor in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lds_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int nb = (int)min(max(bytes, (int64_t)0), (int64_t)0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(nb), 0x00020000);
+}
+// 16 bytes per lane from a buffer into LDS (lane l's at lds + 16 l bytes);
+// a function of its own so that host compilation of the kernel templates
+// never sees the device-only builtin
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, bf16* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
 // Workgroup -> output tile. Workgroups are dealt round-robin to the 8 XCDs
 // (each with its own L2): each XCD gets a contiguous range of the logical
 // tile order, walked in groups of GM tile rows, so the tiles that run
@@ -336,8 +357,11 @@ struct WaitAhead {
 // four partial tiles are summed in LDS before the epilogue. For grids of
 // about one workgroup per CU, where one wave per SIMD with one MFMA per K
 // step spends most of each step waiting on its LDS fragment reads.
+// The RoPE epilogue of the two-workgroups-per-CU tiles needs the register
+// budget stated explicitly to stay at two waves per SIMD.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int ST, int EPI, bool KT, bool KW>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
+    amdgpu_waves_per_eu(EPI == EPI_BIAS_ROPE && (BM + BN) * 64 * ST * 2 <= 81920 ? 2 : 1))) void gemm_mfma32_kernel(
     typename std::conditional<EPI == EPI_POOL, GemmPoolParams<bf16>, GemmParams<bf16>>::type p) {
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   constexpr int BK = 64;
@@ -391,27 +415,41 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
   xcd_tile<8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tmi, tni);
   const int m0 = tmi * (POOL ? PB : BM), n0 = tni * BN;
 
-  // per-lane source rows (clamped into the matrix: rows past M or N are
-  // loaded but never stored)
-  const bf16* src[LPW];
+  // Operand tiles by buffer loads straight into LDS. Load j of wave w
+  // fills LDS row group L = j * NW + w (rows 8L .. 8L+7, 1 KB): loads
+  // j < LA are A rows for every wave, the rest W rows, all of one weight
+  // segment (BM and seg_cols are multiples of 8). So every load's buffer
+  // descriptor is known at compile time: one for A (from the tile's first
+  // row; POOL: from A) and one per W load (from its group's first row to
+  // the segment's end). The per-lane byte offset is fixed over K and the K
+  // tile is a scalar offset: no per-load vector arithmetic. Rows past M or
+  // N read zeros (never stored).
+  const int waveu = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int LA = BM / 8 / NW;
+  static_assert((BM / 8) % NW == 0, "A row groups must split evenly over the waves");
+  const __amdgpu_buffer_rsrc_t rsA = POOL ? lds_rsrc(p.A, (int64_t)p.M * p.lda * 2)
+                                          : lds_rsrc(p.A + (int64_t)m0 * p.lda, (int64_t)(p.M - m0) * p.lda * 2);
+  __amdgpu_buffer_rsrc_t rsW[LPW - LA];
+  uint32_t voff[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int row = (wave * LPW + j) * 8 + lane / 8;
+    const int row0 = (j * NW + waveu) * 8, row = row0 + lane / 8;
     const int chunk = (lane & 7) ^ lds_swz(row);
-    if (row < BM) {
-      int m;
+    if (j < LA) {
       if constexpr (POOL) {
         const int q4 = p.tokens_per_frame / 4, pr = min(m0 + row % PB, p.M / 4 - 1);
-        m = (pr / q4) * p.tokens_per_frame + (row / PB) * q4 + pr % q4;
+        const int m = (pr / q4) * p.tokens_per_frame + (row / PB) * q4 + pr % q4;
+        voff[j] = (uint32_t)(((int64_t)m * p.lda + chunk * 8) * 2);
       } else {
-        m = min(m0 + row, p.M - 1);
+        voff[j] = (uint32_t)(((int64_t)row * p.lda + chunk * 8) * 2);
       }
-      src[j] = p.A + (int64_t)m * p.lda + chunk * 8;
     } else {
-      const int n = min(n0 + row - BM, p.N - 1);
-      const int seg = n / p.seg_cols;
-      const bf16* base = seg_pick<POOL>(p.W0, p.W1, p.W2, W3, seg);
-      src[j] = base + (int64_t)(n - seg * p.seg_cols) * p.K + chunk * 8;
+      const int nf = min(n0 + row0 - BM, p.N - 1);  // the group's first weight row
+      const int seg = nf / p.seg_cols, n_in_seg = nf - seg * p.seg_cols;
+      const bf16* base = seg_pick<POOL>(p.W0, p.W1, p.W2, W3, seg) + (int64_t)n_in_seg * p.K;
+      const int rows_left = min(p.seg_cols, p.N - seg * p.seg_cols) - n_in_seg;
+      rsW[j - LA] = lds_rsrc(base, (int64_t)rows_left * p.K * 2);
+      voff[j] = (uint32_t)(((int64_t)(row - row0) * p.K + chunk * 8) * 2);
     }
   }
   // KT (K % 64 != 0, K >= 64): the partial last tile is read as the last
@@ -422,8 +460,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
   const int klast = p.K - BK;
   // load j of tile kt (LPW per wave per tile)
   auto load = [&](int j, int kt) {
-    __builtin_amdgcn_global_load_lds((const void*)(src[j] + (KT ? min(kt * BK, klast) : kt * BK)),
-                                     (lds_ptr)(sm + (kt % ST) * STAGE + (wave * LPW + j) * 512), 16, 0, 0);
+    buf_load_lds16(j < LA ? rsA : rsW[j < LA ? 0 : j - LA], sm + (kt % ST) * STAGE + (j * NW + waveu) * 512, voff[j],
+                   (KT ? min(kt * BK, klast) : kt * BK) * 2);
   };
   const int wm = KW ? 0 : wave / WAVES_N, wn = KW ? 0 : wave % WAVES_N;
   const int fr = lane & 31, g = lane >> 5;
@@ -537,6 +575,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
   // thread with bias / RoPE / GELU / residual -> one 16-byte store per row
   // chunk. Lane (fr, g) of 32x32 tile (i, j) holds row j*32+fr, columns
   // i*32 + 8q + 4g + e in register 4q + e.
+  //
+  // Every global load of the epilogue is issued ahead of the stores: the
+  // bias once per tile right after the main loop, the residual / RoPE /
+  // position rows of a pass before that pass's staging. A load placed
+  // between the stores of the chunk loops would wait out a full memory
+  // round trip each time (the compiler cannot move a load above a store
+  // that may alias it, and the wait for a load also waits for every store
+  // issued before it).
   constexpr int PR0 = (ST * STAGE * 2) / (CROW * 4);
   constexpr int PR = KW || PR0 >= BM ? BM : (PR0 >= BM / 2 ? BM / 2 : BM / 4);
   static_assert(!POOL || PR == BM, "EPI_POOL stages the whole tile at once");
@@ -559,8 +605,83 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
         scl[i][q] = *reinterpret_cast<const u32x2*>(seg_pick<POOL>(p.ws0, p.ws1, p.ws2, ws3, seg) + (n - seg * p.seg_cols));
       }
   }
+  // Chunk k of a pass (e = tid + k NT) covers row e / G8 and columns
+  // (e % G8) * 8 .. + 7: its columns repeat with period DC in k, so a
+  // thread needs the bias of DC column groups only (1 for BN = 64, 128, 256
+  // with NT = 256, 256, 512; 3 for BN = 192). Likewise the V^T copy below
+  // (one column cc = e % BN per iteration) with period DCV.
+  constexpr int CH = (PR * G8 + NT - 1) / NT;
+  constexpr bool CH_EVEN = (PR * G8) % NT == 0;
+  constexpr int DC = G8 / std::gcd(G8, NT % G8);
+  constexpr bool VT = EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE;
+  constexpr int CHV = ((PR / 8) * BN + NT - 1) / NT;
+  constexpr bool CHV_EVEN = ((PR / 8) * BN) % NT == 0;
+  constexpr int DCV = BN / std::gcd(BN, NT % BN);
+  static_assert(!POOL || DC == 1, "EPI_POOL: one column group per thread");
+  f32x4 bsv[DC][2];
+  float bvt[VT ? DCV : 1];
+#pragma unroll
+  for (int k = 0; k < DC; ++k) {
+    // columns past N take the last valid group's bias (never stored)
+    const int n = min(n0 + ((tid + k * NT) % G8) * 8, p.N - 8);
+    const int seg = n / p.seg_cols;
+    const float* bp = seg_pick<POOL>(p.b0, p.b1, p.b2, b3, seg);
+    // no bias (EPI_BIAS_POS may have none): eight zeros; a load either way,
+    // without a branch around it
+    const float* bq = bp != nullptr ? bp + (n - seg * p.seg_cols) : kZeros8;
+    bsv[k][0] = *reinterpret_cast<const f32x4*>(bq);
+    bsv[k][1] = *reinterpret_cast<const f32x4*>(bq + 4);
+  }
+  if constexpr (VT) {
+#pragma unroll
+    for (int k = 0; k < DCV; ++k) {
+      const int n = min(n0 + (tid + k * NT) % BN, p.N - 1);
+      const int seg = n / p.seg_cols;
+      const float* bp = seg_pick<false>(p.b0, p.b1, p.b2, b3, seg);
+      bvt[k] = *(bp != nullptr ? bp + (n - seg * p.seg_cols) : kZeros8);
+    }
+  }
+  u32x4 resv[EPI == EPI_BIAS_RES ? CH : 1];
+  f32x4 tab[EPI == EPI_BIAS_ROPE || EPI == EPI_BIAS_POS ? CH : 1][2];
 #pragma unroll
   for (int pass = 0; pass < BM / PR; ++pass) {
+    // this pass's residual / position / RoPE rows: chunks 0 .. CH0-1 here,
+    // the rest (8 registers per chunk for the tables) at chunk CH0 of the
+    // store loop, which keeps two workgroups per CU within the register
+    // file. Loaded unconditionally from clamped addresses (rows past M,
+    // columns past N: never stored), so that the loads need no branches.
+    constexpr bool FETCH = !POOL && (EPI == EPI_BIAS_RES || EPI == EPI_BIAS_ROPE || EPI == EPI_BIAS_POS);
+    constexpr int CH0 = EPI == EPI_BIAS_RES ? CH : (CH + 1) / 2;
+    const bool want = EPI == EPI_BIAS_RES || (EPI == EPI_BIAS_POS ? p.pos_mode != POS_NONE : p.rope_cols > 0);
+    auto fetch = [&](int k) {
+      const int e = min(tid + k * NT, PR * G8 - 1);
+      const int r = e / G8, c8 = (e - r * G8) * 8;
+      const int m = min(m0 + pass * PR + r, p.M - 1), n = min(n0 + c8, p.N - 8);
+      if constexpr (EPI == EPI_BIAS_RES) {
+        resv[k] = ld16(p.res + (int64_t)m * p.ldres + n);
+      } else if constexpr (EPI == EPI_BIAS_POS) {
+        const float* pp = p.pos + (int64_t)pos_row(p, m) * p.N + n;
+        tab[k][0] = *reinterpret_cast<const f32x4*>(pp);
+        tab[k][1] = *reinterpret_cast<const f32x4*>(pp + 4);
+      } else if constexpr (EPI == EPI_BIAS_ROPE) {
+        const int t = m % p.tokens_per_frame;
+        int rr = t;
+        if (p.rope_mode == 1) {
+          const int yy = t / p.grid_w, xx = t - yy * p.grid_w;
+          rr = (yy % p.win_h) * p.win_w + (xx % p.win_w);
+        }
+        // multiple of 8: pairs d/2 .. d/2+3 (columns past rope_cols: any
+        // valid row of the table, unused)
+        const int d = (n % (p.rope_cols / 2)) % p.head_dim;
+        const float* cs4 = p.rope + ((int64_t)rr * (p.head_dim / 2) + d / 2) * 2;
+        tab[k][0] = *reinterpret_cast<const f32x4*>(cs4);
+        tab[k][1] = *reinterpret_cast<const f32x4*>(cs4 + 4);
+      }
+    };
+    if (FETCH && want) {
+#pragma unroll
+      for (int k = 0; k < CH0; ++k) fetch(k);
+    }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -599,15 +720,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
       // transposed copy of the V columns: one column x 8 consecutive token
       // rows per thread (a 16-byte run of one V^T row); rows are within one
       // frame since vt_tokens % 8 == 0
-      for (int e = tid; e < (PR / 8) * BN; e += NT) {
+#pragma unroll
+      for (int kv = 0; kv < CHV; ++kv) {
+        const int e = tid + kv * NT;
+        if (!CHV_EVEN && e >= (PR / 8) * BN) break;
         const int cc = e % BN, rg = e / BN;
         const int m = m0 + pass * PR + rg * 8, n = n0 + cc;
         if (m >= p.M || n >= p.N || n < p.vt_col0) continue;
-        const int seg = n / p.seg_cols;
-        const float bn = (seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2))[n - seg * p.seg_cols];
         float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = cs[(rg * 8 + k) * CROW + cc] + bn;
+        for (int k = 0; k < 8; ++k) v[k] = cs[(rg * 8 + k) * CROW + cc] + bvt[kv % DCV];
         const int vv = n - p.vt_col0;
         if (p.hm_q != nullptr) {
           // [frame, window, head, d, i] (head_dim 64): the 8 rows are
@@ -632,12 +754,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
         if (n >= p.pool_col0 || n >= p.N || pr >= mp) continue;
         const int64_t m = (int64_t)(pr / q4) * p.tokens_per_frame + (r / PB) * q4 + pr % q4;
         float v[8];
-        *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8);
-        *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4);
-        const int seg = n / p.seg_cols;
-        const float* bb = seg_pick<true>(p.b0, p.b1, p.b2, b3, seg) + (n - seg * p.seg_cols);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] += bb[t];
+        *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8) + bsv[0][0];
+        *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4) + bsv[0][1];
         st16(p.C + m * p.ldc + n, pack16<bf16>(v));
       }
       // columns >= pool_col0: the max over the four quarter rows, then the bias
@@ -657,60 +775,44 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
             hi[t] = fmaxf(hi[t], h2[t]);
           }
         }
-        const int seg = n / p.seg_cols;
-        const float* bb = seg_pick<true>(p.b0, p.b1, p.b2, b3, seg) + (n - seg * p.seg_cols);
         float v[8];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          v[t] = lo[t] + bb[t];
-          v[4 + t] = hi[t] + bb[4 + t];
+          v[t] = lo[t] + bsv[0][0][t];
+          v[4 + t] = hi[t] + bsv[0][1][t];
         }
         st16(p.pool_out + (int64_t)pr * p.ld_pool + (n - p.pool_col0), pack16<bf16>(v));
       }
       continue;
     }
-    for (int e = tid; e < PR * G8; e += NT) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      if (FETCH && CH0 < CH && k == CH0 && want) {
+#pragma unroll
+        for (int k2 = CH0; k2 < CH; ++k2) fetch(k2);
+      }
+      const int e = tid + k * NT;
+      if (!CH_EVEN && e >= PR * G8) break;
       const int r = e / G8, c8 = (e - r * G8) * 8;
       const int m = m0 + pass * PR + r, n = n0 + c8;
       if (m >= p.M || n >= p.N) continue;
       if (p.vt_only && n >= p.vt_col0) continue;
       const bool to_hm = (EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) && p.hm_q != nullptr && n < p.vt_col0;
       float v[8];
-      *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8);
-      *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4);
-      const int seg = n / p.seg_cols;
-      const float* bseg = seg == 0 ? p.b0 : (seg == 1 ? p.b1 : p.b2);
-      if (EPI != EPI_BIAS_POS || bseg != nullptr) {
-        const float* bb = bseg + (n - seg * p.seg_cols);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bb), b1 = *reinterpret_cast<const f32x4*>(bb + 4);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v[t] += b0[t];
-          v[4 + t] += b1[t];
-        }
-      }
+      *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8) + bsv[k % DC][0];
+      *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(cs + r * CROW + c8 + 4) + bsv[k % DC][1];
       if (EPI == EPI_BIAS_POS) {
         if (p.pos_mode != POS_NONE) {
-          const float* pp = p.pos + (int64_t)pos_row(p, m) * p.N + n;
-          const f32x4 q0 = *reinterpret_cast<const f32x4*>(pp), q1 = *reinterpret_cast<const f32x4*>(pp + 4);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            v[t] += q0[t];
-            v[4 + t] += q1[t];
+            v[t] += tab[k][0][t];
+            v[4 + t] += tab[k][1][t];
           }
         }
       } else if (EPI == EPI_BIAS_ROPE) {
         if (n < p.rope_cols) {
-          const int t = m % p.tokens_per_frame;
-          int rr = t;
-          if (p.rope_mode == 1) {
-            const int yy = t / p.grid_w, xx = t - yy * p.grid_w;
-            rr = (yy % p.win_h) * p.win_w + (xx % p.win_w);
-          }
-          const int d = (n % (p.rope_cols / 2)) % p.head_dim;  // multiple of 8: pairs d/2 .. d/2+3
-          const float* cs4 = p.rope + ((int64_t)rr * (p.head_dim / 2) + d / 2) * 2;
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs4), c1 = *reinterpret_cast<const f32x4*>(cs4 + 4);
-          const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+          const float cc[8] = {tab[k][0][0], tab[k][0][1], tab[k][0][2], tab[k][0][3],
+                               tab[k][1][0], tab[k][1][1], tab[k][1][2], tab[k][1][3]};
 #pragma unroll
           for (int pr = 0; pr < 4; ++pr) {
             const float a0 = v[2 * pr], a1 = v[2 * pr + 1], co = cc[2 * pr], si = cc[2 * pr + 1];
@@ -727,7 +829,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mfma32_kernel(
       } else if (EPI == EPI_BIAS_RES) {
         if (p.branch) st16(p.branch + (int64_t)m * p.ldbranch + n, pack16<bf16>(v));
         float rv[8];
-        unpack16<bf16>(ld16(p.res + (int64_t)m * p.ldres + n), rv);
+        unpack16<bf16>(resv[k], rv);
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] += rv[t];
       }
@@ -856,6 +958,8 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
                  (int64_t)a.M * a.vt_heads * 64 >= (1LL << 31) ||
                  (a.hm_spatial && (a.win_w % 8 || a.grid_w % a.win_w || a.vt_tokens % (a.win_h * a.win_w)))))
     return hipErrorInvalidValue;
+  // the pooled form addresses A's rows by 32-bit byte offsets from its start
+  if (a.epi == EPI_POOL && (int64_t)a.M * a.lda * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   if (a.epi == EPI_POOL) {
     const int T = a.tokens_per_frame;
     if (!mfma32 || a.vt || T <= 0 || T % 4 || a.M % T || a.pool_col0 % 8 || a.pool_col0 > a.N || !a.pool_out)
