@@ -47,7 +47,7 @@ struct GemmParams {
   T* hm_k;
   float hm_qscale;
   bool hm_spatial;
-  float hm_rcp[4];  // 1 / (vt_tokens, grid_w, win_h, win_w)
+  float hm_rcp[5];  // 1 / (vt_tokens, grid_w, win_h, win_w, tokens_per_frame)
   const float* pos;  // EPI_BIAS_POS: table [rows, N]
   int pos_mode, pos_side;
   // optional float16 scale per output column (per weight row), applied to
@@ -641,6 +641,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
       bvt[k] = *(bp != nullptr ? bp + (n - seg * p.seg_cols) : kZeros8);
     }
   }
+  // RoPE: the table column of each column group (pairs d/2 .. d/2+3 of the
+  // head dimension d; a multiple of 8), and the row part below per chunk
+  int ropec[EPI == EPI_BIAS_ROPE ? DC : 1];
+  if constexpr (EPI == EPI_BIAS_ROPE) {
+#pragma unroll
+    for (int k = 0; k < DC; ++k) {
+      const int n = min(n0 + ((tid + k * NT) % G8) * 8, p.N - 8);
+      ropec[k] = p.rope_cols > 0 ? (n % (p.rope_cols / 2)) % p.head_dim : 0;
+    }
+  }
   u32x4 resv[EPI == EPI_BIAS_RES ? CH : 1];
   f32x4 tab[EPI == EPI_BIAS_ROPE || EPI == EPI_BIAS_POS ? CH : 1][2];
 #pragma unroll
@@ -664,16 +674,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
         tab[k][0] = *reinterpret_cast<const f32x4*>(pp);
         tab[k][1] = *reinterpret_cast<const f32x4*>(pp + 4);
       } else if constexpr (EPI == EPI_BIAS_ROPE) {
-        const int t = m % p.tokens_per_frame;
+        // table row: the token's index in its frame, or (spatial windows)
+        // in its window; divisions by float reciprocals (m < 2^22). Columns
+        // past rope_cols read some valid entry, unused.
+        const int t = m - div_small(m, p.tokens_per_frame, p.hm_rcp[4]) * p.tokens_per_frame;
         int rr = t;
         if (p.rope_mode == 1) {
-          const int yy = t / p.grid_w, xx = t - yy * p.grid_w;
-          rr = (yy % p.win_h) * p.win_w + (xx % p.win_w);
+          const int yy = div_small(t, p.grid_w, p.hm_rcp[1]), xx = t - yy * p.grid_w;
+          rr = (yy - div_small(yy, p.win_h, p.hm_rcp[2]) * p.win_h) * p.win_w + (xx - div_small(xx, p.win_w, p.hm_rcp[3]) * p.win_w);
         }
-        // multiple of 8: pairs d/2 .. d/2+3 (columns past rope_cols: any
-        // valid row of the table, unused)
-        const int d = (n % (p.rope_cols / 2)) % p.head_dim;
-        const float* cs4 = p.rope + ((int64_t)rr * (p.head_dim / 2) + d / 2) * 2;
+        const float* cs4 = p.rope + ((int64_t)rr * (p.head_dim / 2) + ropec[k % DC] / 2) * 2;
         tab[k][0] = *reinterpret_cast<const f32x4*>(cs4);
         tab[k][1] = *reinterpret_cast<const f32x4*>(cs4 + 4);
       }
@@ -922,6 +932,7 @@ static GemmParams<T> make_params(const GemmArgs& a) {
   p.hm_rcp[1] = 1.0f / (float)(a.grid_w > 0 ? a.grid_w : 1);
   p.hm_rcp[2] = 1.0f / (float)(a.win_h > 0 ? a.win_h : 1);
   p.hm_rcp[3] = 1.0f / (float)(a.win_w > 0 ? a.win_w : 1);
+  p.hm_rcp[4] = 1.0f / (float)(a.tokens_per_frame > 0 ? a.tokens_per_frame : 1);
   p.ws0 = (const _Float16*)a.wscale[0];
   p.ws1 = (const _Float16*)(a.wscale[1] ? a.wscale[1] : a.wscale[0]);
   p.ws2 = (const _Float16*)(a.wscale[2] ? a.wscale[2] : a.wscale[0]);
@@ -954,6 +965,8 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
   if (a.vt && (!mfma32 || (a.epi != EPI_BIAS && a.epi != EPI_BIAS_ROPE) || a.M % 8 || a.vt_tokens <= 0 ||
                a.vt_tokens % 8 || a.vt_col0 % 8 || a.vt_hd <= 0 || (a.N - a.vt_col0) != a.vt_heads * a.vt_hd))
     return hipErrorInvalidValue;
+  // RoPE rows and head-major placement divide row indices by float reciprocals
+  if (a.epi == EPI_BIAS_ROPE && a.M >= (1 << 22)) return hipErrorInvalidValue;
   if (a.hm_q && (!a.vt || !a.hm_k || a.vt_hd != 64 || a.vt_col0 != 2 * a.vt_heads * 64 || a.M >= (1 << 22) ||
                  (int64_t)a.M * a.vt_heads * 64 >= (1LL << 31) ||
                  (a.hm_spatial && (a.win_w % 8 || a.grid_w % a.win_w || a.vt_tokens % (a.win_h * a.win_w)))))
