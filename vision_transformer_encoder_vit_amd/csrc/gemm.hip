@@ -992,10 +992,12 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
   if (dt == DType::F32) return gemm_go<float, 64, 64, 2, 2>(a, s, ev);
   if (mfma32) {
     // One full wave of 256x256 tiles fills the 256 CUs. Otherwise two
-    // workgroups per CU: 128x128 tiles, or for large products (>= 2e10 FLOP)
+    // workgroups per CU: 128x128 tiles, or for products of >= 9e9 FLOP
     // 128x192 / 192x128 tiles where 192 divides N / M exactly (fewer, larger
     // tiles with no ragged edge; 3-8 % faster on the SigLIP and SAM3 MLP and
-    // qkv shapes, slower on the small projections)
+    // qkv shapes; since the epilogue issues its loads ahead of its stores
+    // also on the out-projections: SAM3 5184x1024x1024 22.1 -> 20.5 us,
+    // SigLIP 8192x768x768 18.6 -> 18.2 us)
     const GemmParams<bf16> p = make_params<bf16>(a);
     const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
     if (a.K % 64 != 0) {
@@ -1008,18 +1010,20 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
     }
     const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (t256 >= 224 && t256 <= 256) return gemm32_go<256, 256, 2, 4>(p, a.epi, s, ev);
-    if (2.0 * a.M * a.N * a.K >= 2e10) {
+    if (2.0 * a.M * a.N * a.K >= 9e9) {
       // at most one workgroup per CU (e.g. fc2, N = 768 or 1024): four LDS
       // stages (all 160 KB), since no second workgroup hides load latency
-      // (13 % faster on the SAM3 fc2, 8 % on SigLIP's)
+      // (13 % faster on the SAM3 fc2, 8 % on SigLIP's), and eight waves of
+      // 96x32 / 32x96 so that each SIMD has two (SAM3 fc2 61.3 -> 58.0 us,
+      // out-projection 20.3 -> 18.8; SigLIP fc2 44.1 -> 43.4, 17.7 -> 17.2)
       const int64_t t_n192 = (int64_t)((a.M + 127) / 128) * (a.N / 192);
       const int64_t t_m192 = (int64_t)(a.M / 192) * ((a.N + 127) / 128);
       if (a.N % 192 == 0) {
-        if (t_n192 <= 256) return gemm32_go<128, 192, 2, 2, 4>(p, a.epi, s, ev);
+        if (t_n192 <= 256) return gemm32_go<128, 192, 4, 2, 4>(p, a.epi, s, ev);
         return gemm32_go<128, 192, 2, 2>(p, a.epi, s, ev);
       }
       if (a.M % 192 == 0) {
-        if (t_m192 <= 256) return gemm32_go<192, 128, 2, 2, 4>(p, a.epi, s, ev);
+        if (t_m192 <= 256) return gemm32_go<192, 128, 2, 4, 4>(p, a.epi, s, ev);
         return gemm32_go<192, 128, 2, 2>(p, a.epi, s, ev);
       }
     }
