@@ -653,6 +653,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
   }
   u32x4 resv[EPI == EPI_BIAS_RES ? CH : 1];
   f32x4 tab[EPI == EPI_BIAS_ROPE || EPI == EPI_BIAS_POS ? CH : 1][2];
+  // RoPE table row of token row m: the token's index in its frame, or
+  // (spatial windows) in its window; divisions by float reciprocals
+  // (m < 2^22)
+  auto rope_row = [&](int m) {
+    const int t = m - div_small(m, p.tokens_per_frame, p.hm_rcp[4]) * p.tokens_per_frame;
+    if (p.rope_mode != 1) return t;
+    const int yy = div_small(t, p.grid_w, p.hm_rcp[1]), xx = t - yy * p.grid_w;
+    return (yy - div_small(yy, p.win_h, p.hm_rcp[2]) * p.win_h) * p.win_w + (xx - div_small(xx, p.win_w, p.hm_rcp[3]) * p.win_w);
+  };
+  // Per-row placement of the tile's rows -- the RoPE table row's float
+  // offset, and the head-major q / k and V^T element offsets -- computed
+  // once per tile into LDS past the staging area (after the first barrier,
+  // when the main loop is done with LDS), so that no chunk of the store
+  // loops repeats the index divisions. Where that space does not exist
+  // (the K-split form) each chunk computes its own.
+  constexpr int RT_OFF = (PR * CROW * 4 * (KW ? NW : 1) + 15) / 16 * 16;  // bytes into sm
+  constexpr bool RT = (EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) && !POOL && RT_OFF + BM * 12 <= SM * 2;
+  int* rt = reinterpret_cast<int*>(reinterpret_cast<char*>(sm) + RT_OFF);
+  const int wn_u = p.hm_spatial ? p.win_h * p.win_w : p.vt_tokens;  // tokens per head-major window
 #pragma unroll
   for (int pass = 0; pass < BM / PR; ++pass) {
     // this pass's residual / position / RoPE rows: chunks 0 .. CH0-1 here,
@@ -674,25 +693,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
         tab[k][0] = *reinterpret_cast<const f32x4*>(pp);
         tab[k][1] = *reinterpret_cast<const f32x4*>(pp + 4);
       } else if constexpr (EPI == EPI_BIAS_ROPE) {
-        // table row: the token's index in its frame, or (spatial windows)
-        // in its window; divisions by float reciprocals (m < 2^22). Columns
-        // past rope_cols read some valid entry, unused.
-        const int t = m - div_small(m, p.tokens_per_frame, p.hm_rcp[4]) * p.tokens_per_frame;
-        int rr = t;
-        if (p.rope_mode == 1) {
-          const int yy = div_small(t, p.grid_w, p.hm_rcp[1]), xx = t - yy * p.grid_w;
-          rr = (yy - div_small(yy, p.win_h, p.hm_rcp[2]) * p.win_h) * p.win_w + (xx - div_small(xx, p.win_w, p.hm_rcp[3]) * p.win_w);
-        }
-        const float* cs4 = p.rope + ((int64_t)rr * (p.head_dim / 2) + ropec[k % DC] / 2) * 2;
+        // pairs ropec/2 .. +3 of the row (columns past rope_cols read some
+        // valid entry, unused)
+        const int row_off = RT ? rt[3 * min(pass * PR + r, BM - 1)] : rope_row(m) * p.head_dim;
+        const float* cs4 = p.rope + (int64_t)row_off + ropec[k % DC];
         tab[k][0] = *reinterpret_cast<const f32x4*>(cs4);
         tab[k][1] = *reinterpret_cast<const f32x4*>(cs4 + 4);
       }
     };
-    if (FETCH && want) {
+    // RoPE with the row table: pass 0's first chunks once the table is
+    // written; all of a pass's chunks up front where they are few
+    constexpr bool RT_ROPE = RT && EPI == EPI_BIAS_ROPE;
+    constexpr int F0 = RT_ROPE && CH <= 4 ? CH : CH0;
+    if (FETCH && want && (!RT_ROPE || pass > 0)) {
 #pragma unroll
-      for (int k = 0; k < CH0; ++k) fetch(k);
+      for (int k = 0; k < F0; ++k) fetch(k);
     }
     __syncthreads();
+    if (RT && pass == 0) {
+      for (int r = tid; r < BM; r += NT) {
+        const int m = min(m0 + r, p.M - 1);
+        if (EPI == EPI_BIAS_ROPE && p.rope_cols > 0) rt[3 * r] = rope_row(m) * p.head_dim;
+        if (p.hm_q != nullptr) {
+          int blk0, wn, i;
+          hm_place(p, m, blk0, wn, i);
+          rt[3 * r + 1] = (blk0 * wn + i) * 64;  // q / k: + (head * wn) * 64 + d
+          rt[3 * r + 2] = blk0 * wn * 64 + i;    // V^T: + (head * 64 + d) * wn
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int row = wm * WROWS + j * 32 + fr;
@@ -726,6 +755,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
       }
       __syncthreads();
     }
+    if (FETCH && want && RT_ROPE && pass == 0) {
+#pragma unroll
+      for (int k = 0; k < F0; ++k) fetch(k);
+    }
     if ((EPI == EPI_BIAS || EPI == EPI_BIAS_ROPE) && p.vt != nullptr && n0 + BN > p.vt_col0) {
       // transposed copy of the V columns: one column x 8 consecutive token
       // rows per thread (a 16-byte run of one V^T row); rows are within one
@@ -745,9 +778,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
           // [frame, window, head, d, i] (head_dim 64): the 8 rows are
           // consecutive tokens of one window row (win_w % 8 == 0), so
           // consecutive i
-          int blk0, wn, i;
-          hm_place(p, m, blk0, wn, i);
-          st16(p.vt + ((blk0 + (vv >> 6)) * 64 + (vv & 63)) * wn + i, pack16<bf16>(v));
+          if constexpr (RT) {
+            st16(p.vt + rt[3 * (pass * PR + rg * 8) + 2] + vv * wn_u, pack16<bf16>(v));
+          } else {
+            int blk0, wn, i;
+            hm_place(p, m, blk0, wn, i);
+            st16(p.vt + ((blk0 + (vv >> 6)) * 64 + (vv & 63)) * wn + i, pack16<bf16>(v));
+          }
         } else {
           const int hh = vv / p.vt_hd, d = vv - hh * p.vt_hd;
           const int fb = m / p.vt_tokens, t = m - fb * p.vt_tokens;
@@ -797,9 +834,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
     }
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      if (FETCH && CH0 < CH && k == CH0 && want) {
+      if (FETCH && F0 < CH && k == F0 && want) {
 #pragma unroll
-        for (int k2 = CH0; k2 < CH; ++k2) fetch(k2);
+        for (int k2 = F0; k2 < CH; ++k2) fetch(k2);
       }
       const int e = tid + k * NT;
       if (!CH_EVEN && e >= PR * G8) break;
@@ -849,13 +886,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((
           // head_dim is 64 here
           const int dq = p.vt_col0 / 2, isk = n >= dq ? 1 : 0, nn = n - isk * dq;
           const int hh = nn >> 6, d = nn & 63;
-          int blk0, wn, i;
-          hm_place(p, m, blk0, wn, i);
+          int off;
+          if constexpr (RT) {
+            off = rt[3 * (pass * PR + r) + 1] + hh * wn_u * 64 + d;
+          } else {
+            int blk0, wn, i;
+            hm_place(p, m, blk0, wn, i);
+            off = ((blk0 + hh) * wn + i) * 64 + d;
+          }
           float hv[8];
           const float sc = isk ? 1.f : p.hm_qscale;
 #pragma unroll
           for (int t2 = 0; t2 < 8; ++t2) hv[t2] = v[t2] * sc;
-          st16((isk ? p.hm_k : p.hm_q) + ((blk0 + hh) * wn + i) * 64 + d, pack16<bf16>(hv));
+          st16((isk ? p.hm_k : p.hm_q) + off, pack16<bf16>(hv));
           if (p.vt_only) continue;
         }
       }
