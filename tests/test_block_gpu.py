@@ -55,6 +55,15 @@ SMALL = {
     "c4_f32": d(C["c4_siglip_b8"], batch=2, grid_h=10, grid_w=10, dim_in=128, dim_out=128, heads=2,
                 mlp=512, dtype="f32"),
     "c3a_f32": d(C["c3a_hiera_trans"], grid_h=16, grid_w=16, n_windows=16, dtype="f32"),
+    # global windows whose 5 query tiles x 16 heads split the keys four ways,
+    # among the waves of each workgroup: 540 queries (a partial last block
+    # of 32) over 9 key tiles (a partial last tile), dealt 3 / 3 / 3 / 0 to
+    # the four waves (one wave without keys)
+    "c3b_ksw_18x30": d(C["c3b_hiera_s2"], grid_h=18, grid_w=30, dim_in=896, dim_out=896, heads=16, mlp=3584),
+    # the same split on pooled queries: 2048 tokens pooled to 512 (4 query
+    # tiles x 16 heads) attending to all 2048
+    "c3b_ksw_pool": d(C["c3b_hiera_s2"], grid_h=32, grid_w=64, dim_in=448, dim_out=896, heads=16, mlp=3584,
+                      q_stride=4),
 }
 
 

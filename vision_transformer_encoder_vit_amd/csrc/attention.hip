@@ -370,18 +370,25 @@ struct WinCursor {
   }
 };
 
-template <int NW, int QB, int MODE, bool POOL>
+// KSW: the workgroup's waves share one block of QW queries and split the
+// window's key tiles among them, each with its own K / V^T buffers; at the
+// end the waves' (max, sum, O) merge through LDS (weights 2^((m_w - m) c)).
+// For grids too small to fill the chip without splitting the keys, and no
+// partials leave the workgroup.
+template <int NW, int QB, int MODE, bool POOL, bool KSW = false>
 __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf16> p) {
   constexpr int QW = 32 * QB;  // queries per wave
   static_assert(MODE == ATTN_GLOBAL || MODE == ATTN_SPATIAL, "large-window kernel");
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][KT * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][64 * KT];
+  constexpr int NB = KSW ? NW : 1;  // K / V^T double buffers: one per wave (KSW) or shared
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[NB][2][KT * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[NB][2][64 * KT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, h = lane >> 5;
+  const int wb = KSW ? wave : 0;
   int bid = blockIdx.x;
-  const int split = bid % p.splits;  // key split: tiles [t0, t1) of the window
-  bid /= p.splits;
+  const int split = KSW ? 0 : bid % p.splits;  // key split: tiles [t0, t1) of the window
+  bid /= KSW ? 1 : p.splits;
   const int head = bid % p.heads;
   bid /= p.heads;
   const int qt = bid % p.q_tiles;
@@ -391,8 +398,9 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   const int hd = p.head_dim, D = p.dim;
   const int ld = (int)p.ld_qkv;
   const int ntiles = (p.n_kv + KT - 1) / KT;
-  const int per = (ntiles + p.splits - 1) / p.splits;
-  const int t0 = split * per, t1 = min(ntiles, t0 + per);
+  const int nsplit = KSW ? NW : p.splits, part = KSW ? wave : split;
+  const int per = (ntiles + nsplit - 1) / nsplit;
+  const int t0 = part * per, t1 = min(ntiles, t0 + per);
   // element offset of this frame + window origin in qkv (fits 32 bits: the
   // host checks the buffer size); token (x, y) of the window is at
   // base + (y * grid_w + x) * ld
@@ -418,7 +426,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   int qrow_out[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int i = qt * NW * QW + wave * QW + qb * 32 + fr;
+    const int i = KSW ? qt * QW + qb * 32 + fr : qt * NW * QW + wave * QW + qb * 32 + fr;
     const bool valid = i < p.n_q;
     WinCursor cur;
     cur.init(valid ? i : 0, wwx);
@@ -448,8 +456,9 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
 
   // ---- K tile: wave instruction j fills LDS rows 8j .. 8j+7 (16 bytes per
   // lane); LDS row R holds key pi(R) of the tile.
-  constexpr int LOADS = KT / 8 / NW;
+  constexpr int LOADS = KSW ? KT / 8 : KT / 8 / NW;
   static_assert(KT % (8 * NW) == 0, "tile rows must split over the waves");
+  const int grp0 = KSW ? 0 : wave * LOADS;  // this wave's first 8-row group of a tile
   const int last_kv = p.n_kv - 1;
   WinCursor last_cur;
   last_cur.init(last_kv, wwx);
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   int kchunk[LOADS], kkey[LOADS];
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
-    const int row = (wave * LOADS + j) * 8 + lane / 8;
+    const int row = (grp0 + j) * 8 + lane / 8;
     kkey[j] = key_of_row(row);
     kcur[j].init(t0 * KT + kkey[j], wwx);
     // chunks past head_dim read neighbouring finite values (Q is zero there)
@@ -474,7 +483,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   vlast.init(p.n_kv - 8, wwx);
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
-    const int row = (wave * LOADS + j) * 8 + lane / 8;
+    const int row = (grp0 + j) * 8 + lane / 8;
     vpos[j] = ((lane & 7) ^ kswz(row)) * 8;
     vcur[j].init(t0 * KT + vpos[j], wwx);
     vrow_off[j] = min(row, hd - 1) * p.tokens_in;
@@ -485,14 +494,14 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
       // keys past the window read the last key (masked out of the softmax)
       const int t = kt * KT + kkey[j] <= last_kv ? tok(kcur[j]) : tok(last_cur);
       __builtin_amdgcn_global_load_lds((const void*)(base + t * ld + kchunk[j]),
-                                       (attn_lds_ptr)(&Ks[kt & 1][(wave * LOADS + j) * 512]), 16, 0, 0);
+                                       (attn_lds_ptr)(&Ks[wb][kt & 1][(grp0 + j) * 512]), 16, 0, 0);
       kcur[j].step(step_dx, step_dy, wwx);
     }
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int t = kt * KT + vpos[j] <= p.n_kv - 8 ? tok(vcur[j]) : tok(vlast);
       __builtin_amdgcn_global_load_lds((const void*)(vt_base + vrow_off[j] + t),
-                                       (attn_lds_ptr)(&Vs[kt & 1][(wave * LOADS + j) * 512]), 16, 0, 0);
+                                       (attn_lds_ptr)(&Vs[wb][kt & 1][(grp0 + j) * 512]), 16, 0, 0);
       vcur[j].step(step_dx, step_dy, wwx);
     }
   };
@@ -515,8 +524,10 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
     const int buf = kt & 1;
     // this wave's loads of tile kt have landed; after the barrier every
     // wave's have, and every wave is done with the buffer refilled next
+    // (KSW: the buffers are the wave's own, and the waves' tile counts
+    // differ, so no barrier)
     __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
-    __syncthreads();
+    if (!KSW) __syncthreads();
     if (kt + 1 < t1) issue(kt + 1);
     f32x16 sacc[QB][2];  // [qb][kb]
 #pragma unroll
@@ -528,7 +539,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = kb * 32 + fr;
-        const u32x4 kfr = ld16(&Ks[buf][row * 64 + ((ks * 2 + h) ^ kswz(row)) * 8]);
+        const u32x4 kfr = ld16(&Ks[wb][buf][row * 64 + ((ks * 2 + h) ^ kswz(row)) * 8]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfr),
@@ -587,12 +598,69 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
           const int row = db * 32 + fr;
-          const u32x4 vf = ld16(&Vs[buf][row * 64 + ((4 * kb + 2 * s + h) ^ kswz(row)) * 8]);
+          const u32x4 vf = ld16(&Vs[wb][buf][row * 64 + ((4 * kb + 2 * s + h) ^ kswz(row)) * 8]);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
                                                                    __builtin_bit_cast(bf16x8, pf[qb][kb][s]), acc_o[qb][db], 0, 0, 0);
         }
+  }
+
+  if constexpr (KSW) {
+    // ---- merge the waves: (m, l) per query -> LDS; each wave's O^T times
+    // 2^((m_w - m) c) / l -> LDS as [wave][query][d]; thread (query, 8 d)
+    // sums the waves' values and stores 16 bytes of ctx
+    float* mls = reinterpret_cast<float*>(&Vs[0][0][0]);  // [NW][QW][2]
+    float* ops = reinterpret_cast<float*>(&Ks[0][0][0]);  // [NW][QW][64]
+    static_assert(NW * QW * 64 * 4 <= (int)sizeof(Ks) && NW * QW * 2 * 4 <= (int)sizeof(Vs), "merge space");
+    __syncthreads();  // every wave is done with its K / V^T buffers
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
+      if (h == 0) {
+        mls[(wave * QW + qb * 32 + fr) * 2] = m_run[qb];
+        mls[(wave * QW + qb * 32 + fr) * 2 + 1] = l;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int q = qb * 32 + fr;
+      float m = mls[q * 2];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) m = fmaxf(m, mls[(w * QW + q) * 2]);
+      float l = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) l += __builtin_amdgcn_exp2f((mls[(w * QW + q) * 2] - m) * c) * mls[(w * QW + q) * 2 + 1];
+      const float sc = __builtin_amdgcn_exp2f((m_run[qb] - m) * c) / l;
+      float* op = ops + (wave * QW + q) * 64;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          *reinterpret_cast<f32x4*>(op + db * 32 + 8 * gq + 4 * h) =
+              f32x4{acc_o[qb][db][4 * gq], acc_o[qb][db][4 * gq + 1], acc_o[qb][db][4 * gq + 2],
+                    acc_o[qb][db][4 * gq + 3]} * sc;
+    }
+    __syncthreads();
+    for (int e = tid; e < QW * 8; e += 64 * NW) {
+      const int q = e / 8, d0 = (e % 8) * 8;
+      const int i = qt * QW + q;
+      if (i >= p.n_q || d0 >= hd) continue;
+      f32x4 o0 = *reinterpret_cast<const f32x4*>(ops + q * 64 + d0);
+      f32x4 o1 = *reinterpret_cast<const f32x4*>(ops + q * 64 + d0 + 4);
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        o0 += *reinterpret_cast<const f32x4*>(ops + (w * QW + q) * 64 + d0);
+        o1 += *reinterpret_cast<const f32x4*>(ops + (w * QW + q) * 64 + d0 + 4);
+      }
+      WinCursor cur;
+      cur.init(i, wwx);
+      bf16* out = p.ctx + ((int64_t)b * p.tokens_out + tok(cur)) * p.ld_ctx + head * hd + d0;
+      store4<bf16>(out, o0);
+      if (d0 + 4 < hd) store4<bf16>(out + 4, o1);
+    }
+    return;
   }
 
   // ---- normalise and store: lane holds ctx[q][32db + 8g + 4h .. +3], g = r/4
@@ -674,14 +742,15 @@ static void combine_go(const AttnParams<bf16>& p, hipStream_t s, hipEvent_t stop
                         p.batch_rows, p.heads, p.head_dim, p.dim, p.scale_log2);
 }
 
-template <int NW, int QB, int MODE, bool POOL>
+template <int NW, int QB, int MODE, bool POOL, bool KSW = false>
 static hipError_t attn32_go(AttnParams<bf16> p, int batch, hipStream_t s, StageEvents ev) {
-  p.q_tiles = (p.n_q + 32 * QB * NW - 1) / (32 * QB * NW);
+  if (KSW) p.splits = 1;
+  p.q_tiles = KSW ? (p.n_q + 32 * QB - 1) / (32 * QB) : (p.n_q + 32 * QB * NW - 1) / (32 * QB * NW);
   const int64_t blocks = (int64_t)batch * p.windows * p.q_tiles * p.heads;
   if (blocks == 0) return hipSuccess;
   p.batch_rows = (int64_t)batch * p.tokens_out;
   const hipEvent_t stop = p.splits > 1 ? nullptr : ev.stop;
-  hipExtLaunchKernelGGL((attention_mfma32_kernel<NW, QB, MODE, POOL>), dim3((unsigned)(blocks * p.splits)),
+  hipExtLaunchKernelGGL((attention_mfma32_kernel<NW, QB, MODE, POOL, KSW>), dim3((unsigned)(blocks * p.splits)),
                         dim3(64 * NW), 0, s, ev.start, stop, 0, p);
   switch (p.splits) {
     case 1: break;
@@ -1039,6 +1108,14 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
                             (int64_t)a.batch * a.tokens_in * a.ld_qkv))
       return hipErrorInvalidValue;
     if constexpr (std::is_same<T, bf16>::value) {
+      // a split of 4 (64-85 query tiles) becomes a split among the four
+      // waves of each workgroup: 256-340 workgroups of one query block
+      // (128 KB of LDS, one per CU), no partials and no combine launch
+      if (p.splits == 4) {
+        if (a.mode == ATTN_SPATIAL) return attn32_go<ATTN_NW, ATTN_QB, ATTN_SPATIAL, false, true>(p, a.batch, s, ev);
+        return pool ? attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, true, true>(p, a.batch, s, ev)
+                    : attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, false, true>(p, a.batch, s, ev);
+      }
       if (a.mode == ATTN_SPATIAL)
         return attn32_go<ATTN_NW, ATTN_QB, ATTN_SPATIAL, false>(p, a.batch, s, ev);
       return pool ? attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, true>(p, a.batch, s, ev)
