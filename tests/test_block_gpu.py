@@ -64,6 +64,10 @@ SMALL = {
     # tiles x 16 heads) attending to all 2048
     "c3b_ksw_pool": d(C["c3b_hiera_s2"], grid_h=32, grid_w=64, dim_in=448, dim_out=896, heads=16, mlp=3584,
                       q_stride=4),
+    # a Hiera stage-3 block (256 tokens, D 896): qkv (with V^T) and fc1 on
+    # 32x64 K-split tiles, the projections on 32x32 ones, attention split
+    # over two workgroups and combined
+    "c3b_s3_16x16": d(C["c3b_hiera_s2"], grid_h=16, grid_w=16, dim_in=896, dim_out=896, heads=16, mlp=3584),
 }
 
 

@@ -1076,6 +1076,18 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, hipStream_t s, StageEvents e
     // load latency behind. With a long K (the Hiera fc2, K = 1792 / 3584)
     // the waves split K instead (13.2 -> 12.3 us on the 1024x448x1792 fc2);
     // for short K the partial-tile reduction costs more than it saves
+    // Up to 256 such tiles the waves split K over smaller tiles instead,
+    // 32x32 (up to 128 64x64 tiles) or 32x64 (up to 256), for four times or
+    // twice the workgroups. Hiera 1024 and 256 token blocks, per launch:
+    // out-projection 5.45 -> 4.51 / 7.20 -> 5.10 us, fc2 9.85 -> 7.26 /
+    // 16.2 -> 10.0; 256 tokens: qkv (with V^T) 8.01 -> 7.19, fc1 8.07 ->
+    // 7.25. (Two LDS stages above 256 tiles won alone, 7.44 -> 7.21 us on
+    // the 1024-token qkv, but lost inside the block.)
+    const int64_t t64 = (int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64);
+    if (t128 < 192 && a.epi != EPI_BIAS_POS) {
+      if (t64 <= 128) return gemm32_go<32, 32, 2, 2, 4, false, true>(p, a.epi, s, ev);
+      if (t64 <= 256) return gemm32_go<32, 64, 2, 2, 4, false, true>(p, a.epi, s, ev);
+    }
     if (t128 < 192 && a.K >= 1024) return gemm32_go<64, 64, 2, 2, 4, false, true>(p, a.epi, s, ev);
     if (t128 < 192) return gemm32_go<64, 64, 2, 2, 4>(p, a.epi, s, ev);
     return gemm32_go<128, 128, 2, 2>(p, a.epi, s, ev);
