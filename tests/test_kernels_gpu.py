@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("dim", [8, 56, 112, 224, 448, 768, 1024, 1792, 4736, 8192])
+@pytest.mark.parametrize("dim", [8, 56, 112, 224, 448, 768, 896, 1024, 1792, 4736, 8192])
 def test_layernorm(dtype, dim):
     r = np.random.default_rng(dim)
     rows = 37
