@@ -60,9 +60,10 @@ SMALL = {
     # of 32) over 9 key tiles (a partial last tile), dealt 3 / 3 / 3 / 0 to
     # the four waves (one wave without keys)
     "c3b_ksw_18x30": d(C["c3b_hiera_s2"], grid_h=18, grid_w=30, dim_in=896, dim_out=896, heads=16, mlp=3584),
-    # the same split on pooled queries: 2048 tokens pooled to 512 (4 query
-    # tiles x 16 heads) attending to all 2048
-    "c3b_ksw_pool": d(C["c3b_hiera_s2"], grid_h=32, grid_w=64, dim_in=448, dim_out=896, heads=16, mlp=3584,
+    # pooled queries split four ways over workgroups (2048 keys: too many
+    # for the in-workgroup split) and combined: 2048 tokens pooled to 512
+    # (4 query tiles x 16 heads) attending to all 2048
+    "c3b_pool_split4": d(C["c3b_hiera_s2"], grid_h=32, grid_w=64, dim_in=448, dim_out=896, heads=16, mlp=3584,
                       q_stride=4),
     # a Hiera stage-3 block (256 tokens, D 896): qkv (with V^T) and fc1 on
     # 32x64 K-split tiles, the projections on 32x32 ones, attention split

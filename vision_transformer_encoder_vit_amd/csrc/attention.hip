@@ -1108,11 +1108,15 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
                             (int64_t)a.batch * a.tokens_in * a.ld_qkv))
       return hipErrorInvalidValue;
     if constexpr (std::is_same<T, bf16>::value) {
-      // a split of 4 (64-85 query tiles) or 2 becomes a split among the
-      // four waves of each workgroup (128 KB of LDS, one per CU): no
-      // partials and no combine launch (Hiera 1024-token blocks: 256
-      // workgroups; 256-token blocks: 128)
-      if (p.splits == 4 || p.splits == 2) {
+      // a split of 4 (64-85 query tiles) or 2 over at most 16 key tiles
+      // becomes a split among the four waves of each workgroup (128 KB of
+      // LDS, one per CU): no partials and no combine launch (Hiera
+      // 1024-token blocks: 256 workgroups; 256-token blocks: 128). Each
+      // wave loads its own K / V^T tiles, four times the LDS fill of a
+      // shared tile, so longer windows (the 4096 keys of the pooled
+      // stage-2 transition: 35.8 us against 29 + 3.7 for the combine) keep
+      // the split over workgroups.
+      if ((p.splits == 4 || p.splits == 2) && p.n_kv <= 16 * 64) {
         if (a.mode == ATTN_SPATIAL) return attn32_go<ATTN_NW, ATTN_QB, ATTN_SPATIAL, false, true>(p, a.batch, s, ev);
         return pool ? attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, true, true>(p, a.batch, s, ev)
                     : attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, false, true>(p, a.batch, s, ev);
