@@ -69,6 +69,11 @@ SMALL = {
     # 32x64 K-split tiles, the projections on 32x32 ones, attention split
     # over two workgroups and combined
     "c3b_s3_16x16": d(C["c3b_hiera_s2"], grid_h=16, grid_w=16, dim_in=896, dim_out=896, heads=16, mlp=3584),
+    # spatial 16x16 windows with head dim 40 (4 windows x 2 query tiles x 4
+    # heads): the in-workgroup split of the keys inside each window, RoPE on
+    # the window raster
+    "c5w_d160_ksw": d(C["c5w_sam3_win"], grid_h=32, grid_w=32, win_h=16, win_w=16, dim_in=160, dim_out=160,
+                      heads=4, mlp=640),
 }
 
 
