@@ -166,12 +166,15 @@ def test_peaked_softmax_bf16():
     gu.check("peaked:y", gu.to64(y), ref["y"], spec)
 
 
-@pytest.mark.parametrize("name", ["c5w_48x48", "c5g_18x22", "c5g_10x20_split"])
+@pytest.mark.parametrize("name", ["c5w_48x48", "c5g_18x22", "c5g_10x20_split", "c3b_12x12", "c3b_ksw_18x30",
+                                  "c5w_d160_ksw", "c3b_pool_split4"])
 def test_attention_range_fallback(name, monkeypatch):
-    # the head_dim-64 attention takes exp2 of the scaled scores without a
-    # running maximum and re-runs a window with the maximum subtracted when a
-    # row sum leaves its band; a band of width 0 sends every window through
-    # that second pass, which must match the oracle on its own
+    # both large-window attention kernels take exp2 of the scaled scores
+    # without a running maximum and re-run a window with the maximum
+    # subtracted when a row sum leaves its band; a band of width 0 sends
+    # every window through that second pass, which must match the oracle on
+    # its own (head dim 64; head dims 56 and 40 with the keys split inside
+    # the workgroup, over workgroups with pooled queries, or not at all)
     monkeypatch.setenv("VIT_ATTN_RANGE_LOG2", "0")
     spec = SMALL[name]
     print("case", name, flush=True)

@@ -61,7 +61,18 @@ struct AttnParams {
   int64_t batch_rows;  // B * tokens_out
   float* part_o;
   float* part_ml;
+  float l_lo, l_hi;  // large-window kernel: the band a row sum must fall in (2^-64, 2^64)
 };
+
+// The row-sum band of the softmax passes without a running maximum.
+// VIT_ATTN_RANGE_LOG2 (test hook, default 64) narrows it; 0 sends every
+// window through the pass with the running maximum.
+static void attn_band(float& lo, float& hi) {
+  int range = 64;
+  if (const char* env = std::getenv("VIT_ATTN_RANGE_LOG2")) range = std::max(0, std::min(64, std::atoi(env)));
+  lo = std::ldexp(1.0f, -range);
+  hi = range == 0 ? 0.f : std::ldexp(1.0f, range);
+}
 
 __device__ __forceinline__ int window_token(int mode, int w, int i, int n_windows, int grid_w, int win_h,
                                             int win_w) {
@@ -468,7 +479,6 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   for (int j = 0; j < LOADS; ++j) {
     const int row = (grp0 + j) * 8 + lane / 8;
     kkey[j] = key_of_row(row);
-    kcur[j].init(t0 * KT + kkey[j], wwx);
     // chunks past head_dim read neighbouring finite values (Q is zero there)
     kchunk[j] = min(((lane & 7) ^ kswz(row)) * 8, 2 * D - head * hd - 8) + D + head * hd;
   }
@@ -485,9 +495,16 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   for (int j = 0; j < LOADS; ++j) {
     const int row = (grp0 + j) * 8 + lane / 8;
     vpos[j] = ((lane & 7) ^ kswz(row)) * 8;
-    vcur[j].init(t0 * KT + vpos[j], wwx);
     vrow_off[j] = min(row, hd - 1) * p.tokens_in;
   }
+  // the cursors at tile t0 (again for the fallback pass)
+  auto cursors_at_start = [&]() {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      kcur[j].init(t0 * KT + kkey[j], wwx);
+      vcur[j].init(t0 * KT + vpos[j], wwx);
+    }
+  };
   auto issue = [&](int kt) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -507,103 +524,145 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   };
 
   f32x16 acc_o[QB][2];  // [qb][db]: O^T[d = 32db + 8(r/4) + 4h + r%4][q]
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < 2; ++db) acc_o[qb][db] = f32x16{};
   float m_run[QB], l_part[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -1e30f;
-    l_part[qb] = 0.f;
-  }
   const float c = p.scale_log2;
+  const bf16x2_t ones = {(bf16)1.f, (bf16)1.f};
 
-  if (t0 < t1) issue(t0);
-  for (int kt = t0; kt < t1; ++kt) {
-    const int buf = kt & 1;
-    // this wave's loads of tile kt have landed; after the barrier every
-    // wave's have, and every wave is done with the buffer refilled next
-    // (KSW: the buffers are the wave's own, and the waves' tile counts
-    // differ, so no barrier)
-    __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
-    if (!KSW) __syncthreads();
-    if (kt + 1 < t1) issue(kt + 1);
-    f32x16 sacc[QB][2];  // [qb][kb]
+  // One pass over tiles t0 .. t1-1. MF (first pass): softmax without a
+  // running maximum, P = 2^(c s) straight from the scores, the row sums
+  // from the bf16 P (m = 0 for the partials and the merge); a row whose sum
+  // leaves the band [2^-64, 2^64] (scores too large or too small for that)
+  // sends its wave, or with shared tiles its workgroup, through the pass
+  // again with the online maximum (m_run subtracted, O and l rescaled as it
+  // grows).
+  auto tile_pass = [&](auto mf_tag) {
+    constexpr bool MF = decltype(mf_tag)::value;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[qb][kb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + fr;
-        const u32x4 kfr = ld16(&Ks[wb][buf][row * 64 + ((ks * 2 + h) ^ kswz(row)) * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfr),
-                                                                __builtin_bit_cast(bf16x8, qf[qb][ks]), sacc[qb][kb], 0, 0, 0);
-      }
+      for (int db = 0; db < 2; ++db) acc_o[qb][db] = f32x16{};
+      m_run[qb] = MF ? 0.f : -1e30f;
+      l_part[qb] = 0.f;
     }
-    const int kv_left = p.n_kv - kt * KT;
-    if (kv_left < KT) {  // uniform: only the last tile of a ragged window
+    cursors_at_start();
+    if (t0 < t1) issue(t0);
+    for (int kt = t0; kt < t1; ++kt) {
+      const int buf = kt & 1;
+      // this wave's loads of tile kt have landed; after the barrier every
+      // wave's have, and every wave is done with the buffer refilled next
+      // (KSW: the buffers are the wave's own, and the waves' tile counts
+      // differ, so no barrier)
+      __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
+      if (!KSW) __syncthreads();
+      if (kt + 1 < t1) issue(kt + 1);
+      f32x16 sacc[QB][2];  // [qb][kb]
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) sacc[qb][kb] = f32x16{};
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key_of_row(kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) >= kv_left) sacc[qb][kb][r] = -1e30f;
-    }
-    u32x4 pf[QB][2][2];  // [qb][kb][s]: bf16 P for MFMA k-step s of key block kb
-    float alpha[QB];
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(sacc[qb][0][0], sacc[qb][0][1]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = kb * 32 + fr;
+          const u32x4 kfr = ld16(&Ks[wb][buf][row * 64 + ((ks * 2 + h) ^ kswz(row)) * 8]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfr),
+                                                                  __builtin_bit_cast(bf16x8, qf[qb][ks]), sacc[qb][kb], 0, 0, 0);
+        }
+      }
+      const int kv_left = p.n_kv - kt * KT;
+      if (kv_left < KT) {  // uniform: only the last tile of a ragged window
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (key_of_row(kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) >= kv_left) sacc[qb][kb][r] = -1e30f;
+      }
+      u32x4 pf[QB][2][2];  // [qb][kb][s]: bf16 P for MFMA k-step s of key block kb
+      if constexpr (MF) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              bf16x8 pv;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) pv[e] = (bf16)__builtin_amdgcn_exp2f(sacc[qb][kb][8 * s + e] * c);
+              pf[qb][kb][s] = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const bf16x2_t pr = {pv[2 * e], pv[2 * e + 1]};
+                l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_part[qb], false);
+              }
+            }
+      } else {
+        float alpha[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float mx = fmaxf(sacc[qb][0][0], sacc[qb][0][1]);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
+          const float m_new = fmaxf(m_run[qb], halves_max(mx));
+          alpha[qb] = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
+          m_run[qb] = m_new;
+          const float mc = m_new * c;
+          float ls = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              bf16x8 pv;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][8 * s + e], c, -mc));
+                ls += pe;
+                pv[e] = (bf16)pe;
+              }
+              pf[qb][kb][s] = __builtin_bit_cast(u32x4, pv);
+            }
+          }
+          l_part[qb] = l_part[qb] * alpha[qb] + ls;
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int db = 0; db < 2; ++db) acc_o[qb][db] = acc_o[qb][db] * alpha[qb];
+      }
+      // O^T += V^T P^T: k-step s of key block kb covers keys 32kb + 16s + 8h + 0..7
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
-      const float m_new = fmaxf(m_run[qb], halves_max(mx));
-      alpha[qb] = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
-      m_run[qb] = m_new;
-      const float mc = m_new * c;
-      float ls = 0.f;
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+          for (int db = 0; db < 2; ++db) {
+            const int row = db * 32 + fr;
+            const u32x4 vf = ld16(&Vs[wb][buf][row * 64 + ((4 * kb + 2 * s + h) ^ kswz(row)) * 8]);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          bf16x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][8 * s + e], c, -mc));
-            ls += pe;
-            pv[e] = (bf16)pe;
+            for (int qb = 0; qb < QB; ++qb)
+              acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
+                                                                     __builtin_bit_cast(bf16x8, pf[qb][kb][s]), acc_o[qb][db], 0, 0, 0);
           }
-          pf[qb][kb][s] = __builtin_bit_cast(u32x4, pv);
-        }
-      }
-      l_part[qb] = l_part[qb] * alpha[qb] + ls;
     }
+  };
+  tile_pass(std::integral_constant<bool, true>{});
+  {
+    bool out = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int db = 0; db < 2; ++db) acc_o[qb][db] = acc_o[qb][db] * alpha[qb];
-    // O^T += V^T P^T: k-step s of key block kb covers keys 32kb + 16s + 8h + 0..7
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int row = db * 32 + fr;
-          const u32x4 vf = ld16(&Vs[wb][buf][row * 64 + ((4 * kb + 2 * s + h) ^ kswz(row)) * 8]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            acc_o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
-                                                                   __builtin_bit_cast(bf16x8, pf[qb][kb][s]), acc_o[qb][db], 0, 0, 0);
-        }
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
+      out |= qrow_out[qb] >= 0 && !(l >= p.l_lo && l <= p.l_hi);
+    }
+    // KSW: the wave's own keys, so its own decision; shared tiles: the
+    // workgroup's (uniform, and a barrier before the tiles are refilled)
+    const bool again = KSW ? __any(out) : __syncthreads_or(out);
+    if (again) tile_pass(std::integral_constant<bool, false>{});
   }
 
   if constexpr (KSW) {
@@ -1030,12 +1089,7 @@ static hipError_t attn_hm_go(const AttnArgs& a, hipStream_t s, StageEvents ev) {
   p.win_h = a.win_h;
   p.win_w = a.win_w;
   p.tokens_per_frame = a.tokens_in;
-  // VIT_ATTN_RANGE_LOG2 (test hook, default 64) narrows the band; 0 sends
-  // every window through the pass with the running maximum
-  int range = 64;
-  if (const char* env = std::getenv("VIT_ATTN_RANGE_LOG2")) range = std::max(0, std::min(64, std::atoi(env)));
-  p.l_lo = std::ldexp(1.0f, -range);
-  p.l_hi = range == 0 ? 0.f : std::ldexp(1.0f, range);
+  attn_band(p.l_lo, p.l_hi);
   constexpr int NW = 4;
   const int q_tiles = (p.n + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = (int64_t)p.groups * q_tiles;
@@ -1095,6 +1149,7 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
     return attn_hm_go(a, s, ev);
   }
   p.vt = (const T*)a.vt;
+  attn_band(p.l_lo, p.l_hi);
   p.splits = 1;
   p.batch_rows = 0;
   p.part_o = a.part_o;
