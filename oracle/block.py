@@ -32,8 +32,14 @@ at position 0, relative-position property; the block's RoPE step against a
 pure-Python block that turns only the q and k parts (spatial and global), v
 equal to the plain projection, and a position-independent rotation dropping
 out of attention exactly; pool groups and window maps against the spatial
-definitions. The whole-block output is parity unpinned
-beyond these: no page prints a block output for a known input.
+definitions. The whole block, every seam, is pinned against pure-Python loop
+blocks (``brute``) on tiny inputs: mask-unit windows with fused qkv and
+erf-GELU, global windows with separate q/k/v and tanh-GELU, spatial and
+global windows with RoPE, and a stage transition with the pooled residual
+and pooled queries; planted mistakes in the composition (a dropped residual,
+LN2 reading the wrong tensor, RoPE on v) fail those comparisons
+(``tests/test_oracle_mutations.py``). No page prints a block output for a
+known input, so brute force on tiny inputs is the pin of the composition.
 """
 import numpy as np
 from scipy.special import erf as _erf

@@ -263,9 +263,56 @@ MUTATIONS += [
 ]
 
 
+# ---------------------------------------------------------- block composition
+# A block with one step of the composition wired wrong (the tiny mask-unit
+# configuration of the brute-force pin: fused qkv, no RoPE, q_stride 1).
+def _block_wired(kind):
+    def fwd(x, w, spec):
+        assert spec.get("qkv", "fused") == "fused" and not spec.get("rope") and spec["q_stride"] == 1
+        f64 = lambda a: np.asarray(a, dtype=np.float64)
+        x = f64(x)
+        D, heads = spec["dim_out"], spec["heads"]
+        hd = D // heads
+        scale = spec.get("scale") or hd ** -0.5
+        gelu = ob.gelu_erf if spec["gelu"] == "erf" else ob.gelu_tanh
+        wins = ob.windows_for(spec)
+        seams = {k: [] for k in ("h", "qkv", "r", "ctx", "attn_branch", "x1", "h2", "u", "mlp_branch", "y")}
+        for b in range(x.shape[0]):
+            xb = x[b]
+            h = xb if kind == "ln1 skipped" else ob.layer_norm(xb, f64(w["ln1_g"]), f64(w["ln1_b"]), spec["eps"])
+            qkv = ob.linear(h, w["qkv_w"], f64(w["qkv_b"]))
+            q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
+            ctx = ob.attention(q, k, v, wins, heads, scale)
+            attn_branch = ob.linear(ctx, w["o_w"], f64(w["o_b"]))
+            x1 = attn_branch if kind == "attention residual dropped" else xb + attn_branch
+            h2 = ob.layer_norm(xb if kind == "ln2 reads x" else x1, f64(w["ln2_g"]), f64(w["ln2_b"]), spec["eps"])
+            pre = ob.linear(h2, w["fc1_w"], f64(w["fc1_b"]))
+            u = pre if kind == "gelu skipped" else gelu(pre)
+            mlp_branch = ob.linear(u, w["fc2_w"], f64(w["fc2_b"]))
+            y = (xb if kind == "mlp residual from x" else x1) + mlp_branch
+            for name, val in (("h", h), ("qkv", qkv), ("r", xb), ("ctx", ctx), ("attn_branch", attn_branch),
+                              ("x1", x1), ("h2", h2), ("u", u), ("mlp_branch", mlp_branch), ("y", y)):
+                seams[name].append(val)
+        return {k: np.stack(v) for k, v in seams.items()}
+    return fwd
+
+
+MUTATIONS += [
+    ("block: " + kind, ob, "block_forward", _block_wired(kind), pins.test_block_vs_brute_on_tiny_config)
+    for kind in ("ln1 skipped", "attention residual dropped", "ln2 reads x", "gelu skipped", "mlp residual from x")
+]
+
+
 @pytest.mark.parametrize("label,mod,attr,bad,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(monkeypatch, label, mod, attr, bad, pin):
     monkeypatch.setattr(mod, attr, bad)
     with pytest.raises((AssertionError, FloatingPointError)):
         with np.errstate(over="ignore", invalid="ignore"):
             pin()
+
+
+def test_block_rewired_without_a_mistake_passes(monkeypatch):
+    # the harness above, with every step wired as the pages have it, passes
+    # the same pin: the planted mistakes, not the harness, make it fail
+    monkeypatch.setattr(ob, "block_forward", _block_wired("none"))
+    pins.test_block_vs_brute_on_tiny_config()
