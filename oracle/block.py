@@ -1,4 +1,5 @@
-"""Pre-LayerNorm ViT encoder block, float64 numpy oracle (test infrastructure).
+"""Pre-LayerNorm ViT encoder block, float64 numpy oracle (test infrastructure:
+only tests/, the smoke check and the benchmark's CPU baseline may import it).
 
 What the block computes, in the order the pages give it:
 

@@ -1,5 +1,5 @@
 """Pure-Python loop versions of the block's steps, for tiny shapes only
-(test infrastructure; pins for ``oracle.block``).
+(test infrastructure, imported by tests/ only; pins for ``oracle.block``).
 
 No numpy arithmetic here: every sum, product, maximum and exponential is a
 Python float operation on one scalar, so an indexing or transposition slip in

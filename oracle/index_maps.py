@@ -1,4 +1,6 @@
-"""Token orders and window membership for the encoder block (oracle side).
+"""Token orders and window membership for the encoder block (oracle side; test
+infrastructure: only tests/, the smoke check and the benchmark's CPU baseline
+may import it).
 
 Integer index arithmetic only. Every map here is compared bit-exactly with
 the HIP permute kernels and with the window addressing of the HIP attention
