@@ -74,6 +74,10 @@ SMALL = {
     # the window raster
     "c5w_d160_ksw": d(C["c5w_sam3_win"], grid_h=32, grid_w=32, win_h=16, win_w=16, dim_in=160, dim_out=160,
                       heads=4, mlp=640),
+    # two frames of 480 tokens (2 x 4 query tiles x 8 heads: the four-way
+    # in-workgroup split with frames kept apart, a partial last key tile;
+    # 32x32 K-split projections)
+    "c3b_ksw_b2": d(C["c3b_hiera_s2"], batch=2, grid_h=16, grid_w=30),
 }
 
 
