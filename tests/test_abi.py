@@ -330,3 +330,27 @@ def test_second_hip_runtime_fails_loudly():
             "    print('REFUSED', e); raise SystemExit(0)\nraise SystemExit(3)\n") % (other[0], ROOT)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "REFUSED" in r.stdout and "HIP runtime" in r.stdout, r.stdout + r.stderr
+
+
+def test_workspace_has_no_partials_for_a_split_inside_the_workgroup():
+    # the 1024-token Hiera stage-2 block splits its keys four ways among the
+    # waves of one workgroup: its workspace is the block's activations (h,
+    # qkv, ctx, x1, h2, u and V^T, bf16), with no fp32 split partials
+    spec = synth.CONFIGS["c3b_hiera_s2"]
+    m, d, f = 1024, 448, 1792
+    acts = 2 * m * (d + 3 * d + d + d + d + f + d)
+    p = vb.Plan(vb.desc_from_spec(spec))
+    try:
+        assert p.workspace_bytes == acts
+    finally:
+        p.close()
+    # a pooled 4096-key window splits over workgroups: fp32 partials (O and
+    # the row max / sum per head) for each of its splits come on top
+    pooled = synth.derive(spec, grid_h=64, grid_w=64, dim_in=448, dim_out=448, q_stride=4)
+    p = vb.Plan(vb.desc_from_spec(pooled))
+    try:
+        mi, mo = 4096, 1024
+        acts = 2 * (mi * (d + 3 * d + d) + mo * (d + d + d + d + f) + mi * d)
+        assert p.workspace_bytes > acts + 2 * 4 * mo * d
+    finally:
+        p.close()

@@ -1156,7 +1156,8 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
   p.part_ml = a.part_ml;
   if (a.vt) {
     p.splits = attention_splits(a.batch, p.windows, p.n_q, p.n_kv, a.heads);
-    if (p.splits > 1 && (!a.part_o || !a.part_ml || a.head_dim % 4)) return hipErrorInvalidValue;
+    const bool ksw = attention_split_in_workgroup(p.splits, p.n_kv);
+    if (p.splits > 1 && (a.head_dim % 4 || (!ksw && (!a.part_o || !a.part_ml)))) return hipErrorInvalidValue;
     // large global or spatial windows: 32x32 MFMA kernel on K and V^T
     if (!std::is_same<T, bf16>::value ||
         !attention_takes_vt(DType::BF16, a.mode, p.n_q, a.head_dim, a.win_w, a.tokens_in,
@@ -1171,7 +1172,7 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
       // shared tile, so longer windows (the 4096 keys of the pooled
       // stage-2 transition: 35.8 us against 29 + 3.7 for the combine) keep
       // the split over workgroups.
-      if ((p.splits == 4 || p.splits == 2) && p.n_kv <= 16 * 64) {
+      if (ksw) {
         if (a.mode == ATTN_SPATIAL) return attn32_go<ATTN_NW, ATTN_QB, ATTN_SPATIAL, false, true>(p, a.batch, s, ev);
         return pool ? attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, true, true>(p, a.batch, s, ev)
                     : attn32_go<ATTN_NW, ATTN_QB, ATTN_GLOBAL, false, true>(p, a.batch, s, ev);

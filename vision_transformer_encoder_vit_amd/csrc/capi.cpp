@@ -59,6 +59,7 @@ struct vit_block_plan {
   size_t off_h, off_qkv, off_rp, off_r, off_ctx, off_x1, off_h2, off_u, off_vt, off_po, off_pml, off_qh, off_kh,
       ws_bytes;
   int attn_splits;       // key splits of the large-window attention (1: none)
+  bool split_partials;   // ... over workgroups, through fp32 partials (off_po, off_pml)
   bool fused_mask_unit;  // whole block per window in one kernel (forward without seams)
   bool attn_vt;          // the large-window attention kernel runs on V^T (workspace off_vt)
   bool vt_in_gemm;       // ... written by the qkv projection's epilogue (else a transpose kernel)
@@ -183,8 +184,10 @@ VIT_API vit_status vit_block_create(const vit_block_desc* desc, vit_block_t* out
   }
   // fp32 partials (sizes in elements of esize bytes, rounded up)
   const int64_t fp32_cols = 4 / p->esize;
-  p->off_po = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, d.dim_out * fp32_cols) : 0;
-  p->off_pml = p->attn_splits > 1 ? take((int64_t)p->attn_splits * p->m_out, 2LL * d.heads * fp32_cols) : 0;
+  const int64_t n_kv_attn = d.attn_mode == VIT_ATTN_SPATIAL ? (int64_t)d.win_h * d.win_w : p->n_in;
+  p->split_partials = p->attn_splits > 1 && !vit::attention_split_in_workgroup(p->attn_splits, n_kv_attn);
+  p->off_po = p->split_partials ? take((int64_t)p->attn_splits * p->m_out, d.dim_out * fp32_cols) : 0;
+  p->off_pml = p->split_partials ? take((int64_t)p->attn_splits * p->m_out, 2LL * d.heads * fp32_cols) : 0;
   if (d.weight_format == VIT_WEIGHTS_Q8_ROW) {
     const int64_t Di = d.dim_in, Do = d.dim_out, F = d.mlp_hidden;
     p->off_cres = d.q_stride == 4 ? take(Do, Di) : 0;
@@ -605,7 +608,7 @@ static vit_status forward_impl(vit_block_t plan, const vit_block_weights* w, con
     a.qh = base + P.off_qh;
     a.kh = base + P.off_kh;
   }
-  if (P.attn_splits > 1) {
+  if (P.split_partials) {
     a.part_o = reinterpret_cast<float*>(base + P.off_po);
     a.part_ml = reinterpret_cast<float*>(base + P.off_pml);
   }

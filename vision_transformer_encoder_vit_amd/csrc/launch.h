@@ -170,6 +170,13 @@ inline int attention_splits(int64_t batch, int64_t windows, int64_t n_q, int64_t
   return s >= 2 ? (int)s : 1;
 }
 
+// A split of 2 or 4 over at most 1024 keys runs among the four waves of one
+// workgroup (no fp32 partials, no combine launch); other splits write
+// partials (AttnArgs::part_o, part_ml) that a combine launch merges.
+inline bool attention_split_in_workgroup(int splits, int64_t n_kv) {
+  return (splits == 2 || splits == 4) && n_kv <= 16 * 64;
+}
+
 // Large windows with head_dim 64 and no query pool: the head-major kernel
 // (operands in window order from the qkv projection; no key split).
 inline bool attention_takes_hm(DType dt, int mode, int64_t n_q, int head_dim, int win_w, int64_t tokens_in,
