@@ -45,6 +45,8 @@ def describe(spec):
         extra.append("separate q/k/v")
     if spec.get("weights") == "q8_row":
         extra.append("q8_row int8 weights")
+    if spec.get("qk_gain", 1.0) != 1.0:
+        extra.append("query/key weights x%g" % spec["qk_gain"])
     return "%s: %d x %dx%d tokens (%d), D %d, %d heads x %d, %s, MLP %d %s-GELU%s" % (
         spec["name"], spec["batch"], spec["grid_h"], spec["grid_w"], n, spec["dim_out"], spec["heads"],
         spec["dim_out"] // spec["heads"], mode, spec["mlp"], spec["gelu"],
@@ -118,7 +120,8 @@ def run(spec, steps, warmup, with_cpu):
 
     dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
     q8 = spec.get("weights") == "q8_row"
-    inp = synth.make_q8_inputs(spec, seed=0) if q8 else synth.make_inputs(spec, seed=0)
+    gain = spec.get("qk_gain", 1.0)
+    inp = synth.make_q8_inputs(spec, seed=0, qk_gain=gain) if q8 else synth.make_inputs(spec, seed=0, qk_gain=gain)
     dev = {}
     for k, a in inp.items():
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -417,6 +420,9 @@ def main():
                          "post_layernorm) instead of one block")
     ap.add_argument("--weights", choices=["bf16", "q8_row"], default="bf16",
                     help="weight matrices in bf16, or as q8_row int8 payloads with float16 row scales")
+    ap.add_argument("--qk-gain", type=float, default=1.0,
+                    help="scale the query and key weights (block workloads): 16 gives the row maxima of "
+                         "trained weights (scores of ~100-200), which take the running-maximum softmax")
     ap.add_argument("--rowops", action="store_true",
                     help="only time LayerNorm, unroll, reroll and pool4 on HBM-resident working sets")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -448,7 +454,9 @@ def main():
         spec = synth.CONFIGS[n]
         if args.weights == "q8_row":
             spec = dict(spec, weights="q8_row")
-        with_cpu = not args.no_cpu_baseline and n == names[0] and args.weights == "bf16"
+        if args.qk_gain != 1.0:
+            spec = dict(spec, qk_gain=args.qk_gain)
+        with_cpu = not args.no_cpu_baseline and n == names[0] and args.weights == "bf16" and args.qk_gain == 1.0
         print(json.dumps(run(spec, args.steps, args.warmup, with_cpu)), flush=True)
 
 

@@ -190,6 +190,89 @@ def test_attention_range_fallback(name, monkeypatch):
         gu.check(name + " (max pass):" + k, gu.to64(got), ref[k], spec)
 
 
+HM_CASES = ["c5w_48x48", "c5g_18x22", "c5g_10x20_split"]  # head dim 64: the head-major kernel
+
+
+def _scores_log2(ref, spec, frame=0):
+    """Per head, the scaled scores of the oracle's post-RoPE q and k in log2
+    units (c*s, the units the head-dim-64 kernel compares): a list over
+    windows of [heads, n, n] arrays, rows = queries in window order."""
+    D, H = spec["dim_out"], spec["heads"]
+    hd = D // H
+    scale = spec["scale"] if spec["scale"] is not None else 1.0 / np.sqrt(hd)
+    if spec["mode"] == "spatial":
+        wins = im.spatial_windows(spec["grid_h"], spec["grid_w"], spec["win_h"], spec["win_w"])
+    else:
+        wins = [np.arange(spec["grid_h"] * spec["grid_w"])]
+    out = []
+    for t in wins:
+        q = ref["qkv"][frame, t, :D].reshape(len(t), H, hd).transpose(1, 0, 2)
+        k = ref["qkv"][frame, t, D:2 * D].reshape(len(t), H, hd).transpose(1, 0, 2)
+        out.append(q @ k.transpose(0, 2, 1) * scale * np.log2(np.e))
+    return out, wins
+
+
+@pytest.mark.parametrize("name", HM_CASES)
+def test_attention_running_max_from_tile0(name, monkeypatch):
+    # every wave takes the running-maximum pass from its tile-0 scores (the
+    # path trained weights take: row maxima of c*s far outside the band)
+    monkeypatch.setenv("VIT_ATTN_TILE0_BAND", "-1")
+    spec = SMALL[name]
+    print("case", name, flush=True)
+    inp = synth.make_inputs(spec, seed=5)
+    ref = ob.block_forward(inp["x"], inp, spec)
+    y, seams = gu.run_block(spec, gu.to_device(inp, spec))
+    for k in ("ctx", "attn_branch", "x1", "y"):
+        got = y if k == "y" else seams[k]
+        gu.check(name + " (running max from tile 0):" + k, gu.to64(got), ref[k], spec)
+
+
+@pytest.mark.parametrize("name", HM_CASES)
+def test_attention_passes_mixed_in_workgroup(name, monkeypatch):
+    # a tile-0 band at the 99.5th percentile of the rows' tile-0 maxima: a
+    # wave of 32 rows exceeds it with probability ~15 %, so workgroups mix
+    # waves on the two passes (one barrier per tile on both)
+    spec = SMALL[name]
+    print("case", name, flush=True)
+    inp = synth.make_inputs(spec, seed=6)
+    ref = ob.block_forward(inp["x"], inp, spec)
+    sc, _ = _scores_log2(ref, spec)
+    m0 = np.concatenate([s[:, :, :64].max(axis=2).ravel() for s in sc])
+    monkeypatch.setenv("VIT_ATTN_TILE0_BAND", "%.6f" % np.percentile(m0, 99.5))
+    y, seams = gu.run_block(spec, gu.to_device(inp, spec))
+    for k in ("ctx", "y"):
+        got = y if k == "y" else seams[k]
+        gu.check(name + " (mixed passes):" + k, gu.to64(got), ref[k], spec)
+
+
+def test_trained_range_scores_bf16():
+    # scores as large as trained SAM3 weights give (row maxima ~75, up to
+    # ~140) on the bf16 path. The bf16 q and k move a score by ~|s| 2^-8,
+    # which decides between near-tied keys, so ctx is compared per (query,
+    # head) where the two largest scores are at least 6 apart (the runner-up
+    # then weighs at most e^-6), y on the rows where that holds in every
+    # head; every output must be finite.
+    spec = SMALL["c5g_18x22"]
+    inp = synth.make_inputs(spec, seed=7, qk_gain=16.0)
+    ref = ob.block_forward(inp["x"], inp, spec)
+    sc, _ = _scores_log2(ref, spec)
+    s = sc[0] / np.log2(np.e)  # natural units, [heads, n, n]
+    assert np.abs(s).max() > 100 and np.median(s.max(axis=2)) > 50
+    top2 = np.sort(s, axis=2)[:, :, -2:]
+    ok = (top2[:, :, 1] - top2[:, :, 0]) >= 6.0  # [heads, n]
+    assert ok.mean() > 0.3 and ok.all(axis=0).sum() >= 16, (ok.mean(), ok.all(axis=0).sum())
+    y, seams = gu.run_block(spec, gu.to_device(inp, spec))
+    ctx, yy = gu.to64(seams["ctx"]), gu.to64(y)
+    assert np.all(np.isfinite(ctx)) and np.all(np.isfinite(yy))
+    H, hd = spec["heads"], spec["dim_out"] // spec["heads"]
+    for hh in range(H):
+        rows = np.where(ok[hh])[0]
+        cols = slice(hh * hd, (hh + 1) * hd)
+        gu.check("trained-range:ctx head %d" % hh, ctx[:, rows, cols], ref["ctx"][:, rows, cols], spec)
+    rows = np.where(ok.all(axis=0))[0]
+    gu.check("trained-range:y", yy[:, rows], ref["y"][:, rows], spec)
+
+
 def test_rerun_is_bitwise_identical():
     spec = C["c5w_sam3_win"]
     dev = gu.to_device(synth.make_inputs(spec, seed=0), spec)

@@ -74,6 +74,15 @@ static void attn_band(float& lo, float& hi) {
   hi = range == 0 ? 0.f : std::ldexp(1.0f, range);
 }
 
+// The band of tile 0's row maxima (c*s units) inside which the head-dim-64
+// kernel runs the pass without a running maximum: 16, or VIT_ATTN_TILE0_BAND
+// (test hook; a negative value sends every window to the running-maximum
+// pass from tile 0).
+static float attn_tile0_band() {
+  const char* env = std::getenv("VIT_ATTN_TILE0_BAND");
+  return env ? (float)std::atof(env) : 16.f;
+}
+
 __device__ __forceinline__ int window_token(int mode, int w, int i, int n_windows, int grid_w, int win_h,
                                             int win_w) {
   if (mode == ATTN_MASK_UNIT) return w + i * n_windows;
@@ -848,6 +857,12 @@ static hipError_t attn32_go(AttnParams<bf16> p, int batch, hipStream_t s, StageE
 // overflows and the terms that matter stay normal floats. The row sums come
 // from the bf16 P that multiply V (dot products with (1, 1) over packed
 // pairs).
+// Trained weights give rows whose largest c*s is in the hundreds, far out
+// of that band, so each wave first takes tile 0's scores: if some row's
+// maximum over them lies outside [-m_band, m_band], the wave runs the
+// running-maximum pass at once (from those scores) instead of a pass that
+// would be discarded. (Decided per wave, with a ballot: a decision shared
+// by the workgroup, through a barrier, cost 3 % on the small-score path.)
 // ---------------------------------------------------------------------------
 struct AttnHmParams {
   const bf16* q;
@@ -860,6 +875,7 @@ struct AttnHmParams {
   int windows;           // per frame
   int spatial, grid_w, win_h, win_w, tokens_per_frame;
   float l_lo, l_hi;      // the band a row sum must fall in (2^-64, 2^64)
+  float m_band;          // tile 0's row maxima of c*s outside [-m_band, m_band]: running-maximum pass at once
 };
 
 constexpr uint32_t BUF_WORD3 = 0x00020000;  // raw buffer, 32-bit data, range-checked
@@ -922,6 +938,9 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
     voff[j] = (row * n + ch * 8) * 2;
   }
   const int ntiles = (n + KT - 1) / KT;
+  // the wave index as a scalar: the LDS destinations of the tile loads are
+  // then scalar arithmetic, not vector registers
+  const int waveu = __builtin_amdgcn_readfirstlane(wave);
   // tile kt's K and V^T into one stage's LDS arrays
   auto issue = [&](bf16* kd, bf16* vd, int kt) {
     // bytes from the tile's start to the end of the (frame, window, head)
@@ -929,9 +948,9 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
     const __amdgpu_buffer_rsrc_t kr = buf_rsrc(kg + (int64_t)kt * KT * 64, (n - kt * KT) * 128);
     const __amdgpu_buffer_rsrc_t vr = buf_rsrc(vg + (int64_t)kt * KT, (n * 64 - kt * KT) * 2);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) buf_load_lds16(kr, kd + (wave * LPW + j) * 512, koff[j]);
+    for (int j = 0; j < LPW; ++j) buf_load_lds16(kr, kd + (waveu * LPW + j) * 512, koff[j]);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) buf_load_lds16(vr, vd + (wave * LPW + j) * 512, voff[j]);
+    for (int j = 0; j < LPW; ++j) buf_load_lds16(vr, vd + (waveu * LPW + j) * 512, voff[j]);
   };
 
   f32x16 acc_o[2] = {f32x16{}, f32x16{}};  // O^T[d = 32db + 8(r/4) + 4h + r%4][query]
@@ -1008,22 +1027,75 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // the pass: tile kt in stage kt & 1, tiles taken in pairs so that the
-  // stage of each is known at compile time
+  // Tile 0's scores choose each wave's pass: where some row of the wave has
+  // its maximum over them outside [-m_band, m_band], the running-maximum
+  // pass from these scores, otherwise the pass without a running maximum.
+  // Both run one barrier per tile, so the waves of a workgroup may differ.
   issue(Ks0, Vs0, 0);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    step(Ks0, Vs0, Ks1, Vs1, kt);
-    if (kt + 1 < ntiles) step(Ks1, Vs1, Ks0, Vs0, kt + 1);
+  __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
+  __syncthreads();
+  if (1 < ntiles) issue(Ks1, Vs1, 1);
+  scores(Ks0, 0);
+  float mt0 = -1e30f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt0 = fmaxf(mt0, sacc[kb][r]);
+  mt0 = halves_max(mt0);
+  const bool wide = __builtin_amdgcn_ballot_w64(!(mt0 >= -p.m_band && mt0 <= p.m_band)) != 0;
+  float m = -1e30f;
+  // the running row maximum m subtracted and O, l rescaled as it grows
+  auto rm_softmax_pv = [&](const bf16* vs) {
+    float mt = -1e30f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+    const float m_new = fmaxf(m, halves_max(mt));
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) acc_o[db] *= alpha;
+    l *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] -= m;
+    pv_step(vs);
+  };
+  auto step_rm = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int kt) {
+    __builtin_amdgcn_s_waitcnt(attn_vmcnt(0));
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kn, vn, kt + 1);
+    scores(ks, kt);
+    rm_softmax_pv(vs);
+  };
+  // tile kt in stage kt & 1, tiles after the first taken in pairs so that
+  // the stage of each is known at compile time
+  if (wide) {
+    rm_softmax_pv(Vs0);
+    for (int kt = 1; kt < ntiles; kt += 2) {
+      step_rm(Ks1, Vs1, Ks0, Vs0, kt);
+      if (kt + 1 < ntiles) step_rm(Ks0, Vs0, Ks1, Vs1, kt + 1);
+    }
+  } else {
+    __builtin_amdgcn_s_setprio(2);
+    pv_step(Vs0);
+    __builtin_amdgcn_s_setprio(0);
+    for (int kt = 1; kt < ntiles; kt += 2) {
+      step(Ks1, Vs1, Ks0, Vs0, kt);
+      if (kt + 1 < ntiles) step(Ks0, Vs0, Ks1, Vs1, kt + 1);
+    }
   }
   l += __shfl_xor(l, 32, 64);
+  const bool running_max = __syncthreads_or(!wide && !(l >= p.l_lo && l <= p.l_hi));
 
-  if (__syncthreads_or(!(l >= p.l_lo && l <= p.l_hi))) {
-    // out of range somewhere in the workgroup: the window again, with the
-    // running row maximum m subtracted and O, l rescaled as it grows
+  if (running_max) {
+    // a row of a wave without the running maximum left the band: the whole
+    // workgroup runs the window again from the start, every wave with the
+    // running maximum
     acc_o[0] = f32x16{};
     acc_o[1] = f32x16{};
     l = 0.f;
-    float m = -1e30f;
+    m = -1e30f;
     issue(Ks0, Vs0, 0);
     for (int kt = 0; kt < ntiles; ++kt) {
       const int stage = kt & 1;
@@ -1034,20 +1106,7 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
         else issue(Ks1, Vs1, kt + 1);
       }
       scores(stage ? Ks1 : Ks0, kt);
-      float mt = -1e30f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      const float m_new = fmaxf(m, halves_max(mt));
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) acc_o[db] *= alpha;
-      l *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb] -= m;
-      pv_step(stage ? Vs1 : Vs0);
+      rm_softmax_pv(stage ? Vs1 : Vs0);
     }
     l += __shfl_xor(l, 32, 64);
   }
@@ -1090,6 +1149,7 @@ static hipError_t attn_hm_go(const AttnArgs& a, hipStream_t s, StageEvents ev) {
   p.win_w = a.win_w;
   p.tokens_per_frame = a.tokens_in;
   attn_band(p.l_lo, p.l_hi);
+  p.m_band = attn_tile0_band();
   constexpr int NW = 4;
   const int q_tiles = (p.n + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = (int64_t)p.groups * q_tiles;
