@@ -64,6 +64,29 @@ struct AttnParams {
   float l_lo, l_hi;  // large-window kernel: the band a row sum must fall in (2^-64, 2^64)
 };
 
+// Work-item and workgroup ids and votes from compiler builtins: this file is
+// compiled without IEEE mode, so the device-library versions behind
+// threadIdx, blockIdx, __any and __syncthreads_or (compiled with it) are not
+// inlined; each was a real call, with the registers it may clobber spilled
+// around it.
+__device__ __forceinline__ int wi_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int wg_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+// true in every thread when p holds in some thread of the workgroup of NW
+// waves: one vote per wave through LDS and a barrier (the votes may be
+// written again only after a later barrier)
+template <int NW>
+__device__ __forceinline__ bool wg_any(bool p) {
+  __shared__ int votes[NW];
+  const bool w = wave_any(p);
+  if ((wi_id() & 63) == 0) votes[wi_id() >> 6] = w;
+  __syncthreads();
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) any |= votes[i] != 0;
+  return any;
+}
+
 // The row-sum band of the softmax passes without a running maximum.
 // VIT_ATTN_RANGE_LOG2 (test hook, default 64) narrows it; 0 sends every
 // window through the pass with the running maximum.
@@ -109,10 +132,10 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams<T> p) {
   __shared__ __attribute__((aligned(16))) T Ks[HPW][KT][KROW];
   __shared__ __attribute__((aligned(16))) T Vt[HPW][HDP][VROW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = wi_id(), lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
 
-  int bid = blockIdx.x;
+  int bid = wg_id();
   const int hg = bid % p.head_groups;
   bid /= p.head_groups;
   const int qt = bid % p.q_tiles;
@@ -403,10 +426,10 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NB][2][KT * 64];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[NB][2][64 * KT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = wi_id(), lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, h = lane >> 5;
   const int wb = KSW ? wave : 0;
-  int bid = blockIdx.x;
+  int bid = wg_id();
   const int split = KSW ? 0 : bid % p.splits;  // key split: tiles [t0, t1) of the window
   bid /= KSW ? 1 : p.splits;
   const int head = bid % p.heads;
@@ -514,7 +537,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
       vcur[j].init(t0 * KT + vpos[j], wwx);
     }
   };
-  auto issue = [&](int kt) {
+  auto issue = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       // keys past the window read the last key (masked out of the softmax)
@@ -670,7 +693,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
     }
     // KSW: the wave's own keys, so its own decision; shared tiles: the
     // workgroup's (uniform, and a barrier before the tiles are refilled)
-    const bool again = KSW ? __any(out) : __syncthreads_or(out);
+    const bool again = KSW ? wave_any(out) : wg_any<NW>(out);
     if (again) tile_pass(std::integral_constant<bool, false>{});
   }
 
@@ -775,7 +798,7 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(const float* __r
                                                                 int64_t ld_ctx, int64_t rows, int heads, int hd,
                                                                 int dim, float c) {
   const int q4 = hd / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = (int64_t)wg_id() * 256 + wi_id();
   const int64_t r = idx / (heads * q4);
   if (r >= rows) return;
   const int rem = (int)(idx - r * heads * q4), head = rem / q4, d = (rem - head * q4) * 4;
@@ -906,11 +929,11 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
   __shared__ __attribute__((aligned(1024))) bf16 Ks1[KT * 64];
   __shared__ __attribute__((aligned(1024))) bf16 Vs1[64 * KT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = wi_id(), lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, h = lane >> 5;
   // consecutive workgroups share (frame, window, head): with groups a
   // multiple of 8 all query tiles of a group land on one XCD (its L2)
-  const int g = blockIdx.x % p.groups, qt = blockIdx.x / p.groups;
+  const int g = wg_id() % p.groups, qt = wg_id() / p.groups;
   const int n = p.n;
   const int64_t gbase = (int64_t)g * n * 64;
   const bf16* kg = p.k + gbase;
@@ -1042,7 +1065,7 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt0 = fmaxf(mt0, sacc[kb][r]);
   mt0 = halves_max(mt0);
-  const bool wide = __builtin_amdgcn_ballot_w64(!(mt0 >= -p.m_band && mt0 <= p.m_band)) != 0;
+  const bool wide = wave_any(!(mt0 >= -p.m_band && mt0 <= p.m_band));
   float m = -1e30f;
   // the running row maximum m subtracted and O, l rescaled as it grows
   auto rm_softmax_pv = [&](const bf16* vs) {
@@ -1086,7 +1109,7 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
     }
   }
   l += __shfl_xor(l, 32, 64);
-  const bool running_max = __syncthreads_or(!wide && !(l >= p.l_lo && l <= p.l_hi));
+  const bool running_max = wg_any<NW>(!wide && !(l >= p.l_lo && l <= p.l_hi));
 
   if (running_max) {
     // a row of a wave without the running maximum left the band: the whole
