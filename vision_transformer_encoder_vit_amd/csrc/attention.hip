@@ -1134,14 +1134,20 @@ __global__ __launch_bounds__(64 * NW, 3) void attention_hm_kernel(AttnHmParams p
     l += __shfl_xor(l, 32, 64);
   }
 
-  if (!qvalid) return;
-  // output row of query qi: its token in the frame
+  // the query row again, from scalars and the lane's index: recomputed so
+  // that no register carries it across the passes (with 168 VGPRs in use
+  // it was spilled to scratch, and a kernel with scratch costs more to
+  // dispatch)
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int qo = (qt * NW + waveu) * 32 + (lane_e & 31);
+  if (qo >= n) return;
+  // output row of query qo: its token in the frame
   const int bw = g / p.heads, head = g - bw * p.heads;
   const int b = bw / p.windows, win = bw - b * p.windows;
-  int t = qi;
+  int t = qo;
   if (p.spatial) {
     const int nwx = p.grid_w / p.win_w, wy = win / nwx, wx = win - wy * nwx;
-    const int iy = qi / p.win_w, ix = qi - iy * p.win_w;
+    const int iy = qo / p.win_w, ix = qo - iy * p.win_w;
     t = (wy * p.win_h + iy) * p.grid_w + wx * p.win_w + ix;
   }
   const float inv = 1.0f / l;
