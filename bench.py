@@ -104,7 +104,24 @@ def cpu_baseline(spec, budget_s=20.0, max_runs=3):
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": model, "cpus_available": ncpu,
             "sample": "float64 numpy oracle, one full block forward of frame 0 (%d tokens); median of %d run(s): "
-                      "%s s" % (n, len(runs), ", ".join("%.2f" % r for r in runs))}
+                      "%s s" % (n, len(runs), ", ".join("%.3g" % r for r in runs))}
+
+
+def oracle_timing(names):
+    """The float64 CPU oracle alone: one block forward of frame 0 per workload,
+    median of three runs, once on one BLAS thread and once on all of them.
+    Prints one JSON line per (workload, threads). No GPU work."""
+    from threadpoolctl import threadpool_limits, threadpool_info
+    from vision_transformer_encoder_vit_amd import synth
+    model, ncpu = cpu_model()
+    full = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    for n in names:
+        spec = synth.CONFIGS[n]
+        for threads in (1, full):
+            with threadpool_limits(limits=threads, user_api="blas"):
+                line = cpu_baseline(spec, budget_s=60.0, max_runs=3)
+            print(json.dumps({"workload": n, "threads": threads, "cpu_model": model, "cpus_available": ncpu,
+                              "tokens_per_s": line["value"], "sample": line["sample"]}), flush=True)
 
 
 def run(spec, steps, warmup, with_cpu):
@@ -423,6 +440,8 @@ def main():
     ap.add_argument("--qk-gain", type=float, default=1.0,
                     help="scale the query and key weights (block workloads): 16 gives the row maxima of "
                          "trained weights (scores of ~100-200), which take the running-maximum softmax")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="only time the float64 CPU oracle on C1-C3 (one thread and all threads)")
     ap.add_argument("--rowops", action="store_true",
                     help="only time LayerNorm, unroll, reroll and pool4 on HBM-resident working sets")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -435,6 +454,9 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         ap.error("steps >= 1 and warmup >= 0")
+    if args.oracle_timing:
+        oracle_timing(["c1_tiny_f32", "c2_hiera_s0", "c3a_hiera_trans", "c3b_hiera_s2"])
+        return
     if args.rowops:
         rowops_cold(args.steps)
         return
