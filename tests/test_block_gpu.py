@@ -190,9 +190,10 @@ def test_attention_range_fallback(name, monkeypatch):
         gu.check(name + " (max pass):" + k, gu.to64(got), ref[k], spec)
 
 
-# head dim 64 (the head-major kernel): its first pass chosen from the first
-# key tile's scores
-TILE0_CASES = ["c5w_48x48", "c5g_18x22", "c5g_10x20_split"]
+# the first pass chosen from the first key tile's scores: head dim 64 (the
+# head-major kernel), and head dims 56 / 40 with the keys split among the
+# waves of a workgroup (each wave's own first tile)
+TILE0_CASES = ["c5w_48x48", "c5g_18x22", "c5g_10x20_split", "c3b_ksw_18x30", "c5w_d160_ksw"]
 
 
 def _scores_log2(ref, spec, frame=0):
@@ -250,9 +251,9 @@ def test_attention_passes_mixed_in_workgroup(name, monkeypatch):
 @pytest.mark.parametrize("name,gain", [("c5g_18x22", 16.0), ("c3b_ksw_18x30", 8.0)])
 def test_trained_range_scores_bf16(name, gain):
     # scores as large as trained weights give (row maxima ~70, the largest
-    # above 100) on the bf16 path: head dim 64 (the first pass chosen from
-    # tile 0) and head dim 56 with the keys split among the waves (the pass
-    # without a running maximum, then the online one). The bf16 q and k move
+    # above 100) on the bf16 path: head dim 64 and head dim 56 with the keys
+    # split among the waves (both choose their pass from the first key
+    # tile). The bf16 q and k move
     # a score by ~|s| 2^-8, which decides between near-tied keys, so ctx is
     # compared per (query, head) where the two largest scores are at least 6
     # apart (the runner-up then weighs at most e^-6), y on the rows where

@@ -62,6 +62,7 @@ struct AttnParams {
   float* part_o;
   float* part_ml;
   float l_lo, l_hi;  // large-window kernel: the band a row sum must fall in (2^-64, 2^64)
+  float m_band;      // large-window kernel with the keys split among the waves: first tile's row maxima band
 };
 
 // Work-item and workgroup ids and votes from compiler builtins: this file is
@@ -97,10 +98,10 @@ static void attn_band(float& lo, float& hi) {
   hi = range == 0 ? 0.f : std::ldexp(1.0f, range);
 }
 
-// The band of tile 0's row maxima (c*s units) inside which the head-dim-64
-// kernel runs the pass without a running maximum: 16, or VIT_ATTN_TILE0_BAND
-// (test hook; a negative value sends every window to the running-maximum
-// pass from tile 0).
+// The band of the first key tile's row maxima (c*s units) inside which the
+// large-window kernels keep the pass without a running maximum: 16, or
+// VIT_ATTN_TILE0_BAND (test hook; a negative value sends every wave to the
+// running-maximum pass).
 static float attn_tile0_band() {
   const char* env = std::getenv("VIT_ATTN_TILE0_BAND");
   return env ? (float)std::atof(env) : 16.f;
@@ -567,6 +568,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
   // sends its wave, or with shared tiles its workgroup, through the pass
   // again with the online maximum (m_run subtracted, O and l rescaled as it
   // grows).
+  bool stopped = false;  // KSW: this wave left the first pass at its first tile
   auto tile_pass = [&](auto mf_tag) {
     constexpr bool MF = decltype(mf_tag)::value;
 #pragma unroll
@@ -613,6 +615,28 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (key_of_row(kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) >= kv_left) sacc[qb][kb][r] = -1e30f;
+      }
+      if constexpr (MF && KSW) {
+        // the wave's own keys and no barriers: a wave some of whose rows
+        // have their maximum c s over its first tile outside [-m_band,
+        // m_band] (trained weights) stops here and takes the online pass
+        if (kt == t0) {
+          bool wide = false;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            float mx = -1e30f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
+            const float mc = halves_max(mx) * c;
+            wide |= qrow_out[qb] >= 0 && !(mc >= -p.m_band && mc <= p.m_band);
+          }
+          if (wave_any(wide)) {
+            stopped = true;
+            break;
+          }
+        }
       }
       u32x4 pf[QB][2][2];  // [qb][kb][s]: bf16 P for MFMA k-step s of key block kb
       if constexpr (MF) {
@@ -693,7 +717,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma32_kernel(AttnParams<bf
     }
     // KSW: the wave's own keys, so its own decision; shared tiles: the
     // workgroup's (uniform, and a barrier before the tiles are refilled)
-    const bool again = KSW ? wave_any(out) : wg_any<NW>(out);
+    const bool again = KSW ? stopped || wave_any(out) : wg_any<NW>(out);
     if (again) tile_pass(std::integral_constant<bool, false>{});
   }
 
@@ -1239,6 +1263,7 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s, StageEvents ev
   }
   p.vt = (const T*)a.vt;
   attn_band(p.l_lo, p.l_hi);
+  p.m_band = attn_tile0_band();
   p.splits = 1;
   p.batch_rows = 0;
   p.part_o = a.part_o;
