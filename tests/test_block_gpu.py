@@ -405,6 +405,37 @@ def test_fused_mask_unit_block(name):
     gu.check(name + ":y (branches)", gu.to64(y_s), ref_s["y"], spec)
 
 
+def test_fused_mask_unit_trained_range_scores():
+    # the single-kernel mask-unit path (its softmax subtracts the row maximum)
+    # with query/key weights scaled to trained score ranges (row maxima ~38,
+    # the largest ~85) and the residual-suppressed input, so y is almost all
+    # branch; compared on the rows whose two largest scores are at least 6
+    # apart in both heads (bf16 q and k decide between near-tied keys)
+    spec = FUSED["c2_32x32"]
+    inp = synth.make_inputs(spec, seed=8, qk_gain=20.0)
+    inp["x"] = inp["x"] * np.float32(2.0 ** -8)
+    ref = ob.block_forward(inp["x"], inp, spec)
+    D, H, nw = spec["dim_out"], spec["heads"], spec["n_windows"]
+    hd, N = D // H, spec["grid_h"] * spec["grid_w"]
+    gaps = np.zeros((H, N))
+    top = 0.0
+    for w in range(nw):
+        tok = np.arange(w, N, nw)  # mask unit w: tokens w, w + nw, ... in unrolled order
+        q = ref["qkv"][0, tok, :D].reshape(len(tok), H, hd).transpose(1, 0, 2)
+        k = ref["qkv"][0, tok, D:2 * D].reshape(len(tok), H, hd).transpose(1, 0, 2)
+        sc = q @ k.transpose(0, 2, 1) / np.sqrt(hd)
+        top = max(top, sc.max())
+        top2 = np.sort(sc, axis=2)[:, :, -2:]
+        gaps[:, tok] = top2[:, :, 1] - top2[:, :, 0]
+    assert top > 60, top
+    rows = np.where((gaps >= 6.0).all(axis=0))[0]
+    assert len(rows) >= 100, len(rows)
+    y, _ = gu.run_block(spec, gu.to_device(inp, spec), seams=False)
+    yy = gu.to64(y)
+    assert np.all(np.isfinite(yy))
+    gu.check("c2 fused trained-range:y", yy[:, rows], ref["y"][:, rows], spec)
+
+
 @pytest.mark.parametrize("x_scale", [1.0, 2.0 ** -8], ids=["plain", "residual_suppressed"])
 def test_fused_mask_unit_full_size_sampled_rows(x_scale):
     # the single-kernel path at the benchmark's full size (256 mask units);
